@@ -1,0 +1,168 @@
+"""CPU oracle for the DSA hot path — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain C,
+fp64) with numpy marshalling; it never touches the GPU and shares no code
+with the HIP library.  Every function states the page passage it follows
+in ``oracle.c``.
+
+Parity status of each function (what pins it, see tests/test_oracle_*.py):
+  indexer_scores  pinned: H=1/w=1 reduces to ReLU of a numpy GEMV; all dots
+                  non-negative reduces to one numpy matmul; linearity in w;
+                  one-hot keys/queries; causal -inf mask.
+  topk            pinned: numpy stable argsort on every row (brute force);
+                  closed-form special cases (ties, monotone rows, k >= p+1).
+  sparse_mla_attn pinned: dense causal attention from torch's CPU
+                  scaled_dot_product_attention in fp64 when k >= p+1;
+                  one-hot logits; identical rows; permutation invariance.
+  layer_group     pinned through its parts plus bitwise reuse of one index
+                  list by every layer.
+  mtp_verify      pinned: sum-min identities (p=q -> 1, disjoint -> 0,
+                  1 - TV distance), scipy softmax, Monte-Carlo check of the
+                  speculative-sampling theorem (acceptance rate = sum-min,
+                  emitted token ~ p).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        p, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.oracle_indexer_scores.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i32, p]
+        L.oracle_topk.argtypes = [p, p, i32, i32, i32, i32, p]
+        L.oracle_sparse_mla_attn.argtypes = [p, p, i64, p, i32, i32, i32, i32, i32, i32, i32, f64, p, p]
+        L.oracle_layer_group.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i32, i32, i32,
+                                         p, p, p, i32, i32, i32, f64, p, p, p, p]
+        L.oracle_softmax_row.argtypes = [p, i32, p]
+        L.oracle_mtp_verify.argtypes = [p, p, p, p, p, i32, i32, i32, p, p, p, p]
+        for fn in ("oracle_indexer_scores", "oracle_topk", "oracle_sparse_mla_attn", "oracle_layer_group",
+                   "oracle_softmax_row", "oracle_mtp_verify"):
+            getattr(L, fn).restype = None
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype)
+    return a
+
+
+def _p(a) -> int:
+    return a.ctypes.data
+
+
+def indexer_scores(q_idx, w, k_idx, q_pos, L=None) -> np.ndarray:
+    """q_idx [B,T,H,D] bf16 bits (uint16), w [B,T,H] f32, k_idx [B,Lk,D] uint16,
+    q_pos [B,T] int32 -> scores [B,T,L] f32 (-inf where s > p)."""
+    q_idx = _c(q_idx, np.uint16)
+    w = _c(w, np.float32)
+    k_idx = _c(k_idx, np.uint16)
+    q_pos = _c(q_pos, np.int32)
+    B, T, H, D = q_idx.shape
+    assert D <= 1024 and k_idx.shape[0] == B and k_idx.shape[2] == D and w.shape == (B, T, H)
+    Lk = k_idx.shape[1]
+    L = Lk if L is None else L
+    assert L <= Lk
+    out = np.empty((B, T, L), np.float32)
+    lib().oracle_indexer_scores(_p(q_idx), _p(w), _p(k_idx), Lk * D, _p(q_pos), B, T, L, H, D, _p(out))
+    return out
+
+
+def topk(scores, q_pos, k) -> np.ndarray:
+    """scores [B,T,L] f32, q_pos [B,T] -> idx [B,T,k] int32 (ascending, -1 padded)."""
+    scores = _c(scores, np.float32)
+    q_pos = _c(q_pos, np.int32)
+    B, T, L = scores.shape
+    out = np.empty((B, T, k), np.int32)
+    lib().oracle_topk(_p(scores), _p(q_pos), B, T, L, k, _p(out))
+    return out
+
+
+def sparse_mla_attn(q, kv, idx, sm_scale, Dv=512, L=None):
+    """q [B,T,Hq,Dqk] uint16, kv [B,Lk,Dqk] uint16, idx [B,T,k] int32
+    -> (out [B,T,Hq,Dv] f64, lse [B,T,Hq] f64)."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    idx = _c(idx, np.int32)
+    B, T, Hq, Dqk = q.shape
+    Lk = kv.shape[1]
+    L = Lk if L is None else L
+    k = idx.shape[2]
+    assert kv.shape[0] == B and kv.shape[2] == Dqk and idx.shape[:2] == (B, T)
+    out = np.empty((B, T, Hq, Dv), np.float64)
+    lse = np.empty((B, T, Hq), np.float64)
+    lib().oracle_sparse_mla_attn(_p(q), _p(kv), Lk * Dqk, _p(idx), B, T, L, Hq, Dqk, Dv, k, float(sm_scale),
+                                 _p(out), _p(lse))
+    return out, lse
+
+
+def layer_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, Dv=512):
+    """One IndexShare group.  qs/kvs: lists (one per layer).  Returns
+    (scores, idx, [out_l], [lse_l])."""
+    q_idx = _c(q_idx, np.uint16)
+    w = _c(w, np.float32)
+    k_idx = _c(k_idx, np.uint16)
+    q_pos = _c(q_pos, np.int32)
+    qs = [_c(q, np.uint16) for q in qs]
+    kvs = [_c(kv, np.uint16) for kv in kvs]
+    B, T, H, D = q_idx.shape
+    L = k_idx.shape[1]
+    n = len(qs)
+    Hq, Dqk = qs[0].shape[2], qs[0].shape[3]
+    scores = np.empty((B, T, L), np.float32)
+    idx = np.empty((B, T, k), np.int32)
+    outs = [np.empty((B, T, Hq, Dv), np.float64) for _ in range(n)]
+    lses = [np.empty((B, T, Hq), np.float64) for _ in range(n)]
+    P = ctypes.c_void_p * n
+    q_ptrs = P(*[_p(a) for a in qs])
+    kv_ptrs = P(*[_p(a) for a in kvs])
+    strides = (ctypes.c_int64 * n)(*[a.shape[1] * Dqk for a in kvs])
+    out_ptrs = P(*[_p(a) for a in outs])
+    lse_ptrs = P(*[_p(a) for a in lses])
+    lib().oracle_layer_group(_p(q_idx), _p(w), _p(k_idx), L * D, _p(q_pos), B, T, L, H, D, k, n,
+                             ctypes.cast(q_ptrs, ctypes.c_void_p), ctypes.cast(kv_ptrs, ctypes.c_void_p),
+                             ctypes.cast(strides, ctypes.c_void_p), Hq, Dqk, Dv, float(sm_scale),
+                             _p(scores), _p(idx), ctypes.cast(out_ptrs, ctypes.c_void_p),
+                             ctypes.cast(lse_ptrs, ctypes.c_void_p))
+    return scores, idx, outs, lses
+
+
+def softmax_row(logits) -> np.ndarray:
+    logits = _c(logits, np.float32)
+    out = np.empty(logits.shape[-1], np.float64)
+    lib().oracle_softmax_row(_p(logits), logits.shape[-1], _p(out))
+    return out
+
+
+def mtp_verify(target, draft, draft_tokens, u_acc, u_res):
+    """target [B,S+1,V] f32, draft [B,S,V] f32, draft_tokens [B,S] int32,
+    u_acc [B,S] f32, u_res [B] f32 -> dict(min_sum [B,S] f64, n_acc [B],
+    next_tok [B], ratio [B,S] f64 = p(x)/q(x) at each draft token)."""
+    target = _c(target, np.float32)
+    draft = _c(draft, np.float32)
+    draft_tokens = _c(draft_tokens, np.int32)
+    u_acc = _c(u_acc, np.float32)
+    u_res = _c(u_res, np.float32)
+    B, S, V = draft.shape
+    assert target.shape == (B, S + 1, V)
+    min_sum = np.empty((B, S), np.float64)
+    ratio = np.empty((B, S), np.float64)
+    n_acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    lib().oracle_mtp_verify(_p(target), _p(draft), _p(draft_tokens), _p(u_acc), _p(u_res), B, S, V,
+                            _p(min_sum), _p(n_acc), _p(nxt), _p(ratio))
+    return {"min_sum": min_sum, "n_acc": n_acc, "next_tok": nxt, "ratio": ratio}

@@ -1,0 +1,308 @@
+/*
+ * CPU oracle for the DSA sparse-attention hot path.  TEST INFRASTRUCTURE ONLY:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header or constant with the HIP
+ * path and is deliberately plain: scalar loops, fp64 arithmetic, library
+ * qsort/exp/log, no blocking or fusion beyond what each definition states.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [TEARDOWN]  "GLM-5.2 开源：读完 1M 上下文的实现原理，你能更懂 AI",
+ *               clawlihai.cn/blog/glm-52-1m-architecture-teardown
+ *   [MTPBLOG]   GLM-5.2 MTP / IndexShare inference write-up,
+ *               4sapi.ai/blog/glm-52-mtp-indexshare-inference
+ *   [CTXFR]     "Le contexte d'un million de tokens", glmmodel.cn/fr/context-window
+ *   [SPECYUN]   "GLM-5.2 speculative decoding 实测：MTP 接受长度提升 20% 的体感",
+ *               yun88.com/news/9578
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - indexer score = sum_h w_h * max(0, q_h . k_s); no scale factor, one
+ *     128-dim key per cached token shared by all 32 heads; key s is visible
+ *     to a query at absolute position p iff s <= p;
+ *   - top-k ties go to the lower position; the chosen positions are emitted
+ *     in ascending order and padded with -1 when fewer than k are visible;
+ *   - attention values are the first 512 of the 576 latent dims; an index
+ *     outside [0, L) is masked; a query with nothing visible outputs zeros;
+ *   - verification is standard speculative sampling (accept x with
+ *     probability min(1, p(x)/q(x)), on rejection resample from
+ *     max(p - q, 0) normalised, after S acceptances sample from the next
+ *     target distribution); uniforms are inputs.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+int oracle_abi_version(void) { return 1; }
+
+/* bf16 bit pattern -> double: the bf16 value is the top half of an fp32. */
+static double bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------ indexer
+ * [TEARDOWN, 刀一 DSA]: before attention, a small indexer with
+ * index_n_heads 32 and index_head_dim 128 coarse-screens every history
+ * token; [CTXFR, "Attention sparse IndexShare"]: the screen is made of dot
+ * products.  For each query (b,t) at position p and each key s <= p:
+ *     score[b,t,s] = sum_{h<H} w[b,t,h] * max(0, sum_{d<D} q[b,t,h,d] k[b,s,d])
+ * accumulated in fp64 and rounded once to fp32.  Keys s > p get -inf.
+ * Layouts: q_idx [B,T,H,D], w [B,T,H], k_idx row s of batch b at
+ * k_idx + b*k_bstride + s*D, q_pos [B,T], scores [B,T,L].
+ */
+void oracle_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                           const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores) {
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const int64_t bt = (int64_t)b * T + t;
+            const int64_t p = q_pos[bt];
+            double* q = (double*)malloc(sizeof(double) * (size_t)H * (size_t)D);
+            for (int i = 0; i < H * D; ++i) q[i] = bf16_to_double(q_idx[bt * H * D + i]);
+            float* row = scores + bt * (int64_t)L;
+#pragma omp parallel for schedule(static)
+            for (int64_t s = 0; s < L; ++s) {
+                if (s > p) {
+                    row[s] = -INFINITY;
+                    continue;
+                }
+                const uint16_t* key = k_idx + (int64_t)b * k_bstride + s * D;
+                double kd[1024];
+                for (int d = 0; d < D; ++d) kd[d] = bf16_to_double(key[d]);
+                double acc = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += q[h * D + d] * kd[d];
+                    double relu = dot > 0.0 ? dot : 0.0;
+                    acc += (double)w[bt * H + h] * relu;
+                }
+                float f = (float)acc;
+                row[s] = (f == 0.0f) ? 0.0f : f; /* one zero: +0 */
+            }
+            free(q);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ top-k
+ * [TEARDOWN, 刀一 DSA]: index_topk 2048 — keep the 2048 best-scoring
+ * history tokens for each query.  Candidates are s in [0, min(p, L-1)].
+ * Order them by (score descending, s ascending), keep the first
+ * min(k, #candidates), and write the kept positions in ascending order,
+ * padding the row with -1 up to k.
+ */
+typedef struct {
+    float score;
+    int32_t pos;
+} cand_t;
+
+static int cmp_cand(const void* a, const void* b) {
+    const cand_t* x = (const cand_t*)a;
+    const cand_t* y = (const cand_t*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+void oracle_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, int k, int32_t* idx) {
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+        int64_t p = q_pos[bt];
+        int64_t n = (p < L - 1 ? p : L - 1) + 1;
+        if (n < 0) n = 0;
+        cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+        for (int64_t s = 0; s < n; ++s) {
+            c[s].score = scores[bt * (int64_t)L + s];
+            c[s].pos = (int32_t)s;
+        }
+        qsort(c, (size_t)n, sizeof(cand_t), cmp_cand);
+        int64_t m = n < k ? n : k;
+        int32_t* out = idx + bt * (int64_t)k;
+        for (int64_t j = 0; j < m; ++j) out[j] = c[j].pos;
+        qsort(out, (size_t)m, sizeof(int32_t), cmp_i32);
+        for (int64_t j = m; j < k; ++j) out[j] = -1;
+        free(c);
+    }
+}
+
+/* ------------------------------------------------------------------ attention
+ * [TEARDOWN, 刀一 DSA]: full attention only over the selected tokens;
+ * [TEARDOWN, 刀三 MLA]: the cache holds one compressed latent vector per
+ * token (kv_lora_rank 512, plus the 64-dim rope part: 576 values), shared by
+ * the 64 heads, expanded through learned matrices that the absorbed form
+ * folds into the query.  For query (b,t), head h and each valid j
+ * (0 <= idx[b,t,j] < L), with c_j the cached row idx[b,t,j] of batch b:
+ *     z_j = sm_scale * sum_{d<Dqk} q[b,t,h,d] c_j[d]
+ *     out[b,t,h,:] = sum_j softmax(z)_j c_j[0:Dv]
+ *     lse[b,t,h]   = log sum_j exp(z_j)            (-inf if no valid j)
+ * in fp64.  Layouts: q [B,T,Hq,Dqk], kv row r of batch b at
+ * kv + b*kv_bstride + r*Dqk, idx [B,T,k], out [B,T,Hq,Dv], lse [B,T,Hq].
+ */
+void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx,
+                            int B, int T, int L, int Hq, int Dqk, int Dv, int k, double sm_scale,
+                            double* out, double* lse) {
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+        const int64_t b = bt / T;
+        const int32_t* sel = idx + bt * (int64_t)k;
+        double* rows = (double*)malloc(sizeof(double) * (size_t)k * (size_t)Dqk);
+        double* z = (double*)malloc(sizeof(double) * (size_t)k);
+        double* qh = (double*)malloc(sizeof(double) * (size_t)Dqk);
+        int nv = 0;
+        for (int j = 0; j < k; ++j) {
+            int32_t r = sel[j];
+            if (r < 0 || r >= L) continue;
+            const uint16_t* src = kv + b * kv_bstride + (int64_t)r * Dqk;
+            for (int d = 0; d < Dqk; ++d) rows[(int64_t)nv * Dqk + d] = bf16_to_double(src[d]);
+            ++nv;
+        }
+        for (int h = 0; h < Hq; ++h) {
+            const uint16_t* qsrc = q + (bt * Hq + h) * (int64_t)Dqk;
+            for (int d = 0; d < Dqk; ++d) qh[d] = bf16_to_double(qsrc[d]);
+            double* o = out + (bt * Hq + h) * (int64_t)Dv;
+            if (nv == 0) {
+                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+                if (lse) lse[bt * Hq + h] = -INFINITY;
+                continue;
+            }
+            double m = -INFINITY;
+            for (int j = 0; j < nv; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < Dqk; ++d) dot += qh[d] * rows[(int64_t)j * Dqk + d];
+                z[j] = sm_scale * dot;
+                if (z[j] > m) m = z[j];
+            }
+            double den = 0.0;
+            for (int j = 0; j < nv; ++j) {
+                z[j] = exp(z[j] - m);
+                den += z[j];
+            }
+            for (int d = 0; d < Dv; ++d) {
+                double num = 0.0;
+                for (int j = 0; j < nv; ++j) num += z[j] * rows[(int64_t)j * Dqk + d];
+                o[d] = num / den;
+            }
+            if (lse) lse[bt * Hq + h] = m + log(den);
+        }
+        free(rows);
+        free(z);
+        free(qh);
+    }
+}
+
+/* ------------------------------------------------------------------ IndexShare group
+ * [TEARDOWN, 刀二 IndexShare] (index_topk_freq 4) and [CTXFR, "Attention
+ * sparse IndexShare"]: the indexer sits in the first layer of each group of
+ * four; its top-k list is used unchanged by all four layers, so indexer and
+ * top-k run once.  scores ([B,T,L]) and idx ([B,T,k]) receive the shared
+ * intermediate results; layer l reads q[l], kv[l], kv_bstride[l] and writes
+ * out[l], lse[l] (lse[l] may be NULL).
+ */
+void oracle_layer_group(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                        const int32_t* q_pos, int B, int T, int L, int H, int D, int k, int n_layers,
+                        const uint16_t* const* q, const uint16_t* const* kv, const int64_t* kv_bstride,
+                        int Hq, int Dqk, int Dv, double sm_scale, float* scores, int32_t* idx,
+                        double* const* out, double* const* lse) {
+    oracle_indexer_scores(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, scores);
+    oracle_topk(scores, q_pos, B, T, L, k, idx);
+    for (int l = 0; l < n_layers; ++l)
+        oracle_sparse_mla_attn(q[l], kv[l], kv_bstride[l], idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out[l],
+                               lse ? lse[l] : NULL);
+}
+
+/* ------------------------------------------------------------------ verification
+ * [MTPBLOG, "Rejection Sampling"]: for every vocabulary entry take the
+ * smaller of the two models' probabilities and sum; the sum is the
+ * probability that the draft is accepted.  [MTPBLOG, "MTP"] and [TEARDOWN,
+ * 刀四 MTP]: accepted drafts are kept and everything from the first rejected
+ * position on is dropped.  The accept/resample rule that realises exactly
+ * that acceptance probability is standard speculative sampling (Leviathan,
+ * Kalman & Matias 2023; Chen et al. 2023):
+ *   p_i = softmax(target[b,i]), q_i = softmax(draft[b,i])      (fp64)
+ *   min_sum[b,i] = sum_v min(p_i[v], q_i[v])
+ *   for i = 0..S-1: accept x_i = draft_tokens[b,i] iff u_acc[b,i] < p_i(x_i)/q_i(x_i);
+ *     at the first rejection: next = InvCDF(max(p_i - q_i, 0), u_res[b]), stop;
+ *   if all S accepted: next = InvCDF(p_S, u_res[b]);
+ *   n_acc[b] = number accepted.
+ * InvCDF(r, u) = the smallest v with sum_{v' <= v} r[v'] > u * sum r.
+ * Layouts: target [B,S+1,V], draft [B,S,V], draft_tokens/u_acc/min_sum
+ * [B,S], u_res/n_acc/next_tok [B].  ratio (may be NULL) receives
+ * p_i(x_i)/q_i(x_i) for every (b,i).
+ */
+void oracle_softmax_row(const float* logits, int V, double* p) {
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if ((double)logits[v] > m) m = (double)logits[v];
+    double s = 0.0;
+    for (int v = 0; v < V; ++v) {
+        p[v] = exp((double)logits[v] - m);
+        s += p[v];
+    }
+    for (int v = 0; v < V; ++v) p[v] /= s;
+}
+
+static int32_t inv_cdf(const double* r, int V, double u) {
+    double tot = 0.0;
+    int32_t last_pos = -1;
+    for (int v = 0; v < V; ++v) {
+        tot += r[v];
+        if (r[v] > 0.0) last_pos = v;
+    }
+    double thr = u * tot;
+    double c = 0.0;
+    for (int v = 0; v < V; ++v) {
+        c += r[v];
+        if (c > thr) return (int32_t)v;
+    }
+    return last_pos; /* u*tot rounded up to the total: the last token with mass */
+}
+
+void oracle_mtp_verify(const float* target, const float* draft, const int32_t* draft_tokens,
+                       const float* u_acc, const float* u_res, int B, int S, int V, double* min_sum,
+                       int32_t* n_acc, int32_t* next_tok, double* ratio) {
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)V);
+        int rejected_at = -1;
+        for (int i = 0; i < S; ++i) {
+            oracle_softmax_row(target + ((int64_t)b * (S + 1) + i) * V, V, p);
+            oracle_softmax_row(draft + ((int64_t)b * S + i) * V, V, qd);
+            double ms = 0.0;
+            for (int v = 0; v < V; ++v) ms += p[v] < qd[v] ? p[v] : qd[v];
+            min_sum[(int64_t)b * S + i] = ms;
+            int32_t x = draft_tokens[(int64_t)b * S + i];
+            double rt = p[x] / qd[x];
+            if (ratio) ratio[(int64_t)b * S + i] = rt;
+            if (rejected_at < 0 && !((double)u_acc[(int64_t)b * S + i] < rt)) {
+                rejected_at = i;
+                for (int v = 0; v < V; ++v) p[v] = p[v] > qd[v] ? p[v] - qd[v] : 0.0;
+                double tot = 0.0;
+                for (int v = 0; v < V; ++v) tot += p[v];
+                if (tot > 0.0) {
+                    next_tok[b] = inv_cdf(p, V, (double)u_res[b]);
+                } else { /* p == q in fp64: cannot reject in exact arithmetic */
+                    oracle_softmax_row(target + ((int64_t)b * (S + 1) + i) * V, V, p);
+                    next_tok[b] = inv_cdf(p, V, (double)u_res[b]);
+                }
+            }
+        }
+        if (rejected_at < 0) {
+            n_acc[b] = S;
+            oracle_softmax_row(target + ((int64_t)b * (S + 1) + S) * V, V, p);
+            next_tok[b] = inv_cdf(p, V, (double)u_res[b]);
+        } else {
+            n_acc[b] = rejected_at;
+        }
+        free(p);
+        free(qd);
+    }
+}

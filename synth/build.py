@@ -1,0 +1,22 @@
+"""Compile the synthetic-input generator (synth.c) into synth/libsynth.so."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libsynth.so")
+
+
+def build(verbose: bool = False) -> str:
+    src = os.path.join(HERE, "synth.c")
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC", "-Wall", "-Werror",
+           "-o", tmp, src, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
