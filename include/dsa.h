@@ -1,0 +1,179 @@
+/*
+ * dsa.h — C ABI of libdsa.so: the DSA sparse-attention hot path on MI355X (gfx950).
+ *
+ * The method (from the pages cited below): a lightweight indexer scores every
+ * cached token for each query, the 2048 best positions are kept, and absorbed
+ * MLA attention runs over only those latent rows.  Under IndexShare one index
+ * list serves a group of four layers; in the MTP draft path the step-1 list is
+ * reused by the later steps and a rejection-sampling check computes the
+ * acceptance probability sum_v min(p_v, q_v).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [TEARDOWN]  "GLM-5.2 开源：读完 1M 上下文的实现原理，你能更懂 AI"
+ *               (clawlihai.cn/blog/glm-52-1m-architecture-teardown)
+ *   [MTPBLOG]   GLM-5.2 MTP / IndexShare inference write-up
+ *               (4sapi.ai/blog/glm-52-mtp-indexshare-inference)
+ *   [CTXFR]     "Le contexte d'un million de tokens" (glmmodel.cn/fr/context-window)
+ *   [SPECYUN]   "GLM-5.2 speculative decoding 实测：MTP 接受长度提升 20% 的体感"
+ *               (yun88.com/news/9578)
+ *
+ * Conventions for every entry point
+ *   Memory    Tensor pointers are DEVICE pointers owned by the caller.  The
+ *             library never allocates or frees device memory; scratch comes
+ *             from the caller's `ws` buffer of at least the size the matching
+ *             *_workspace_size() returns (256-byte aligned).  Inner dimensions
+ *             are contiguous; batch strides are given in elements.  bf16
+ *             values are passed as uint16_t bit patterns.  Pointers and batch
+ *             strides must be 16-byte aligned.  Outputs must not alias inputs.
+ *   Streams   `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *             only enqueue kernels; none synchronises, allocates or memsets,
+ *             so a call may be captured in a HIP graph.
+ *   Errors    Each call returns DSA_OK (0) or a negative DSA_ERR_* code.  On
+ *             error nothing has been enqueued, except DSA_ERR_HIP, which
+ *             reports a failed launch.  dsa_last_error() returns a
+ *             thread-local description of the last error.  Faults inside a
+ *             kernel surface at the caller's next synchronisation.
+ *   Positions q_pos[b,t] is the absolute position p of query (b,t); cached
+ *             key s is visible to it iff 0 <= s <= p.  p must be < L.
+ *   Thread safety  Stateless and re-entrant; concurrent calls must use
+ *             distinct workspaces.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* Shapes fixed by the GLM-5.2 config ([TEARDOWN, 刀一 DSA]: index_n_heads 32,
+ * index_head_dim 128, index_topk 2048; [TEARDOWN, 刀三 MLA]: kv_lora_rank
+ * 512, 64 heads; the rope width 64 completes the 576-value latent row). */
+#define DSA_INDEX_HEADS 32
+#define DSA_INDEX_DIM 128
+#define DSA_TOPK_MAX 2048
+#define DSA_ATTN_HEADS 64
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+#define DSA_GROUP_LAYERS_MAX 8
+
+enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+    DSA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    DSA_ERR_UNSUPPORTED = -3, /* a head count / dim other than the ones above */
+    DSA_ERR_ALIGN = -4,       /* a pointer or stride is not 16-byte aligned */
+    DSA_ERR_WORKSPACE = -5,   /* ws is NULL or smaller than required */
+    DSA_ERR_HIP = -6          /* the HIP runtime reported a launch error */
+};
+
+int dsa_abi_version(void);
+const char* dsa_last_error(void);
+
+/* ---------------------------------------------------------------- indexer
+ * [TEARDOWN, 刀一 DSA]; [CTXFR, "Attention sparse IndexShare"].
+ *   scores[b,t,s] = sum_{h<H} w[b,t,h] * max(0, sum_{d<D} q_idx[b,t,h,d] * k_idx[b,s,d])
+ * for s <= q_pos[b,t]; scores[b,t,s] = -inf for s > q_pos[b,t].  bf16 products,
+ * fp32 accumulation (exact whenever every partial sum is representable, e.g.
+ * small-integer inputs).
+ *   q_idx   [B,T,H,D] bf16      w [B,T,H] fp32      q_pos [B,T] int32
+ *   k_idx   row s of batch b at k_idx + b*k_bstride + s*D (bf16), s < L
+ *   scores  [B,T,L] fp32 (output)
+ * H must be 32 and D 128.  Needs no workspace. */
+int dsa_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                       const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores, void* stream);
+
+/* ---------------------------------------------------------------- top-k
+ * [TEARDOWN, 刀一 DSA] (index_topk 2048).  For each row (b,t) the candidates
+ * are s in [0, q_pos[b,t]]; they are ordered by (score descending, s
+ * ascending) and the first min(k, q_pos+1) are kept.  idx[b,t,:] receives the
+ * kept positions in ascending order, padded with -1 up to k.  Scores are
+ * compared as IEEE values (-0 == +0); NaN scores give an unspecified choice.
+ *   scores [B,T,L] fp32 (entries beyond q_pos are never read)
+ *   idx    [B,T,k] int32 (output)
+ * 1 <= k <= 2048. */
+size_t dsa_topk_workspace_size(int B, int T, int L, int k);
+int dsa_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, int k, int32_t* idx, void* ws,
+             size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- sparse MLA attention
+ * [TEARDOWN, 刀一 DSA] (full attention over the selected tokens only) and
+ * [TEARDOWN, 刀三 MLA] (one compressed latent row per token, shared by all
+ * heads).  For query (b,t), head h, and every j with 0 <= idx[b,t,j] < L
+ * (other entries are masked and never dereferenced):
+ *   z_j = sm_scale * <q[b,t,h,:], c_j>,   c_j = kv row idx[b,t,j] of batch b (Dqk values)
+ *   out[b,t,h,:] = sum_j softmax(z)_j * c_j[0:Dv]      (bf16, round-to-nearest-even)
+ *   lse[b,t,h]   = ln sum_j exp(z_j)                   (fp32; -inf if no valid j)
+ * A query with no valid entry outputs zeros.  bf16 operands, fp32
+ * accumulation, online softmax.
+ *   q    [B,T,Hq,Dqk] bf16         kv row r of batch b at kv + b*kv_bstride + r*Dqk
+ *   idx  [B,T,k] int32             out [B,T,Hq,Dv] bf16      lse [B,T,Hq] fp32 or NULL
+ * Hq must be 64, Dqk 576, Dv 512; 1 <= k <= 2048. */
+size_t dsa_attn_workspace_size(int B, int T, int k);
+int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
+                        int T, int L, int Hq, int Dqk, int Dv, int k, float sm_scale, uint16_t* out, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- IndexShare layer group
+ * [TEARDOWN, 刀二 IndexShare] (index_topk_freq 4: the indexer sits in the
+ * first of four layers and its top-k list is used by all four) and [CTXFR,
+ * "Attention sparse IndexShare"].  Runs dsa_indexer_scores and dsa_topk once,
+ * writes the shared list to idx_out, then runs dsa_sparse_mla_attn for each
+ * layer with that same list, all on `stream`.  Layers stay separate launches:
+ * in a model each layer's query depends on the previous layer's output.
+ * struct_size must be sizeof(dsa_group_args); fields added later go at the end. */
+typedef struct {
+    uint32_t struct_size;
+    int n_layers;                          /* 1..DSA_GROUP_LAYERS_MAX (4 for a group) */
+    int B, T, L, k;
+    float sm_scale;
+    /* indexer inputs (the group's first layer) */
+    const uint16_t* q_idx;                 /* [B,T,32,128] */
+    const float* w;                        /* [B,T,32] */
+    const uint16_t* k_idx;                 /* rows as in dsa_indexer_scores */
+    int64_t k_bstride;
+    const int32_t* q_pos;                  /* [B,T] */
+    int32_t* idx_out;                      /* [B,T,k] shared index list (output) */
+    /* per layer */
+    const uint16_t* q[DSA_GROUP_LAYERS_MAX];    /* [B,T,64,576] */
+    const uint16_t* kv[DSA_GROUP_LAYERS_MAX];   /* rows as in dsa_sparse_mla_attn */
+    int64_t kv_bstride[DSA_GROUP_LAYERS_MAX];
+    uint16_t* out[DSA_GROUP_LAYERS_MAX];        /* [B,T,64,512] */
+    float* lse[DSA_GROUP_LAYERS_MAX];           /* [B,T,64] or NULL */
+} dsa_group_args;
+
+size_t dsa_layer_group_workspace_size(const dsa_group_args* a);
+int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- MTP verification
+ * [MTPBLOG, "Rejection Sampling"]: summing min(p_v, q_v) over the vocabulary
+ * gives the probability that a draft token is accepted; [MTPBLOG, "MTP"] and
+ * [TEARDOWN, 刀四 MTP]: accepted drafts are kept and everything from the first
+ * rejection on is dropped.  The rule realising that acceptance probability is
+ * standard speculative sampling:
+ *   p_i = softmax(target_logits[b,i]),  q_i = softmax(draft_logits[b,i])
+ *   min_sum[b,i] = sum_v min(p_i[v], q_i[v])                  (every i < S)
+ *   for i = 0..S-1: accept draft_tokens[b,i] = x iff u_accept[b,i] < p_i(x)/q_i(x);
+ *     at the first rejection i: next_token[b] = InvCDF(max(p_i - q_i, 0), u_resample[b]);
+ *   if all S are accepted: next_token[b] = InvCDF(p_S, u_resample[b]);
+ *   n_accepted[b] = number of accepted drafts (acceptance length n_accepted + 1)
+ * where InvCDF(r, u) is the smallest v with sum_{v'<=v} r[v'] > u * sum_v r[v].
+ * fp32 exponentials, fp64 sums.  Decisions whose margin is below the fp32
+ * resolution of p/q, or a CDF step closer to u*sum r than that resolution,
+ * may go either way.
+ *   target_logits [B,S+1,V] fp32   draft_logits [B,S,V] fp32
+ *   draft_tokens, u_accept [B,S]   u_resample [B]   (uniforms in (0,1))
+ *   min_sum [B,S] fp32, n_accepted [B] int32, next_token [B] int32 (outputs) */
+size_t mtp_verify_workspace_size(int B, int S, int V);
+int mtp_draft_verify(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
+                     const float* u_accept, const float* u_resample, int B, int S, int V, float* min_sum,
+                     int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

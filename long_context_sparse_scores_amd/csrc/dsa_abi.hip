@@ -1,0 +1,204 @@
+// C ABI of libdsa.so: argument validation, workspace planning and launch order.
+// The operations themselves are described in include/dsa.h with the page
+// passages that define them.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    std::snprintf(g_err, sizeof(g_err), "no error");
+    return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxBlocks = (int64_t)1 << 31;
+
+int check_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                  const int32_t* q_pos, int B, int T, int L, int H, int D, const float* scores) {
+    if (!q_idx || !w || !k_idx || !q_pos || !scores) return fail(DSA_ERR_NULL, "indexer: NULL pointer argument");
+    if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "indexer: B=%d T=%d L=%d must be >= 1", B, T, L);
+    if (H != DSA_INDEX_HEADS || D != DSA_INDEX_DIM)
+        return fail(DSA_ERR_UNSUPPORTED, "indexer: H=%d D=%d, supported H=%d D=%d", H, D, DSA_INDEX_HEADS,
+                    DSA_INDEX_DIM);
+    if (B > 1 && k_bstride < (int64_t)L * D)
+        return fail(DSA_ERR_SHAPE, "indexer: k_bstride %lld < L*D", (long long)k_bstride);
+    if ((int64_t)B * T * ((L + 2047) / 2048) >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "indexer: grid too large");
+    if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(scores) || (k_bstride % 8) != 0)
+        return fail(DSA_ERR_ALIGN, "indexer: pointers and k_bstride*2 bytes must be 16-byte aligned");
+    return DSA_OK;
+}
+
+int check_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, int k, const int32_t* idx) {
+    if (!scores || !q_pos || !idx) return fail(DSA_ERR_NULL, "topk: NULL pointer argument");
+    if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "topk: B=%d T=%d L=%d must be >= 1", B, T, L);
+    if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_UNSUPPORTED, "topk: k=%d outside [1, %d]", k, DSA_TOPK_MAX);
+    if ((int64_t)B * T * ((L + 4095) / 4096) >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "topk: grid too large");
+    if (!aligned16(scores) || !aligned16(idx)) return fail(DSA_ERR_ALIGN, "topk: pointers must be 16-byte aligned");
+    return DSA_OK;
+}
+
+int check_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T, int L,
+               int Hq, int Dqk, int Dv, int k, float sm_scale, const uint16_t* out, const float* lse) {
+    if (!q || !kv || !idx || !out) return fail(DSA_ERR_NULL, "attn: NULL pointer argument");
+    if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "attn: B=%d T=%d L=%d must be >= 1", B, T, L);
+    if (Hq != DSA_ATTN_HEADS || Dqk != DSA_LATENT_DIM || Dv != DSA_VALUE_DIM)
+        return fail(DSA_ERR_UNSUPPORTED, "attn: Hq=%d Dqk=%d Dv=%d, supported %d/%d/%d", Hq, Dqk, Dv, DSA_ATTN_HEADS,
+                    DSA_LATENT_DIM, DSA_VALUE_DIM);
+    if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_UNSUPPORTED, "attn: k=%d outside [1, %d]", k, DSA_TOPK_MAX);
+    if (!std::isfinite(sm_scale)) return fail(DSA_ERR_SHAPE, "attn: sm_scale must be finite");
+    if (B > 1 && kv_bstride < (int64_t)L * Dqk)
+        return fail(DSA_ERR_SHAPE, "attn: kv_bstride %lld < L*Dqk", (long long)kv_bstride);
+    if ((int64_t)B * T * 64 >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "attn: grid too large");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(out) || (lse && !aligned16(lse)) ||
+        (kv_bstride % 8) != 0)
+        return fail(DSA_ERR_ALIGN, "attn: pointers and kv_bstride*2 bytes must be 16-byte aligned");
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                       const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores, void* stream) {
+    int st = check_indexer(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, scores);
+    if (st != DSA_OK) return st;
+    return hip_status(dsa::launch_indexer(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, (hipStream_t)stream),
+                      "dsa_indexer_scores");
+}
+
+size_t dsa_topk_workspace_size(int B, int T, int L, int k) {
+    if (B < 1 || T < 1 || L < 1) return 0;
+    return dsa::topk_ws_bytes(B * T, L, k);
+}
+
+int dsa_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, int k, int32_t* idx, void* ws,
+             size_t ws_bytes, void* stream) {
+    int st = check_topk(scores, q_pos, B, T, L, k, idx);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::topk_ws_bytes(B * T, L, k);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(DSA_ERR_WORKSPACE, "topk: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes, need);
+    return hip_status(dsa::launch_topk(scores, q_pos, B * T, L, k, idx, ws, (hipStream_t)stream), "dsa_topk");
+}
+
+size_t dsa_attn_workspace_size(int B, int T, int k) {
+    if (B < 1 || T < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
+    return dsa::attn_ws_bytes(B * T, k);
+}
+
+int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
+                        int L, int Hq, int Dqk, int Dv, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
+    int st = check_attn(q, kv, kv_bstride, idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out, lse);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::attn_ws_bytes(B * T, k);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(DSA_ERR_WORKSPACE, "attn: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes, need);
+    return hip_status(
+        dsa::launch_attn(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, (hipStream_t)stream),
+        "dsa_sparse_mla_attn");
+}
+
+// Workspace of a group: [scores B*T*L fp32][top-k scratch][attention scratch], each 256-byte aligned.
+size_t dsa_layer_group_workspace_size(const dsa_group_args* a) {
+    if (!a || a->struct_size != sizeof(dsa_group_args) || a->B < 1 || a->T < 1 || a->L < 1 || a->k < 1 ||
+        a->k > DSA_TOPK_MAX)
+        return 0;
+    const int rows = a->B * a->T;
+    return dsa::align_up((size_t)rows * a->L * sizeof(float), 256) + dsa::topk_ws_bytes(rows, a->L, a->k) +
+           dsa::attn_ws_bytes(rows, a->k);
+}
+
+int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream) {
+    if (!a) return fail(DSA_ERR_NULL, "group: NULL args");
+    if (a->struct_size != sizeof(dsa_group_args))
+        return fail(DSA_ERR_SHAPE, "group: struct_size %u, expected %zu", a->struct_size, sizeof(dsa_group_args));
+    if (a->n_layers < 1 || a->n_layers > DSA_GROUP_LAYERS_MAX)
+        return fail(DSA_ERR_SHAPE, "group: n_layers=%d outside [1, %d]", a->n_layers, DSA_GROUP_LAYERS_MAX);
+    const int B = a->B, T = a->T, L = a->L, k = a->k;
+    // validate everything before enqueueing anything
+    int st = check_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS, DSA_INDEX_DIM,
+                           reinterpret_cast<const float*>(ws ? ws : (void*)16));
+    if (st != DSA_OK) return st;
+    if (!a->idx_out) return fail(DSA_ERR_NULL, "group: NULL idx_out");
+    st = check_topk(reinterpret_cast<const float*>(16), a->q_pos, B, T, L, k, a->idx_out);
+    if (st != DSA_OK) return st;
+    for (int l = 0; l < a->n_layers; ++l) {
+        st = check_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS, DSA_LATENT_DIM,
+                        DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l]);
+        if (st != DSA_OK) return st;
+    }
+    const size_t need = dsa_layer_group_workspace_size(a);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(DSA_ERR_WORKSPACE, "group: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
+                    need);
+    const int rows = B * T;
+    char* base = reinterpret_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base);
+    void* topk_ws = base + dsa::align_up((size_t)rows * L * sizeof(float), 256);
+    void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores, s);
+    if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
+    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s);
+    if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
+    for (int l = 0; l < a->n_layers; ++l) {
+        e = dsa::launch_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, k, a->sm_scale, a->out[l],
+                             a->lse[l], attn_ws, s);
+        if (e != hipSuccess) return hip_status(e, "dsa_layer_group/attention");
+    }
+    return ok();
+}
+
+size_t mtp_verify_workspace_size(int B, int S, int V) {
+    if (B < 1 || S < 1 || V < 1) return 0;
+    return dsa::verify_ws_bytes(B, S, V);
+}
+
+int mtp_draft_verify(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
+                     const float* u_accept, const float* u_resample, int B, int S, int V, float* min_sum,
+                     int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream) {
+    if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_resample || !min_sum || !n_accepted ||
+        !next_token)
+        return fail(DSA_ERR_NULL, "verify: NULL pointer argument");
+    if (B < 1 || S < 1 || S > 64 || V < 1) return fail(DSA_ERR_SHAPE, "verify: B=%d S=%d V=%d (1 <= S <= 64)", B, S, V);
+    if ((int64_t)(2 * S + 1) * B * ((V + 8191) / 8192) >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "verify: too large");
+    if (!aligned16(target_logits) || !aligned16(draft_logits))
+        return fail(DSA_ERR_ALIGN, "verify: logits must be 16-byte aligned");
+    const size_t need = dsa::verify_ws_bytes(B, S, V);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(DSA_ERR_WORKSPACE, "verify: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
+                    need);
+    return hip_status(dsa::launch_verify(target_logits, draft_logits, draft_tokens, u_accept, u_resample, B, S, V,
+                                         min_sum, n_accepted, next_token, ws, (hipStream_t)stream),
+                      "mtp_draft_verify");
+}
+
+}  // extern "C"

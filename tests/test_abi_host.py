@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/dsa.h declares, the ctypes struct mirrors the C
+layout, and argument validation rejects bad calls before any HIP work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import long_context_sparse_scores_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from long_context_sparse_scores_amd import _build
+        _build.build()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(dsa):
+    names = declared_functions()
+    assert len(names) == 11, names
+    lib = dsa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_version_and_error_string(dsa):
+    assert dsa.abi_version() == 1
+    assert isinstance(dsa.last_error(), str)
+
+
+def test_group_struct_layout_matches_c(dsa, tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "dsa.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(dsa_group_args),'
+                   ' offsetof(dsa_group_args, q_idx), offsetof(dsa_group_args, idx_out),'
+                   ' offsetof(dsa_group_args, q), offsetof(dsa_group_args, kv_bstride),'
+                   ' offsetof(dsa_group_args, lse)); return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
+    G = dsa.GroupArgs
+    assert vals == [ctypes.sizeof(G), G.q_idx.offset, G.idx_out.offset, G.q.offset, G.kv_bstride.offset,
+                    G.lse.offset]
+
+
+def test_validation_rejects_before_launch(dsa):
+    lib = dsa.lib()
+    # NULL pointers
+    assert lib.dsa_indexer_scores(None, None, None, 0, None, 1, 1, 16, 32, 128, None, None) == -1
+    assert "NULL" in dsa.last_error()
+    fake = 4096  # never dereferenced: every call below fails validation first
+    # unsupported head count / dims
+    assert lib.dsa_indexer_scores(fake, fake, fake, 16 * 128, fake, 1, 1, 16, 16, 128, fake, None) == -3
+    assert lib.dsa_sparse_mla_attn(fake, fake, 576, fake, 1, 1, 1, 32, 576, 512, 16, 0.1, fake, None, None, 0,
+                                   None) == -3
+    # k out of range
+    assert lib.dsa_topk(fake, fake, 1, 1, 100, 0, fake, fake, 1 << 20, None) == -3
+    assert lib.dsa_topk(fake, fake, 1, 1, 100, 2049, fake, fake, 1 << 20, None) == -3
+    # bad shapes
+    assert lib.dsa_indexer_scores(fake, fake, fake, 0, fake, 1, 0, 16, 32, 128, fake, None) == -2
+    assert lib.dsa_indexer_scores(fake, fake, fake, 100, fake, 2, 1, 16, 32, 128, fake, None) == -2  # stride < L*D
+    # misalignment
+    assert lib.dsa_indexer_scores(fake + 2, fake, fake, 16 * 128, fake, 1, 1, 16, 32, 128, fake, None) == -4
+    # workspace too small
+    assert lib.dsa_topk(fake, fake, 1, 1, 100, 10, fake, fake, 8, None) == -5
+    assert lib.mtp_draft_verify(fake, fake, fake, fake, fake, 1, 2, 100, fake, fake, fake, None, 0, None) == -5
+    # group: wrong struct size, bad layer count
+    a = dsa.GroupArgs()
+    a.struct_size = 3
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    a.struct_size = ctypes.sizeof(dsa.GroupArgs)
+    a.n_layers = 0
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+
+
+def test_workspace_sizes(dsa):
+    assert dsa.topk_workspace_size(32, 1, 131072, 2048) > 32 * 3 * 2048 * 4
+    assert dsa.topk_workspace_size(0, 1, 10, 10) == 0
+    assert dsa.attn_workspace_size(4096, 1, 2048) == 0           # one split per query: no partials
+    assert dsa.attn_workspace_size(32, 1, 2048) > 0              # split-K partials
+    assert dsa.verify_workspace_size(16, 7, 151552) > 0

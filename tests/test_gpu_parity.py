@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs — small cases element by element, ragged shapes and edge
+cases.  Bit-exact for scores and indices; attention within 2e-2 of the
+output scale; verification exact outside the fp32 ambiguity band."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (DEV, LSE_TOL, assert_attn_close, bf16_dev, check_topk_properties, check_verify, f32_dev,
+                         host, i32_dev, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import long_context_sparse_scores_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+# ------------------------------------------------------------------ indexer
+def test_indexer_tiny_bit_exact(dsa):
+    cfg = synth.TINY
+    say("indexer tiny %s" % cfg.name)
+    qi, w, ki, pos = cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos()
+    got = host(dsa.indexer_scores(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos)))
+    ref = oracle.indexer_scores(qi, w, ki, pos)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_indexer_ragged_strided(dsa):
+    B, T, L, Lc = 2, 3, 5000, 5104
+    say("indexer ragged B=%d T=%d L=%d Lc=%d" % (B, T, L, Lc))
+    qi = synth.int_bf16(31, 1, (B, T, 32, 128))
+    w = synth.pow2_f32(31, 2, (B, T, 32))
+    ki = synth.int_bf16(31, 3, (B, Lc, 128))
+    pos = np.array([[0, 17, 4999], [2500, 4095, 4096]], np.int32)
+    got = host(dsa.indexer_scores(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), L=L))
+    ref = oracle.indexer_scores(qi, w, ki, pos, L=L)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_indexer_negative_weights(dsa):
+    # general weights (not the test distribution): still exact for integer inputs
+    B, T, L = 1, 2, 777
+    qi = synth.int_bf16(32, 1, (B, T, 32, 128))
+    ki = synth.int_bf16(32, 3, (B, L, 128))
+    w = (synth.pow2_f32(32, 2, (B, T, 32)) * np.where(np.arange(32) % 3 == 0, -1, 1)).astype(np.float32)
+    pos = np.array([[776, 300]], np.int32)
+    got = host(dsa.indexer_scores(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos)))
+    ref = oracle.indexer_scores(qi, w, ki, pos)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ top-k
+def _topk_case(dsa, scores, pos, k):
+    got = host(dsa.topk(f32_dev(scores), i32_dev(pos), k))
+    ref = oracle.topk(scores, pos, k)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_topk_tiny_from_oracle_scores(dsa):
+    cfg = synth.TINY
+    say("topk tiny")
+    scores = oracle.indexer_scores(cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos())
+    _topk_case(dsa, scores, cfg.q_pos(), cfg.k)
+
+
+@pytest.mark.parametrize("k", [1, 7, 2048])
+def test_topk_tie_heavy_multichunk(dsa, k):
+    rng = np.random.default_rng(100 + k)
+    B, T, L = 2, 3, 10000
+    say("topk ties k=%d" % k)
+    scores = (rng.integers(0, 8, size=(B, T, L)) / 16).astype(np.float32)
+    pos = np.array([[L - 1, 4096, 8191], [3, 2047, 9000]], np.int32)
+    _topk_case(dsa, scores, pos, k)
+
+
+def test_topk_signed_and_special_values(dsa):
+    rng = np.random.default_rng(7)
+    B, T, L, k = 1, 4, 9000, 2048
+    say("topk signed")
+    s = rng.standard_normal((B, T, L)).astype(np.float32)
+    s[0, 0, ::5] = -0.0
+    s[0, 0, 1::5] = 0.0
+    s[0, 1, :] = 1.5                     # all equal
+    s[0, 2, ::3] = -np.inf
+    s[0, 3] = np.arange(L, dtype=np.float32)  # increasing
+    pos = np.array([[L - 1, L - 1, L - 1, L - 1]], np.int32)
+    _topk_case(dsa, s, pos, k)
+
+
+def test_topk_short_rows(dsa):
+    rng = np.random.default_rng(8)
+    s = rng.standard_normal((1, 3, 3000)).astype(np.float32)
+    pos = np.array([[0, 999, 2047]], np.int32)
+    say("topk short rows")
+    _topk_case(dsa, s, pos, 2048)
+
+
+# ------------------------------------------------------------------ attention
+def test_attn_tiny_layers(dsa):
+    cfg = synth.TINY
+    say("attn tiny")
+    scores = oracle.indexer_scores(cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos())
+    idx = oracle.topk(scores, cfg.q_pos(), cfg.k)
+    for l in range(2):
+        q, kv = cfg.q_attn(l), cfg.kv(l)
+        out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), cfg.sm_scale, want_lse=True)
+        ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, cfg.sm_scale)
+        assert_attn_close(host(out), ref, "layer %d" % l)
+        np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
+def test_attn_masked_ragged(dsa):
+    rng = np.random.default_rng(9)
+    B, T, L, k = 2, 2, 3000, 100
+    say("attn masked ragged")
+    q = synth.normal_bf16(41, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(41, 2, (B, L, 576))
+    idx = np.stack([np.sort(rng.choice(L, size=(T, k), replace=False), axis=1) for _ in range(B)]).astype(np.int32)
+    idx[0, 0, 90:] = -1
+    idx[0, 1, 5] = L + 3          # out of range: masked
+    idx[1, 0, :] = -1             # nothing visible: zeros
+    idx[1, 1, ::2] = -7
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16)
+    g = host(out)
+    assert np.all(g[1, 0] == 0)
+    assert_attn_close(g, ref)
+    fin = np.isfinite(ref_lse)
+    assert np.all(np.isneginf(host(lse)[~fin]))
+    np.testing.assert_allclose(host(lse)[fin], ref_lse[fin], atol=LSE_TOL, rtol=0)
+
+
+def test_attn_dense_case(dsa):
+    # k >= p+1: every visible row selected, sparse attention == dense causal attention
+    B, T, L, k = 1, 3, 500, 512
+    say("attn dense")
+    q = synth.normal_bf16(42, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(42, 2, (B, L, 576))
+    pos = np.array([[10, 255, 499]], np.int32)
+    scores = np.zeros((B, T, L), np.float32)
+    idx = oracle.topk(scores, pos, k)
+    got = host(dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16))
+    ref, _ = oracle.sparse_mla_attn(q, kv, idx, 1 / 16)
+    assert_attn_close(got, ref)
+
+
+def test_attn_many_queries_direct_path(dsa):
+    # enough queries that each gets one split (the direct, combine-free kernel)
+    rng = np.random.default_rng(10)
+    B, T, L, k = 1, 600, 4000, 256
+    say("attn direct path T=%d" % T)
+    q = synth.normal_bf16(43, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(43, 2, (B, L, 576))
+    idx = np.sort(rng.choice(L, size=(B, T, k)), axis=2).astype(np.int32)
+    assert dsa.attn_workspace_size(B, T, k) == 0
+    got = host(dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16))
+    sample = [0, 1, 299, 599]
+    ref, _ = oracle.sparse_mla_attn(q[:, sample], kv, idx[:, sample], 1 / 16)
+    assert_attn_close(got[:, sample], ref)
+
+
+# ------------------------------------------------------------------ IndexShare group
+def test_group_tiny(dsa):
+    cfg = synth.TINY
+    say("group tiny")
+    qi, w, ki, pos = cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos()
+    qs = [cfg.q_attn(l) for l in range(cfg.n_layers)]
+    kvs = [cfg.kv(l) for l in range(cfg.n_layers)]
+    dq = [bf16_dev(q) for q in qs]
+    dkv = [bf16_dev(kv) for kv in kvs]
+    idx, outs, lses = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k, dq, dkv,
+                                      cfg.sm_scale, want_lse=True)
+    _, ref_idx, ref_outs, ref_lses = oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    for l in range(cfg.n_layers):
+        assert_attn_close(host(outs[l]), ref_outs[l], "layer %d" % l)
+        np.testing.assert_allclose(host(lses[l]), ref_lses[l], atol=LSE_TOL, rtol=0)
+        # every layer consumed the one shared list: bitwise equal to a standalone call with it
+        alone = dsa.sparse_mla_attn(dq[l], dkv[l], idx, cfg.sm_scale)
+        assert torch.equal(alone.view(torch.int16), outs[l].view(torch.int16))
+
+
+# ------------------------------------------------------------------ verification
+@pytest.mark.parametrize("rho", [0.0, 0.9, 1.0])
+def test_verify_small(dsa, rho):
+    rng = np.random.default_rng(int(rho * 10) + 50)
+    B, S, V = 8, 3, 1000
+    say("verify small rho=%.1f" % rho)
+    t = (rng.standard_normal((B, S + 1, V)) * 2).astype(np.float32)
+    d = (rho * t[:, :S] + np.sqrt(1 - rho * rho) * rng.standard_normal((B, S, V)) * 2).astype(np.float32)
+    tok = rng.integers(0, V, (B, S)).astype(np.int32)
+    tok[:, 0] = np.argmax(d[:, 0], -1)
+    u = rng.random((B, S)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
+def test_verify_mtp_vocab(dsa):
+    cfg = synth.MtpConfig("mtp_small", seed=5, B=3, L=1024)
+    say("verify vocab %d" % cfg.V)
+    t = cfg.target_logits()
+    d = cfg.draft_logits(t)
+    tok = cfg.draft_tokens(d)
+    u, ur = cfg.u_accept(), cfg.u_resample()
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
+def test_verify_out_of_vocab_token_rejected(dsa):
+    rng = np.random.default_rng(3)
+    B, S, V = 1, 2, 100
+    t = rng.standard_normal((B, S + 1, V)).astype(np.float32)
+    d = rng.standard_normal((B, S, V)).astype(np.float32)
+    tok = np.array([[V + 5, 3]], np.int32)
+    u = np.full((B, S), 0.01, np.float32)
+    ur = np.array([0.5], np.float32)
+    _, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    assert int(host(na)[0]) == 0 and 0 <= int(host(nx)[0]) < V
