@@ -129,17 +129,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         // O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads]
 #pragma unroll
         for (int db = 0; db < kDv / 16; ++db) {
-            const i16x4_t lo = lds_read_tr16(tile + tr_row * kPitch + 16 * db + tr_col);
-            const i16x4_t hi = lds_read_tr16(tile + (16 + tr_row) * kPitch + 16 * db + tr_col);
-            bf16x8_t a;
-            a[0] = __builtin_bit_cast(__bf16, lo[0]);
-            a[1] = __builtin_bit_cast(__bf16, lo[1]);
-            a[2] = __builtin_bit_cast(__bf16, lo[2]);
-            a[3] = __builtin_bit_cast(__bf16, lo[3]);
-            a[4] = __builtin_bit_cast(__bf16, hi[0]);
-            a[5] = __builtin_bit_cast(__bf16, hi[1]);
-            a[6] = __builtin_bit_cast(__bf16, hi[2]);
-            a[7] = __builtin_bit_cast(__bf16, hi[3]);
+            const bf16x4_t lo = lds_read_tr16(tile + tr_row * kPitch + 16 * db + tr_col);
+            const bf16x4_t hi = lds_read_tr16(tile + (16 + tr_row) * kPitch + 16 * db + tr_col);
+            const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             o[db] = mfma16x16x32(a, pb, o[db]);
         }
     }

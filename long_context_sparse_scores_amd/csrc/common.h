@@ -6,7 +6,7 @@
 namespace dsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -32,9 +32,11 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 
 // LDS transpose read of 4 bf16: within each group of 16 lanes, lane 4q+r
 // receives element r of the 8-byte chunk addressed by lane 4j+q as value j.
-__device__ __forceinline__ i16x4_t lds_read_tr16(const void* lds_ptr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(const_cast<void*>(lds_ptr)));
+// The result is consumed as a whole vector (concatenated with a shuffle):
+// extracting its elements one by one has been seen to miscompile.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const void* lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4_t*)(const_cast<void*>(lds_ptr)));
 }
 
 // Order-preserving map fp32 -> uint32 (larger score -> larger key); -0 and +0 map to one key.

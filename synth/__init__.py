@@ -166,7 +166,7 @@ class GroupConfig:
     # ---- tensors (host, numpy) ----
     def q_pos(self) -> np.ndarray:
         p = self.first_pos + np.arange(self.T, dtype=np.int32)
-        return np.ascontiguousarray(np.broadcast_to(p, (self.B, self.T)), np.int32)
+        return np.array(np.broadcast_to(p, (self.B, self.T)), np.int32)
 
     def q_idx(self) -> np.ndarray:
         return int_bf16(self.seed, T_Q_IDX, (self.B, self.T, self.H, self.D))
