@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA sparse-attention hot path on one MI355X.
+
+A step is one IndexShare group on the decode workload at 128K context:
+indexer scoring of every cached key, top-2048 selection, then sparse
+absorbed-MLA attention for each of the 4 layers with the shared index list
+(dsa_layer_group), for batch 32 with one query token per sequence.  Inputs
+are synthetic and seeded (synth/), resident in HBM before timing starts.
+
+Prints ONE JSON line: throughput in query tokens per second, the HBM
+roofline of the dominant kernel (the index-key scan), a per-phase breakdown
+and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+METRIC = "query-tokens/sec per 4-layer DSA group at 128K ctx; % of HBM roofline"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_128k_b32",
+                    help="decode_128k_b32 (default), decode_1m_b4, prefill_4096_at_128k, tiny_decode_8k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
+    ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for
+    this kernel, workload and kernel source exists under profiles/."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "long_context_sparse_scores_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None       # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (requested --gpus %d); the multi-GPU "
+              "context-parallel path is a design, not a measured configuration." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_sparse_scores_amd as dsa
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    assert isinstance(cfg, synth.GroupConfig)
+    dev = torch.device("cuda:0")
+    B, T, L, k, nl = cfg.B, cfg.T, cfg.L, cfg.k, cfg.n_layers
+    log("bench: workload %s B=%d T=%d L=%d k=%d layers=%d" % (cfg.name, B, T, L, k, nl))
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.time()
+    q_idx = to_dev(cfg.q_idx())
+    w = torch.from_numpy(cfg.w()).to(dev)
+    q_pos = torch.from_numpy(cfg.q_pos()).to(dev)
+    k_idx = to_dev(cfg.k_idx())
+    qs = [to_dev(cfg.q_attn(l)) for l in range(nl)]
+    host_kv = np.empty((B, L, cfg.Dqk), np.uint16)
+    kvs = []
+    for l in range(nl):
+        cfg.kv(l, out=host_kv)
+        kvs.append(to_dev(host_kv))
+    del host_kv
+    torch.cuda.synchronize()
+    log("bench: inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
+
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, T, cfg.Hq, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+    args_c = dsa.make_group_args(q_idx, w, k_idx, q_pos, k, qs, kvs, cfg.sm_scale, idx, outs)
+    ws_bytes = dsa.layer_group_workspace_size(args_c)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    lib = dsa.lib()
+    import ctypes
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    argp = ctypes.byref(args_c)
+
+    def group_step():
+        rc = lib.dsa_layer_group(argp, ws.data_ptr(), ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(dsa.last_error())
+
+    scores = ws[: B * T * L * 4].view(torch.float32).view(B, T, L)
+
+    def indexer_step():
+        dsa.indexer_scores(q_idx, w, k_idx, q_pos, scores=scores)
+
+    # ---------------- timed group steps
+    if not args.indexer_only:
+        for _ in range(args.warmup):
+            group_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            group_step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        log("bench: group step %.3f ms" % ms)
+
+    # ---------------- dominant kernel: the index-key scan, timed alone on the same stream
+    for _ in range(args.warmup):
+        indexer_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        indexer_step()
+    e1.record()
+    torch.cuda.synchronize()
+    idx_ms = e0.elapsed_time(e1) / args.steps
+    idx_bytes = B * T * (L * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4)
+    log("bench: indexer %.3f ms, %.1f GB/s" % (idx_ms, idx_bytes / idx_ms / 1e6))
+    if args.indexer_only:
+        return
+
+    # ---------------- per-phase breakdown (same kernels, called one entry point at a time)
+    topk_ws = torch.empty(dsa.topk_workspace_size(B, T, L, k), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, T, k)), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 + nl)]
+    phase = np.zeros(2 + nl)
+    reps = max(5, args.steps // 5)
+    for r in range(reps + 2):
+        ev[0].record()
+        indexer_step()
+        ev[1].record()
+        dsa.topk(scores, q_pos, k, idx=idx, ws=topk_ws)
+        ev[2].record()
+        for l in range(nl):
+            dsa.sparse_mla_attn(qs[l], kvs[l], idx, cfg.sm_scale, out=outs[l], ws=attn_ws)
+            ev[3 + l].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            phase += [ev[i].elapsed_time(ev[i + 1]) for i in range(2 + nl)]
+    phase /= reps
+    breakdown = {"indexer_ms": round(phase[0], 4), "topk_ms": round(phase[1], 4),
+                 "attn_ms_per_layer": [round(x, 4) for x in phase[2:]]}
+    log("bench: breakdown %s" % breakdown)
+
+    qtok = B * T
+    value = qtok / (ms / 1e3)
+    step_bytes = qtok * synth.group_bytes_per_query(cfg)
+    achieved = idx_bytes / (idx_ms / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; GLM-5.2 shapes)",
+        "config": {"workload": cfg.name, "batch": B, "query_tokens_per_seq": T, "context": L, "topk": k,
+                   "layers_per_group": nl, "index_heads": cfg.H, "index_dim": cfg.D, "attn_heads": cfg.Hq,
+                   "latent_dim": cfg.Dqk, "value_dim": cfg.Dv},
+        "hbm_roofline_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("indexer", cfg.name),
+                     "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 4)},
+        "breakdown": breakdown,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, target_s):
+    """The CPU oracle (oracle/, plain C fp64 + OpenMP), untuned, on whole
+    sequences of the same workload: indexer over all L keys, top-k, and the
+    attention of every layer.  Runs sequences until about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    done, spent = 0, 0.0
+    b = 0
+    while spent < target_s and b < cfg.B:
+        qi = cfg.q_idx()[b:b + 1]
+        w = cfg.w()[b:b + 1]
+        ki = cfg.k_idx_rows(b)[None]
+        pos = cfg.q_pos()[b:b + 1]
+        qs = [cfg.q_attn(l)[b:b + 1] for l in range(cfg.n_layers)]
+        kvs = [cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
+        t0 = time.perf_counter()
+        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
+        spent += time.perf_counter() - t0
+        done += cfg.T
+        b += 1
+        log("bench: cpu oracle %d sequence(s), %.2f s" % (b, spent))
+    return {"value": round(done / spent, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (%d query tokens) of %s, whole pipeline per sequence: indexer over "
+                      "all %d keys, top-%d, %d attention layers; fp64 plain C with OpenMP"
+                      % (b, cfg.B, done, cfg.name, cfg.L, cfg.k, cfg.n_layers)}
+
+
+if __name__ == "__main__":
+    main()

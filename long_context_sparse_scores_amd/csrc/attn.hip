@@ -7,16 +7,21 @@
 // In absorbed form each head's query already lives in that latent space, so
 //   z_j = sm_scale * <q_h, c_j>   (576 dims),   o_h = softmax(z) . c[:, 0:512].
 //
-// Work unit: one query (b,t) and a split of its index list.  A workgroup of
-// four waves gathers 32 selected rows at a time into LDS (1152 bytes each,
-// padded pitch), wave w owns heads 16w..16w+15:
+// Work unit: one query (b,t) and a split of its index list; one 256-thread
+// workgroup per CU.  Selected rows are gathered 32 at a time (36 KiB tiles)
+// straight from HBM into LDS with direct-to-LDS loads (no registers), four
+// tile buffers deep so three tiles are in flight while one is computed.  The
+// tile layout XOR-swizzles 16-byte chunks per row to spread operand reads
+// over the LDS banks.  Wave w owns heads 16w..16w+15:
 //   S^T (32 rows x 16 heads) = K_rows . Q^T   v_mfma_f32_16x16x32_bf16, q in registers
 //   O^T (512 dims x 16 heads) += V^T . P^T    V^T read with ds_read_b64_tr_b16,
 //                                             P^T stays in the S^T registers
 // Softmax is online in base 2 with a lazily moved reference maximum (the
 // accumulators are rescaled only when a tile's maximum exceeds the reference
 // by more than 8, so exponentials stay below 2^8).  Splits write unnormalised
-// partial outputs plus (max, sum); a combine kernel merges them in split order.
+// fp32 partial outputs plus (max, sum); a combine kernel, one block per
+// (query, head), merges them in split order.  A query whose list fits one
+// split is normalised and written directly.
 #include "common.h"
 
 namespace dsa {
@@ -25,15 +30,131 @@ namespace {
 constexpr int kHq = 64;
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kRows = 32;                        // gathered rows per tile
-constexpr int kPitch = kDqk + 16;                // LDS row pitch in bf16 (1184 bytes)
-constexpr int kChunks = kDqk / 8;                // 16-byte chunks per latent row
+constexpr int kRows = 32;                         // gathered rows per tile
+constexpr int kChunks = kDqk / 8;                 // 16-byte chunks per latent row (72)
+constexpr int kTileChunks = kRows * kChunks;      // 2304 chunks = 36 KiB per tile
 constexpr int kThreads = 256;
-constexpr int kLoads = kRows * kChunks / kThreads;  // 9 chunks per thread per tile
-constexpr int kTargetBlocks = 512;
-constexpr float kRescaleSlack = 8.0f;            // log2 units
+constexpr int kWaves = kThreads / kWave;
+constexpr int kLoads = kTileChunks / kThreads;    // 9 direct-to-LDS loads per thread per tile
+constexpr int kStages = 4;                        // LDS tile buffers (3 tiles in flight + 1 computing)
+constexpr int kMaxSplitRows = 2048;
+constexpr int kTargetBlocks = 256;                // one resident block per CU
+constexpr float kRescaleSlack = 8.0f;             // log2 units
 
-static_assert(kRows * kChunks % kThreads == 0, "tile load must split evenly");
+static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
+
+// Tile layout in LDS: row r, 16-byte chunk cc lives at chunk slot r*72 + (cc ^ (r & 7)).
+// The XOR spreads the 16 rows read by one MFMA operand over all LDS banks while
+// keeping each wave's 64 direct-to-LDS writes (one contiguous KiB) in place.
+__device__ __forceinline__ int slot(int r, int cc) { return r * kChunks + (cc ^ (r & 7)); }
+
+// One 16-byte-per-lane direct-to-LDS load: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// Issued from asm so that the compiler, which cannot tell which tile buffer the
+// load fills, does not drain every in-flight load before each LDS read; the
+// kernel orders these writes itself with wait_vmem() and lds_barrier().  The
+// instruction has no register result and reads its address when issued.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+__device__ __forceinline__ void gather_tile(const uint16_t* __restrict__ kvb, const int* __restrict__ rows_lds,
+                                            int t, int nrows, int L, const uint16_t* tile, int wave, int lane) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int blk = kWaves * i + wave;              // this wave's KiB of the tile
+        const int p = 64 * blk + lane;                  // chunk slot written by this lane
+        const int r = p / kChunks;
+        const int cc = (p % kChunks) ^ (r & 7);         // logical chunk stored in that slot
+        const int j = t * kRows + r;
+        int rid = j < nrows ? rows_lds[j] : 0;
+        rid = (rid >= 0 && rid < L) ? rid : 0;          // masked rows read row 0 (finite) and get P = 0
+        lds_dma16(kvb + (int64_t)rid * kDqk + 8 * cc, __builtin_amdgcn_readfirstlane(base + 1024u * blk));
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only.  (__syncthreads() also waits for every outstanding global load,
+// which would drain the gather pipeline.)  The asm memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct SoftmaxState {
+    f32x4_t o[kDv / 16];  // O^T accumulators: dims 16*db + 4g + r of head 16w + c
+    float m_ref;          // reference maximum (log2 units) of head 16w + c
+    float lsum;           // this lane's share of the softmax denominator
+};
+
+// One tile of 32 gathered rows already resident in LDS at `tl`.
+__device__ __forceinline__ void attend_tile(const uint16_t* tl, const int* __restrict__ rows_lds, int t, int nrows,
+                                            int L, float scale_log2, const bf16x8_t (&qb)[kDqk / 32], int lane,
+                                            SoftmaxState& st) {
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    // S^T tile: rows (rb*16 + 4g + r) x head (16w + c)
+    f32x4_t s[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int r = rb * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks)
+            s[rb] = mfma16x16x32(*reinterpret_cast<const bf16x8_t*>(tl + 8 * slot(r, 4 * ks + g)), qb[ks], s[rb]);
+    }
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = t * kRows + (e >> 2) * 16 + 4 * g + (e & 3);
+        const int rid = j < nrows ? rows_lds[j] : -1;
+        const float v = (rid >= 0 && rid < L) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        x[e] = v;
+        mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    if (__ballot(mx > st.m_ref + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m_ref, mx);
+        const float f = (m_new == -INFINITY) ? 1.0f : exp2f(st.m_ref - m_new);
+#pragma unroll
+        for (int db = 0; db < kDv / 16; ++db) st.o[db] *= f;
+        st.lsum *= f;
+        st.m_ref = m_new;
+    }
+    const float mu = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
+    // P^T operand: k-slot 8g+e holds row (e<4 ? 4g+e : 16+4g+e-4), i.e. this lane's own S^T values.
+    bf16x8_t pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint16_t h = f32_to_bf16_rne(exp2f(x[e] - mu));
+        st.lsum += bf16_to_f32(h);
+        pb[e] = __builtin_bit_cast(__bf16, h);
+    }
+    // O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads].
+    // Transpose-read addressing: lane (g, 4j+q) points at row 4g+j (+16), dims 4q..4q+3 of the block.
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_q = lane & 3;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+        const int cc = 2 * db + (tr_q >> 1);
+        const int off = 4 * (tr_q & 1);
+        const bf16x4_t lo = lds_read_tr16(tl + 8 * slot(tr_row, cc) + off);
+        const bf16x4_t hi = lds_read_tr16(tl + 8 * slot(16 + tr_row, cc) + off);
+        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[db] = mfma16x16x32(a, pb, st.o[db]);
+    }
+}
 
 template <bool DIRECT>
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
@@ -48,11 +169,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const int c = lane & 15;
     const int g = lane >> 4;
     const int j0 = split * rows_per_split;
-    const int j1 = min(k, j0 + rows_per_split);
+    const int nrows = min(k, j0 + rows_per_split) - j0;
+    const int ntiles = (nrows + kRows - 1) / kRows;
 
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kRows * kPitch];
-    __shared__ int row_ok[kRows];
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
+    __shared__ int rows_lds[kMaxSplitRows];
 
+    const int32_t* sel = idx + (int64_t)bt * k + j0;
+    for (int j = threadIdx.x; j < nrows; j += kThreads) rows_lds[j] = sel[j];
     // B operand of S^T: q[head 16w+c][32*ks + 8*g .. +7].
     bf16x8_t qb[kDqk / 32];
     {
@@ -60,85 +184,42 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 #pragma unroll
         for (int ks = 0; ks < kDqk / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
     }
-    f32x4_t o[kDv / 16];
+    SoftmaxState st;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;  // reference maximum (log2 units) of head 16w+c
-    float lsum = 0.0f;        // this lane's share of the softmax denominator
+    for (int db = 0; db < kDv / 16; ++db) st.o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m_ref = -INFINITY;
+    st.lsum = 0.0f;
+    // Consume q here so the compiler's own wait for these loads happens before the
+    // gathers start, not inside the tile loop where it would also drain them.
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qb[ks]));
+    __syncthreads();  // rows_lds ready
 
-    const int32_t* sel = idx + (int64_t)bt * k;
     const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
-    // transpose-read addressing: lane (g, 4j+q) points at row 4g+j (+16), dims 4q..4q+3 of a 16-dim block
-    const int tr_row = 4 * g + ((lane & 15) >> 2);
-    const int tr_col = 4 * (lane & 3);
-
-    for (int j = j0; j < j1; j += kRows) {
-        __syncthreads();  // the previous tile is no longer read
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int ci = threadIdx.x + kThreads * i;
-            const int r = ci / kChunks, cc = ci % kChunks;
-            const int jj = j + r;
-            const int rid = jj < j1 ? sel[jj] : -1;
-            const bool ok = rid >= 0 && rid < L;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (ok) v = *reinterpret_cast<const u32x4_t*>(kvb + (int64_t)rid * kDqk + 8 * cc);
-            *reinterpret_cast<u32x4_t*>(tile + r * kPitch + 8 * cc) = v;
-            if (cc == 0) row_ok[r] = ok;
-        }
-        __syncthreads();
-
-        // S^T tile: rows (rb*16 + 4g + r) x head (16w + c)
-        f32x4_t s[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* arow = tile + (rb * 16 + c) * kPitch + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < kDqk / 32; ++ks)
-                s[rb] = mfma16x16x32(*reinterpret_cast<const bf16x8_t*>(arow + 32 * ks), qb[ks], s[rb]);
-        }
-        float x[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int rb = e >> 2, r = e & 3;
-            const float v = row_ok[rb * 16 + 4 * g + r] ? s[rb][r] * scale_log2 : -INFINITY;
-            x[e] = v;
-            mx = fmaxf(mx, v);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        if (__ballot(mx > m_ref + kRescaleSlack)) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float f = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
-#pragma unroll
-            for (int db = 0; db < kDv / 16; ++db) o[db] *= f;
-            lsum *= f;
-            m_ref = m_new;
-        }
-        const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-        // P^T operand: k-slot 8g+e holds row (e<4 ? 4g+e : 16+4g+e-4), i.e. this lane's own S^T values.
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t h = f32_to_bf16_rne(exp2f(x[e] - mu));
-            lsum += bf16_to_f32(h);
-            pb[e] = __builtin_bit_cast(__bf16, h);
-        }
-        // O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads]
-#pragma unroll
-        for (int db = 0; db < kDv / 16; ++db) {
-            const bf16x4_t lo = lds_read_tr16(tile + tr_row * kPitch + 16 * db + tr_col);
-            const bf16x4_t hi = lds_read_tr16(tile + (16 + tr_row) * kPitch + 16 * db + tr_col);
-            const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = mfma16x16x32(a, pb, o[db]);
-        }
+    for (int t = 0; t < kStages - 1 && t < ntiles; ++t)
+        gather_tile(kvb, rows_lds, t, nrows, L, tiles + t * (kTileChunks * 8), wave, lane);
+    for (int t = 0; t < ntiles; ++t) {
+        // refill the buffer released at the end of the previous step with tile t+3
+        if (t + kStages - 1 < ntiles)
+            gather_tile(kvb, rows_lds, t + kStages - 1, nrows, L, tiles + ((t + kStages - 1) % kStages) * (kTileChunks * 8),
+                        wave, lane);
+        // this thread's loads of tile t are done once at most the loads of the later tiles are outstanding
+        const int later = min(ntiles - 1 - t, kStages - 1);
+        if (later >= 3) wait_vmem<3 * kLoads>();
+        else if (later == 2) wait_vmem<2 * kLoads>();
+        else if (later == 1) wait_vmem<kLoads>();
+        else wait_vmem<0>();
+        lds_barrier();  // every thread's part of tile t is in LDS
+        attend_tile(tiles + (t % kStages) * (kTileChunks * 8), rows_lds, t, nrows, L, scale_log2, qb, lane, st);
+        lds_barrier();  // nobody reads buffer t % kStages any more
     }
 
+    float lsum = st.lsum;
+    const float m_ref = st.m_ref;
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
     const int head = 16 * wave + c;
+    const f32x4_t* o = st.o;
     if (DIRECT) {
         const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
         uint16_t* dst = out + ((int64_t)bt * kHq + head) * kDv + 4 * g;
@@ -162,37 +243,34 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     }
 }
 
-// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, in split order.
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                                const float* __restrict__ part_ml, int nsplit,
-                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int bt = blockIdx.x;
-    const float* pm = part_ml + (int64_t)bt * nsplit * kHq * 2;
-    for (int e = threadIdx.x; e < kHq * kDv / 4; e += kThreads) {
-        const int head = e / (kDv / 4);
-        const int d4 = e % (kDv / 4);
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[(s * kHq + head) * 2]);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        float den = 0.0f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const float ms = pm[(s * kHq + head) * 2];
-                if (ms == -INFINITY) continue;
-                const float a = exp2f(ms - M);
-                den += a * pm[(s * kHq + head) * 2 + 1];
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(
-                    part_o + (((int64_t)bt * nsplit + s) * kHq + head) * kDv + 4 * d4);
-                acc += a * v;
-            }
+// Merge split partials of one (query, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// summed in split order.  One 128-thread block per (query, head), 4 dims per thread.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml, int nsplit,
+                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int bt = blockIdx.x / kHq;
+    const int head = blockIdx.x % kHq;
+    const float* pm = part_ml + ((int64_t)bt * nsplit * kHq + head) * 2;  // split s at pm[s * kHq * 2]
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[(int64_t)s * kHq * 2]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.0f;
+    if (M != -INFINITY) {
+        const float* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
+        for (int s = 0; s < nsplit; ++s) {
+            const float ms = pm[(int64_t)s * kHq * 2];
+            if (ms == -INFINITY) continue;
+            const float a = exp2f(ms - M);
+            den += a * pm[(int64_t)s * kHq * 2 + 1];
+            acc += a * *reinterpret_cast<const f32x4_t*>(po + (int64_t)s * kHq * kDv);
         }
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-        uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-        *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * d4) = make_uint2(lo, hi);
-        if (lse && d4 == 0)
-            lse[(int64_t)bt * kHq + head] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
     }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+    uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) = make_uint2(lo, hi);
+    if (lse && threadIdx.x == 0)
+        lse[(int64_t)bt * kHq + head] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 struct SplitPlan {
@@ -234,8 +312,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     float* part_ml = part_o + (size_t)rows * p.nsplit * kHq * kDv;
     hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, q, kv, kv_bstride, idx, T, L,
                        k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_ml, nullptr, nullptr);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(rows), dim3(kThreads), 0, stream, part_o, part_ml, p.nsplit, out,
-                       lse);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)rows * kHq)), dim3(128), 0, stream, part_o, part_ml,
+                       p.nsplit, out, lse);
     return hipGetLastError();
 }
 

@@ -193,6 +193,10 @@ class GroupConfig:
             assert out.shape == shape and out.dtype == np.uint16
         return normal_bf16(self.seed, T_KV + layer, shape, out=out)
 
+    def kv_seq(self, layer: int, b: int) -> np.ndarray:
+        """kv[layer][b] alone, [1, L, Dqk]."""
+        return normal_bf16(self.seed, T_KV + layer, (1, self.L, self.Dqk), start=b * self.L * self.Dqk)
+
     def kv_rows(self, layer: int, b: int, rows: np.ndarray) -> np.ndarray:
         """kv[layer][b, rows, :] regenerated without building the cache."""
         rows = np.asarray(rows, np.int64)
