@@ -36,19 +36,24 @@ constexpr int kChunks = kDqk / 8;                 // 16-byte chunks per latent r
 constexpr int kTileChunks = kRows * kChunks;      // 2304 chunks = 36 KiB per tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kLoads = kTileChunks / kThreads;    // 9 direct-to-LDS loads per thread per tile
+constexpr int kLoads = 9;                         // direct-to-LDS loads per wave per tile: 8 row mains + 1 tail block
 constexpr int kStages = 4;                        // LDS tile buffers (3 tiles in flight + 1 computing)
 constexpr int kMaxSplitRows = 2048;
 constexpr int kTargetBlocks = 256;                // one resident block per CU
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs, block ids dealt round-robin
+#ifndef QK_AHEAD
+#define QK_AHEAD 2
+#endif
 constexpr float kRescaleSlack = 32.0f;            // log2 units: P < 2^32, |O| < 2^46 in fp32
 
 static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
 
-// Tile layout in LDS: row r, 16-byte chunk cc lives at chunk slot r*72 + (cc ^ (r & 7)).
-// The XOR spreads the 16 rows read by one MFMA operand over all LDS banks while
-// keeping each wave's 64 direct-to-LDS writes (one contiguous KiB) in place.
-__device__ __forceinline__ int slot(int r, int cc) { return r * kChunks + (cc ^ (r & 7)); }
+// Tile layout in LDS (36 KiB for 32 rows): the first 64 chunks (1 KiB) of row r
+// at byte r*1024 + 16*(c ^ (r & 15)) ("main"), the last 8 chunks at
+// 32 KiB + r*128 + 16*((c - 64) ^ (r & 7)) ("tail").  The XORs spread the 16
+// rows read by one MFMA operand over all LDS banks.  Value dims (the first 512)
+// live in the main part only.
+constexpr int kMainBytes = kRows * 1024;
 
 // One 16-byte-per-lane direct-to-LDS load: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
 // Issued from asm so that the compiler, which cannot tell which tile buffer the
@@ -59,23 +64,45 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_byte_add
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte_addr) : "memory", "m0");
 }
 
+// Same, with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
 
+// Gather tile t (rows t*32 .. t*32+31 of this split) into LDS at `tile`.  Wave w
+// loads the main KiB of rows 8w .. 8w+7 (one load per row: the row index is
+// wave-uniform, so the address is a scalar base plus this lane's swizzled
+// offset) and the tails of the same 8 rows (one load).  Masked or missing rows
+// read row 0 (finite values) and get P = 0.
 __device__ __forceinline__ void gather_tile(const uint16_t* __restrict__ kvb, const int* __restrict__ rows_lds,
                                             int t, int nrows, int L, const uint16_t* tile, int wave, int lane) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
+    const int r0 = 8 * wave;
+    // the wave's 8 row indices in two 16-byte LDS reads (rows_lds is padded to whole tiles)
+    const int4 ra = *reinterpret_cast<const int4*>(rows_lds + t * kRows + r0);
+    const int4 rb = *reinterpret_cast<const int4*>(rows_lds + t * kRows + r0 + 4);
+    const int rows8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int blk = kWaves * i + wave;              // this wave's KiB of the tile
-        const int p = 64 * blk + lane;                  // chunk slot written by this lane
-        const int r = p / kChunks;
-        const int cc = (p % kChunks) ^ (r & 7);         // logical chunk stored in that slot
+    for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        const int j = t * kRows + r;
+        int rid = j < nrows ? rows8[i] : 0;
+        rid = __builtin_amdgcn_readfirstlane((rid >= 0 && rid < L) ? rid : 0);
+        const uint32_t voff = (uint32_t)((lane ^ (r & 15)) << 4);
+        lds_dma16_sbase(kvb + (int64_t)rid * kDqk, voff, __builtin_amdgcn_readfirstlane(base + 1024u * r));
+    }
+    {
+        const int r = r0 + (lane >> 3);
         const int j = t * kRows + r;
         int rid = j < nrows ? rows_lds[j] : 0;
-        rid = (rid >= 0 && rid < L) ? rid : 0;          // masked rows read row 0 (finite) and get P = 0
-        lds_dma16(kvb + (int64_t)rid * kDqk + 8 * cc, __builtin_amdgcn_readfirstlane(base + 1024u * blk));
+        rid = (rid >= 0 && rid < L) ? rid : 0;
+        const int c = 64 + ((lane & 7) ^ (r & 7));
+        lds_dma16(kvb + (int64_t)rid * kDqk + 8 * c, __builtin_amdgcn_readfirstlane(base + kMainBytes + 1024u * wave));
     }
 }
 
@@ -98,69 +125,86 @@ struct SoftmaxState {
     float lsum;           // this lane's share of the softmax denominator
 };
 
-// Per-lane LDS read addresses of one tile (chunk units, relative to the tile),
-// split into a lane base plus compile-time offsets.  The swizzle XORs only the
-// low three bits of a chunk index, so for chunk = 8m + d it maps to
-// 8m + (d ^ (r & 7)): one base per value of d, the 8m part is an immediate.
+// Per-lane LDS read addresses of one tile (bytes, relative to the tile), split
+// into a lane base plus compile-time offsets.
+//   S^T A operand, row rr = c (+16 per row block), chunk x = 4ks + g:
+//     ks < 16: main, rr*1024 + 16*(16*(ks/4) + ((4*(ks%4) + g) ^ (rr & 15)))  -> qk[ks%4] + 256*(ks/4)
+//     ks >= 16: tail, 32K + rr*128 + 16*((4*(ks-16) + g) ^ (rr & 7))         -> qt[ks-16]
+//   V^T transpose read, row r = tr_row (+16), chunk 2db + q/2, byte 8*(q&1):
+//     r*1024 + 16*(16*(db/8) + ((2*(db%8) + q/2) ^ (r & 15))) + 8*(q&1)       -> tr[db%8] + 256*(db/8)
 struct TileAddr {
-    int qk[2];  // S^T A operand, row c (+16 per row block): chunks 8m + (4*(ks&1) + g) ^ (c&7)
-    int tr[4];  // V^T transpose reads, row tr_row (+16): chunks 8n + (2d + (lane&3)/2) ^ (tr_row&7)
+    int qk[4];
+    int qt[2];
+    int tr[8];
 };
 
 __device__ __forceinline__ TileAddr tile_addr(int lane) {
     const int c = lane & 15, g = lane >> 4;
     const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int q = lane & 3;
     TileAddr a;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) a.qk[par] = c * kChunks + ((4 * par + g) ^ (c & 7));
+    for (int m = 0; m < 4; ++m) a.qk[m] = c * 1024 + 16 * ((4 * m + g) ^ (c & 15));
 #pragma unroll
-    for (int d = 0; d < 4; ++d) a.tr[d] = tr_row * kChunks + ((2 * d + ((lane & 3) >> 1)) ^ (tr_row & 7));
+    for (int m = 0; m < 2; ++m) a.qt[m] = kMainBytes + c * 128 + 16 * ((4 * m + g) ^ (c & 7));
+#pragma unroll
+    for (int d = 0; d < 8; ++d) a.tr[d] = tr_row * 1024 + 16 * ((2 * d + (q >> 1)) ^ (tr_row & 15)) + 8 * (q & 1);
     return a;
 }
 
-// One tile of 32 gathered rows already resident in LDS at `tl`.
-__device__ __forceinline__ void attend_tile(const uint16_t* tl, const TileAddr& ad, const int* __restrict__ rows_lds,
-                                            int t, int nrows, int L, float scale_log2,
-                                            const bf16x8_t (&qb)[kDqk / 32], int lane, SoftmaxState& st) {
-    const int g = lane >> 4;
-    // S^T tile: rows (rb*16 + 4g + r) x head (16w + c); A operand = row (rb*16 + c), dims 32ks + 8g.
-    // Two independent accumulator chains (row blocks) share each q operand; the
-    // operand reads run kAhead k-steps ahead of the MFMAs (order pinned below).
+__device__ __forceinline__ int qk_offset(const TileAddr& ad, int ks) {
+    return ks < 16 ? ad.qk[ks & 3] + 256 * (ks >> 2) : ad.qt[ks - 16];
+}
+
+// S^T for one tile resident in LDS at `tl`: rows (rb*16 + 4g + r) x head (16w + c).
+// Two independent accumulator chains (row blocks) share each q operand; the operand
+// reads run kAhead k-steps ahead of the MFMAs.
+__device__ __forceinline__ void qk_tile(const uint16_t* tl, const TileAddr& ad, const bf16x8_t (&qb)[kDqk / 32],
+                                        f32x4_t (&s)[2]) {
     constexpr int kSteps = kDqk / 32;
-    constexpr int kAhead = 3;
-    f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    constexpr int kAhead = QK_AHEAD;
+    s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     bf16x8_t a[kSteps][2];
     auto load_a = [&](int ks) {
-        const uint16_t* p = tl + 8 * (ad.qk[ks & 1] + 8 * (ks >> 1));
+        const char* p = reinterpret_cast<const char*>(tl) + qk_offset(ad, ks);
         a[ks][0] = *reinterpret_cast<const bf16x8_t*>(p);
-        a[ks][1] = *reinterpret_cast<const bf16x8_t*>(p + 8 * 16 * kChunks);
+        a[ks][1] = *reinterpret_cast<const bf16x8_t*>(p + 16 * (ks < 16 ? 1024 : 128));
     };
 #pragma unroll
     for (int ks = 0; ks < kAhead; ++ks) load_a(ks);
-    __builtin_amdgcn_sched_group_barrier(0x0100, 2 * kAhead, 0);
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-        if (ks + kAhead < kSteps) {
-            load_a(ks + kAhead);
-            __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
-        }
+        if (ks + kAhead < kSteps) load_a(ks + kAhead);
         s[0] = mfma16x16x32(a[ks][0], qb[ks], s[0]);
         s[1] = mfma16x16x32(a[ks][1], qb[ks], s[1]);
-        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);
     }
+}
+
+// Online softmax of one S^T tile (bit r of `valid`: row r of the tile is visible):
+// updates the running reference maximum and denominator share, rescales the
+// accumulators if the reference moves, and returns this lane's P^T operand
+// (k-slot 8g+e holds row e<4 ? 4g+e : 16+4g+e-4, i.e. its own S^T values) in bf16.
+__device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, float scale_log2, int lane,
+                                                 SoftmaxState& st) {
+    const int g = lane >> 4;
     float x[8];
-    float mx = -INFINITY;
+    bool over = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int j = t * kRows + (e >> 2) * 16 + 4 * g + (e & 3);
-        const int rid = j < nrows ? rows_lds[j] : -1;
-        const float v = (rid >= 0 && rid < L) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        const int rr = (e >> 2) * 16 + 4 * g + (e & 3);
+        const float v = ((valid >> rr) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
         x[e] = v;
-        mx = fmaxf(mx, v);
+        over |= v > st.m_ref + kRescaleSlack;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (__ballot(mx > st.m_ref + kRescaleSlack)) {
+    // The exact tile maximum is only needed when the reference has to move
+    // (the first tile with a visible row, or a jump beyond the slack).
+    if (__ballot(over)) {
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         const float m_new = fmaxf(st.m_ref, mx);
         // While the reference is -inf nothing has been accumulated, so only a
         // finite old reference needs the accumulators rescaled.
@@ -177,7 +221,6 @@ __device__ __forceinline__ void attend_tile(const uint16_t* tl, const TileAddr& 
         st.m_ref = m_new;
     }
     const float mu = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-    // P^T operand: k-slot 8g+e holds row (e<4 ? 4g+e : 16+4g+e-4), i.e. this lane's own S^T values.
     bf16x8_t pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -185,15 +228,55 @@ __device__ __forceinline__ void attend_tile(const uint16_t* tl, const TileAddr& 
         st.lsum += bf16_to_f32(h);
         pb[e] = __builtin_bit_cast(__bf16, h);
     }
-    // O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads].
-    // Transpose-read addressing: lane (g, 4j+q) points at row 4g+j (+16), dims 4q..4q+3 of the block,
-    // i.e. chunk 2db + q/2, byte offset 8*(q&1).
-    const int off = 4 * (lane & 1);
+    return pb;
+}
+
+// P.V of the tile in `tv` fused with Q.K^T of the next tile in `tq`: the two are
+// independent, so alternating chunks of them (8 value blocks, then 4-5 k-steps)
+// gives the wave two instruction streams to overlap; the scheduling barriers
+// keep each chunk's operand reads from being hoisted all at once.
+__device__ __forceinline__ void pv_then_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad, bf16x8_t pb,
+                                           const bf16x8_t (&qb)[kDqk / 32], int lane, SoftmaxState& st,
+                                           f32x4_t (&s)[2]) {
+    s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int kChunksPv = 4;
+    constexpr int kDbPer = kDv / 16 / kChunksPv;  // 8 value blocks per chunk
+#pragma unroll
+    for (int ch = 0; ch < kChunksPv; ++ch) {
+#pragma unroll
+        for (int i = 0; i < kDbPer; ++i) {
+            const int db = ch * kDbPer + i;
+            const char* p = reinterpret_cast<const char*>(tv) + ad.tr[db & 7] + 256 * (db >> 3);
+            const bf16x4_t lo = lds_read_tr16(p);
+            const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
+            st.o[db] = mfma16x16x32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, st.o[db]);
+        }
+        // k-steps [ks0, ks1) of the next tile: 5, 5, 4, 4
+        const int ks0 = ch == 0 ? 0 : (ch == 1 ? 5 : (ch == 2 ? 10 : 14));
+        const int ks1 = ch == 0 ? 5 : (ch == 1 ? 10 : (ch == 2 ? 14 : 18));
+#pragma unroll
+        for (int ks = ks0; ks < ks1; ++ks) {
+            const char* p = reinterpret_cast<const char*>(tq) + qk_offset(ad, ks);
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + 16 * (ks < 16 ? 1024 : 128));
+            s[0] = mfma16x16x32(a0, qb[ks], s[0]);
+            s[1] = mfma16x16x32(a1, qb[ks], s[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads] for one tile.
+// Transpose-read addressing: lane (g, 4j+q) points at row 4g+j (+16), dims 4q..4q+3 of the block,
+// i.e. chunk 2db + q/2, byte offset 8*(q&1).
+__device__ __forceinline__ void pv_tile(const uint16_t* tl, const TileAddr& ad, bf16x8_t pb, int lane,
+                                        SoftmaxState& st) {
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) {
-        const uint16_t* p = tl + 8 * (ad.tr[db & 3] + 8 * (db >> 2)) + off;
+        const char* p = reinterpret_cast<const char*>(tl) + ad.tr[db & 7] + 256 * (db >> 3);
         const bf16x4_t lo = lds_read_tr16(p);
-        const bf16x4_t hi = lds_read_tr16(p + 8 * 16 * kChunks);
+        const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         st.o[db] = mfma16x16x32(a, pb, st.o[db]);
     }
@@ -224,17 +307,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int ntiles = (nrows + kRows - 1) / kRows;
 
     __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
-    __shared__ int rows_lds[kMaxSplitRows];
+    __shared__ __attribute__((aligned(16))) int rows_lds[kMaxSplitRows];
+    __shared__ uint32_t valid_lds[kMaxSplitRows / kRows];
 
     const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < nrows; j += kThreads) rows_lds[j] = sel[j];
-    __syncthreads();  // rows_lds ready
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) {
+        const int rid = j < nrows ? sel[j] : -1;
+        rows_lds[j] = rid;
+        // bit r of valid_lds[tile]: row r of that tile exists and indexes the cache
+        const uint64_t m = __ballot(rid >= 0 && rid < L);
+        if (lane == 0) {
+            valid_lds[j / kRows] = (uint32_t)m;
+            valid_lds[j / kRows + 1] = (uint32_t)(m >> 32);
+        }
+    }
+    __syncthreads();  // rows_lds, valid_lds ready
 
     // Start the first gathers, then fetch q while they are in flight.
     const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
     const TileAddr ad = tile_addr(lane);
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t)
         gather_tile(kvb, rows_lds, t, nrows, L, tiles + t * (kTileChunks * 8), wave, lane);
+
     // B operand of S^T: q[head 16w+c][32*ks + 8*g .. +7].
     bf16x8_t qb[kDqk / 32];
     {
@@ -252,21 +346,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qb[ks]));
 
-    for (int t = 0; t < ntiles; ++t) {
-        // refill the buffer released at the end of the previous step with tile t+3
-        if (t + kStages - 1 < ntiles)
-            gather_tile(kvb, rows_lds, t + kStages - 1, nrows, L, tiles + ((t + kStages - 1) % kStages) * (kTileChunks * 8),
-                        wave, lane);
-        // this thread's loads of tile t are done once at most the loads of the later tiles are outstanding
-        const int later = min(ntiles - 1 - t, kStages - 1);
-        if (later >= 3) wait_vmem<3 * kLoads>();
-        else if (later == 2) wait_vmem<2 * kLoads>();
+    // Software pipeline over tiles: iteration t runs P.V of tile t and Q.K^T of tile t+1
+    // side by side (independent work for the same wave), then the softmax of t+1.
+    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued here.
+    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
+    {
+        const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
+        if (later >= 2) wait_vmem<2 * kLoads>();
         else if (later == 1) wait_vmem<kLoads>();
         else wait_vmem<0>();
-        lds_barrier();  // every thread's part of tile t is in LDS
-        attend_tile(tiles + (t % kStages) * (kTileChunks * 8), ad, rows_lds, t, nrows, L, scale_log2, qb, lane, st);
+    }
+    lds_barrier();
+    f32x4_t s[2];
+    qk_tile(buf(0), ad, qb, s);
+    bf16x8_t pb = softmax_tile(s, valid_lds[0], scale_log2, lane, st);
+    // One code path per iteration (the last tile is peeled off below) so the
+    // accumulators stay in place across the loop back-edge.
+    for (int t = 0; t + 1 < ntiles; ++t) {
+        if (t + kStages - 1 < ntiles) gather_tile(kvb, rows_lds, t + kStages - 1, nrows, L, buf(t + kStages - 1), wave, lane);
+        // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
+        const int later = min(ntiles - 1, t + kStages - 1) - (t + 1);
+        if (later >= 2) wait_vmem<2 * kLoads>();
+        else if (later == 1) wait_vmem<kLoads>();
+        else wait_vmem<0>();
+        lds_barrier();  // every thread's part of tile t+1 is in LDS
+        const uint32_t valid = valid_lds[t + 1];
+        pv_then_qk(buf(t), buf(t + 1), ad, pb, qb, lane, st, s);
+        pb = softmax_tile(s, valid, scale_log2, lane, st);
         lds_barrier();  // nobody reads buffer t % kStages any more
     }
+    pv_tile(buf(ntiles - 1), ad, pb, lane, st);
 
     float lsum = st.lsum;
     const float m_ref = st.m_ref;
