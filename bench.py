@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -66,6 +68,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibrate:
+        copy_calibrate(torch)
+        return
 
     import long_context_sparse_scores_amd as dsa
     import synth
@@ -199,6 +205,19 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def copy_calibrate(torch):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings per
+    dispatch, divided by 1 GiB, calibrate the same counters on other kernels."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("bench: 5 copies of %d bytes done" % n)
 
 
 def cpu_baseline(cfg, target_s):
