@@ -60,6 +60,7 @@ extern "C" {
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
 #define DSA_GROUP_LAYERS_MAX 8
+#define DSA_ATTN_CONTEXT_MAX 4194304 /* rows per sequence the attention kernels address (2^22) */
 
 enum {
     DSA_OK = 0,
@@ -112,7 +113,7 @@ int dsa_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, int
  * accumulation, online softmax.
  *   q    [B,T,Hq,Dqk] bf16         kv row r of batch b at kv + b*kv_bstride + r*Dqk
  *   idx  [B,T,k] int32             out [B,T,Hq,Dv] bf16      lse [B,T,Hq] fp32 or NULL
- * Hq must be 64, Dqk 576, Dv 512; 1 <= k <= 2048. */
+ * Hq must be 64, Dqk 576, Dv 512; 1 <= k <= 2048; L <= DSA_ATTN_CONTEXT_MAX. */
 size_t dsa_attn_workspace_size(int B, int T, int k);
 int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                         int T, int L, int Hq, int Dqk, int Dv, int k, float sm_scale, uint16_t* out, float* lse,

@@ -19,10 +19,10 @@
 // Softmax is online in base 2 with a lazily moved reference maximum: the
 // accumulators are rescaled only when a tile's maximum exceeds the reference
 // by more than 32 (so P < 2^32 and the fp32 sums stay far from overflow);
-// after the first tile this practically never happens.  Splits write unnormalised
-// fp32 partial outputs plus (max, sum); a combine kernel, one block per
-// (query, head), merges them in split order.  A query whose list fits one
-// split is normalised and written directly.
+// after the first tile this practically never happens.  Splits write
+// normalised bf16 partial outputs plus their log2-sum-exp; a combine kernel,
+// one block per (query, head), merges them in split order.  A query whose
+// list fits one split is normalised and written directly.
 #include "common.h"
 
 namespace dsa {
@@ -74,13 +74,26 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
 
-// Gather tile t (rows t*32 .. t*32+31 of this split) into LDS at `tile`.  Wave w
-// loads the main KiB of rows 8w .. 8w+7 (one load per row: the row index is
-// wave-uniform, so the address is a scalar base plus this lane's swizzled
+// Gather of tile t (rows t*32 .. t*32+31 of this split) into LDS at `tile`.
+// Wave w loads the main KiB of rows 8w .. 8w+7 (one load per row: the row index
+// is wave-uniform, so the address is a scalar base plus this lane's swizzled
 // offset) and the tails of the same 8 rows (one load).  Masked or missing rows
-// read row 0 (finite values) and get P = 0.
-__device__ __forceinline__ void gather_tile(const uint16_t* __restrict__ kvb, const int* __restrict__ rows_lds,
-                                            int t, int nrows, int L, const uint16_t* tile, int wave, int lane) {
+// read row 0 (finite values) and get P = 0.  The plan is computed once; its nine
+// loads are then issued one at a time between matrix instructions, because a
+// wave stalls while the CU's address unit works through the loads ahead of
+// its own.
+struct GatherPlan {
+    const uint16_t* row[8];  // wave-uniform row bases
+    uint32_t lds[8];         // wave-uniform LDS byte addresses of the rows' main parts
+    uint32_t tail_off;       // this lane's 16-byte tail chunk: element offset from kvb
+    uint32_t lds_tail;
+    int xr;                  // (8w) & 15: row r = 8w + i has r & 15 == xr + i
+    bool active;             // wave-uniform: false when there is no tile left to gather
+};
+
+__device__ __forceinline__ GatherPlan plan_gather(const uint16_t* __restrict__ kvb, const int* __restrict__ rows_lds,
+                                                  int t, int nrows, int L, const uint16_t* tile, int wave, int lane) {
+    GatherPlan gp;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
     const int r0 = 8 * wave;
     // the wave's 8 row indices in two 16-byte LDS reads (rows_lds is padded to whole tiles)
@@ -89,12 +102,11 @@ __device__ __forceinline__ void gather_tile(const uint16_t* __restrict__ kvb, co
     const int rows8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        const int j = t * kRows + r;
+        const int j = t * kRows + r0 + i;
         int rid = j < nrows ? rows8[i] : 0;
         rid = __builtin_amdgcn_readfirstlane((rid >= 0 && rid < L) ? rid : 0);
-        const uint32_t voff = (uint32_t)((lane ^ (r & 15)) << 4);
-        lds_dma16_sbase(kvb + (int64_t)rid * kDqk, voff, __builtin_amdgcn_readfirstlane(base + 1024u * r));
+        gp.row[i] = kvb + (int64_t)rid * kDqk;
+        gp.lds[i] = __builtin_amdgcn_readfirstlane(base + 1024u * (r0 + i));
     }
     {
         const int r = r0 + (lane >> 3);
@@ -102,8 +114,29 @@ __device__ __forceinline__ void gather_tile(const uint16_t* __restrict__ kvb, co
         int rid = j < nrows ? rows_lds[j] : 0;
         rid = (rid >= 0 && rid < L) ? rid : 0;
         const int c = 64 + ((lane & 7) ^ (r & 7));
-        lds_dma16(kvb + (int64_t)rid * kDqk + 8 * c, __builtin_amdgcn_readfirstlane(base + kMainBytes + 1024u * wave));
+        gp.tail_off = (uint32_t)rid * kDqk + 8 * c;  // fits: L <= 2^22 rows is checked at the boundary
+        gp.lds_tail = __builtin_amdgcn_readfirstlane(base + kMainBytes + 1024u * wave);
     }
+    gp.xr = r0 & 15;
+    gp.active = true;
+    return gp;
+}
+
+// Load i of the plan: i < 8 the main part of row 8w+i, i == 8 the tails.
+__device__ __forceinline__ void issue_gather(const GatherPlan& gp, const uint16_t* kvb, int i, int lane) {
+    if (!gp.active) return;
+    if (i < 8)
+        lds_dma16_sbase(gp.row[i], (uint32_t)((lane ^ (gp.xr + i)) << 4), gp.lds[i]);
+    else
+        lds_dma16(kvb + gp.tail_off, gp.lds_tail);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), packed low-first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <int N>
@@ -221,27 +254,31 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
         st.m_ref = m_new;
     }
     const float mu = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-    bf16x8_t pb;
+    u32x4_t pw;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint16_t h = f32_to_bf16_rne(exp2f(x[e] - mu));
-        st.lsum += bf16_to_f32(h);
-        pb[e] = __builtin_bit_cast(__bf16, h);
+    for (int e = 0; e < 8; e += 2) {
+        const uint32_t h2 = pack_bf16x2(exp2f(x[e] - mu), exp2f(x[e + 1] - mu));
+        st.lsum += __uint_as_float(h2 << 16) + __uint_as_float(h2 & 0xFFFF0000u);  // the bf16 values P uses
+        pw[e / 2] = h2;
     }
-    return pb;
+    return __builtin_bit_cast(bf16x8_t, pw);
 }
 
 // P.V of the tile in `tv` fused with Q.K^T of the next tile in `tq`: the two are
 // independent, so alternating chunks of them (8 value blocks, then 4-5 k-steps)
 // gives the wave two instruction streams to overlap; the scheduling barriers
-// keep each chunk's operand reads from being hoisted all at once.
+// keep each chunk's operand reads from being hoisted all at once.  When `gp` is
+// active, its nine loads are issued two per chunk (plus one up front), each
+// behind a few matrix instructions that keep the matrix unit busy while the
+// wave waits for the address unit to accept the load.
 __device__ __forceinline__ void pv_then_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad, bf16x8_t pb,
                                            const bf16x8_t (&qb)[kDqk / 32], int lane, SoftmaxState& st,
-                                           f32x4_t (&s)[2]) {
+                                           f32x4_t (&s)[2], const GatherPlan& gp, const uint16_t* kvb) {
     s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     constexpr int kChunksPv = 4;
     constexpr int kDbPer = kDv / 16 / kChunksPv;  // 8 value blocks per chunk
+    issue_gather(gp, kvb, 8, lane);
 #pragma unroll
     for (int ch = 0; ch < kChunksPv; ++ch) {
 #pragma unroll
@@ -251,6 +288,7 @@ __device__ __forceinline__ void pv_then_qk(const uint16_t* tv, const uint16_t* t
             const bf16x4_t lo = lds_read_tr16(p);
             const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
             st.o[db] = mfma16x16x32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, st.o[db]);
+            if (i == 3) issue_gather(gp, kvb, 2 * ch, lane);
         }
         // k-steps [ks0, ks1) of the next tile: 5, 5, 4, 4
         const int ks0 = ch == 0 ? 0 : (ch == 1 ? 5 : (ch == 2 ? 10 : 14));
@@ -262,6 +300,7 @@ __device__ __forceinline__ void pv_then_qk(const uint16_t* tv, const uint16_t* t
             const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + 16 * (ks < 16 ? 1024 : 128));
             s[0] = mfma16x16x32(a0, qb[ks], s[0]);
             s[1] = mfma16x16x32(a1, qb[ks], s[1]);
+            if (ks == ks0 + 1) issue_gather(gp, kvb, 2 * ch + 1, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -310,6 +349,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ __attribute__((aligned(16))) int rows_lds[kMaxSplitRows];
     __shared__ uint32_t valid_lds[kMaxSplitRows / kRows];
 
+    // B operand of S^T: q[head 16w+c][32*ks + 8*g .. +7], loaded while the row
+    // list is fetched so that the two latencies overlap.
+    bf16x8_t qb[kDqk / 32];
+    {
+        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * wave + c) * kDqk + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
+    }
     const int32_t* sel = idx + (int64_t)bt * k + j0;
     for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) {
         const int rid = j < nrows ? sel[j] : -1;
@@ -321,34 +368,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             valid_lds[j / kRows + 1] = (uint32_t)(m >> 32);
         }
     }
+    // Consume q here so the compiler's own wait for these loads (it cannot see the
+    // gathers, which are issued from asm) stays ahead of the first gather.
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qb[ks]));
     __syncthreads();  // rows_lds, valid_lds ready
 
-    // Start the first gathers, then fetch q while they are in flight.
+    // Start the first gathers.
     const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
     const TileAddr ad = tile_addr(lane);
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t)
-        gather_tile(kvb, rows_lds, t, nrows, L, tiles + t * (kTileChunks * 8), wave, lane);
-
-    // B operand of S^T: q[head 16w+c][32*ks + 8*g .. +7].
-    bf16x8_t qb[kDqk / 32];
-    {
-        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * wave + c) * kDqk + 8 * g;
+    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
+        const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, tiles + t * (kTileChunks * 8), wave, lane);
 #pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
+        for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
     }
+
     SoftmaxState st;
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) st.o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     st.m_ref = -INFINITY;
     st.lsum = 0.0f;
-    // Consume q here so the compiler's own wait for these loads happens before the
-    // tile loop, not inside it where it would also drain later gathers.
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qb[ks]));
 
     // Software pipeline over tiles: iteration t runs P.V of tile t and Q.K^T of tile t+1
     // side by side (independent work for the same wave), then the softmax of t+1.
-    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued here.
+    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
     auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
     {
         const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
@@ -363,15 +406,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // One code path per iteration (the last tile is peeled off below) so the
     // accumulators stay in place across the loop back-edge.
     for (int t = 0; t + 1 < ntiles; ++t) {
-        if (t + kStages - 1 < ntiles) gather_tile(kvb, rows_lds, t + kStages - 1, nrows, L, buf(t + kStages - 1), wave, lane);
         // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
-        const int later = min(ntiles - 1, t + kStages - 1) - (t + 1);
-        if (later >= 2) wait_vmem<2 * kLoads>();
-        else if (later == 1) wait_vmem<kLoads>();
+        const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
+        if (later >= 1) wait_vmem<kLoads>();
         else wait_vmem<0>();
-        lds_barrier();  // every thread's part of tile t+1 is in LDS
+        lds_barrier();  // every thread's part of tile t+1 is in LDS; buffer (t+3) % 4 is free
         const uint32_t valid = valid_lds[t + 1];
-        pv_then_qk(buf(t), buf(t + 1), ad, pb, qb, lane, st, s);
+        // tile t+3 (if any) is gathered while this iteration computes
+        GatherPlan gp = plan_gather(kvb, rows_lds, min(t + kStages - 1, ntiles - 1), nrows, L, buf(t + kStages - 1),
+                                    wave, lane);
+        gp.active = t + kStages - 1 < ntiles;
+        pv_then_qk(buf(t), buf(t + 1), ad, pb, qb, lane, st, s, gp, kvb);
         pb = softmax_tile(s, valid, scale_log2, lane, st);
         lds_barrier();  // nobody reads buffer t % kStages any more
     }
@@ -383,66 +428,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     lsum += __shfl_xor(lsum, 32, kWave);
     const int head = 16 * wave + c;
     const f32x4_t* o = st.o;
-    if (DIRECT) {
-        const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-        uint16_t* dst = out + ((int64_t)bt * kHq + head) * kDv + 4 * g;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    uint16_t* dst = DIRECT ? out + ((int64_t)bt * kHq + head) * kDv + 4 * g
+                           : part_o + (((int64_t)bt * nsplit + split) * kHq + head) * kDv + 4 * g;
 #pragma unroll
-        for (int db = 0; db < kDv / 16; ++db) {
-            uint32_t lo = (uint32_t)f32_to_bf16_rne(o[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][1] * inv) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16_rne(o[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][3] * inv) << 16);
-            *reinterpret_cast<uint2*>(dst + 16 * db) = make_uint2(lo, hi);
-        }
+    for (int db = 0; db < kDv / 16; ++db)
+        *reinterpret_cast<uint2*>(dst + 16 * db) =
+            make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
+    if (DIRECT) {
         if (lse && g == 0)
             lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (m_ref + log2f(lsum)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        // Normalised partial output (bf16) and its log2-sum-exp; an empty split has lse -inf.
-        const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-        uint16_t* po = part_o + (((int64_t)bt * nsplit + split) * kHq + head) * kDv + 4 * g;
-#pragma unroll
-        for (int db = 0; db < kDv / 16; ++db) {
-            uint32_t lo = (uint32_t)f32_to_bf16_rne(o[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][1] * inv) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16_rne(o[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[db][3] * inv) << 16);
-            *reinterpret_cast<uint2*>(po + 16 * db) = make_uint2(lo, hi);
-        }
-        if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
+        return;
     }
+    // Normalised partial output (bf16) and its log2-sum-exp; an empty split has lse -inf.
+    if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
 }
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
-// split s, out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), in split order.
-// One 128-thread block per (query, head), 4 dims per thread; blocks numbered
-// like the split kernel so each reads partials from its own XCD's L2.
-__global__ __launch_bounds__(128) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse, int rows, int nsplit,
-                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
+// split s, out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
+// summed in split order.  One 128-thread block per (query, head), 4 dims per
+// thread; blocks numbered like the split kernel so each reads partials from its
+// own XCD's L2.  The split weights go through LDS while the partial loads are
+// already in flight.
+constexpr int kCombineThreads = 128;
+constexpr int kCombineBatch = 16;  // splits loaded per round
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
+                                                                       const float* __restrict__ part_lse, int rows,
+                                                                       int nsplit, uint16_t* __restrict__ out,
+                                                                       float* __restrict__ lse) {
     const int grp = blockIdx.x / (kXcds * kHq);
     const int rem = blockIdx.x % (kXcds * kHq);
     const int head = rem / kXcds;
     const int bt = grp * kXcds + rem % kXcds;
     if (bt >= rows) return;
+    __shared__ float wl[kMaxSplitRows / kRows];  // per split: log2-sum-exp, then weight
+    __shared__ float stat[2];
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pl[(int64_t)s * kHq]);
+    const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.0f;
-    if (M != -INFINITY) {
-        const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
-        for (int s = 0; s < nsplit; ++s) {
-            const float ls = pl[(int64_t)s * kHq];
-            if (ls == -INFINITY) continue;
-            const float a = exp2f(ls - M);
-            den += a;
-            const uint2 v = *reinterpret_cast<const uint2*>(po + (int64_t)s * kHq * kDv);
-            acc[0] += a * __uint_as_float(v.x << 16);
-            acc[1] += a * __uint_as_float(v.x & 0xFFFF0000u);
-            acc[2] += a * __uint_as_float(v.y << 16);
-            acc[3] += a * __uint_as_float(v.y & 0xFFFF0000u);
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        uint2 v[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sp = min(s0 + u, nsplit - 1);  // past the end: a valid split, weight 0 below
+            v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
+        }
+        if (s0 == 0) {
+            for (int sp = threadIdx.x; sp < nsplit; sp += kCombineThreads) wl[sp] = pl[(int64_t)sp * kHq];
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float M = -INFINITY;
+                for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wl[sp]);
+                float den = 0.0f;
+                if (M != -INFINITY)
+                    for (int sp = 0; sp < nsplit; ++sp) {
+                        const float a = wl[sp] == -INFINITY ? 0.0f : exp2f(wl[sp] - M);
+                        wl[sp] = a;
+                        den += a;
+                    }
+                else
+                    for (int sp = 0; sp < nsplit; ++sp) wl[sp] = 0.0f;
+                stat[0] = M;
+                stat[1] = den;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const float a = s0 + u < nsplit ? wl[s0 + u] : 0.0f;
+            acc[0] += a * __uint_as_float(v[u].x << 16);
+            acc[1] += a * __uint_as_float(v[u].x & 0xFFFF0000u);
+            acc[2] += a * __uint_as_float(v[u].y << 16);
+            acc[3] += a * __uint_as_float(v[u].y & 0xFFFF0000u);
         }
     }
+    const float M = stat[0], den = stat[1];
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-    uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-    *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) =
+        make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
     if (lse && threadIdx.x == 0)
         lse[(int64_t)bt * kHq + head] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
@@ -492,8 +556,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q, kv,
                        kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
                        nullptr, nullptr);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(128), 0, stream, part_o, part_lse, rows,
-                       p.nsplit, out, lse);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
+                       part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
 }
 

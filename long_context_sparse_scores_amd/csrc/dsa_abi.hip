@@ -63,6 +63,7 @@ int check_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const 
                int Hq, int Dqk, int Dv, int k, float sm_scale, const uint16_t* out, const float* lse) {
     if (!q || !kv || !idx || !out) return fail(DSA_ERR_NULL, "attn: NULL pointer argument");
     if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "attn: B=%d T=%d L=%d must be >= 1", B, T, L);
+    if (L > DSA_ATTN_CONTEXT_MAX) return fail(DSA_ERR_SHAPE, "attn: L=%d above %d", L, DSA_ATTN_CONTEXT_MAX);
     if (Hq != DSA_ATTN_HEADS || Dqk != DSA_LATENT_DIM || Dv != DSA_VALUE_DIM)
         return fail(DSA_ERR_UNSUPPORTED, "attn: Hq=%d Dqk=%d Dv=%d, supported %d/%d/%d", Hq, Dqk, Dv, DSA_ATTN_HEADS,
                     DSA_LATENT_DIM, DSA_VALUE_DIM);

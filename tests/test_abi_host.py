@@ -75,6 +75,10 @@ def test_validation_rejects_before_launch(dsa):
     # bad shapes
     assert lib.dsa_indexer_scores(fake, fake, fake, 0, fake, 1, 0, 16, 32, 128, fake, None) == -2
     assert lib.dsa_indexer_scores(fake, fake, fake, 100, fake, 2, 1, 16, 32, 128, fake, None) == -2  # stride < L*D
+    big_l = (1 << 22) + 1  # above the attention's addressable context
+    assert lib.dsa_sparse_mla_attn(fake, fake, big_l * 576, fake, 1, 1, big_l, 64, 576, 512, 16, 0.1, fake, None,
+                                   None, 0, None) == -2
+    assert "above" in dsa.last_error()
     # misalignment
     assert lib.dsa_indexer_scores(fake + 2, fake, fake, 16 * 128, fake, 1, 1, 16, 32, 128, fake, None) == -4
     # workspace too small
