@@ -78,12 +78,24 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* scratc
 }
 
 // ------------------------------------------------------------- launch interfaces
+// Words [r*stride, r*stride + count) of a uint32 buffer, for every row r: a
+// range some later kernel needs zeroed, which the indexer clears on the way.
+struct ZeroRange {
+    uint32_t* base = nullptr;
+    int64_t stride = 0;
+    int count = 0;
+};
+
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                          const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream);
+                          const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                          ZeroRange zero = ZeroRange());
 
 size_t topk_ws_bytes(int rows, int L, int k);
+// The part of the top-k workspace that must be zero when the selection starts.
+ZeroRange topk_state_range(void* ws, int rows, int L);
+// state_zeroed: the caller has already cleared topk_state_range (e.g. through the indexer).
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool state_zeroed = false);
 
 int attn_num_splits(int rows, int k);
 size_t attn_ws_bytes(int rows, int k);

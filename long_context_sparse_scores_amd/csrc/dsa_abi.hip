@@ -166,9 +166,11 @@ int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* st
     void* topk_ws = base + dsa::align_up((size_t)rows * L * sizeof(float), 256);
     void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores, s);
+    // the indexer also clears the top-k state, which saves the selection a launch
+    hipError_t e = dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores, s,
+                                       dsa::topk_state_range(topk_ws, rows, L));
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
-    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s);
+    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s, /*state_zeroed=*/true);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
     for (int l = 0; l < a->n_layers; ++l) {
         e = dsa::launch_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, k, a->sm_scale, a->out[l],

@@ -44,7 +44,8 @@ constexpr int kAhead = INDEXER_AHEAD;          // tiles loaded ahead of the one 
 template <int kWaves, int kTilesPerWave>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores) {
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
+    ZeroRange zero) {
     constexpr int kKeysPerBlock = kWaves * kTile * kTilesPerWave;
     __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * 2 * kTileBytes / 2];
     const int row = blockIdx.x / nblk;  // b*T + t
@@ -55,6 +56,8 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     const int c = lane & 15;  // key within tile (B/C column)
     const int g = lane >> 4;  // lane group: 8-dim slice of each 32-dim step; head row block in C
     const int64_t p = q_pos[row];
+    if (zero.base && blk == 0)
+        for (int i = threadIdx.x; i < zero.count; i += kWaves * kWave) zero.base[row * zero.stride + i] = 0u;
 
     // A operands: q rows (heads) 16*ht + c, dims 32*kk + 8*g .. +7.
     bf16x8_t qa[2][4];
@@ -132,19 +135,21 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
 
 template <int W, int N>
 hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                              const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream) {
+                              const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                              ZeroRange zero) {
     constexpr int keys_per_block = W * kTile * N;
     const int nblk = (L + keys_per_block - 1) / keys_per_block;
     dim3 grid((unsigned)((int64_t)nblk * B * T));
     hipLaunchKernelGGL((indexer_decode_kernel<W, N>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx, k_bstride,
-                       q_pos, T, L, nblk, scores);
+                       q_pos, T, L, nblk, scores, zero);
     return hipGetLastError();
 }
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                          const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream) {
+                          const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                          ZeroRange zero) {
     return launch_indexer_cfg<INDEXER_WAVES, INDEXER_TILES>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores,
-                                                            stream);
+                                                            stream, zero);
 }
 
 }  // namespace dsa

@@ -492,11 +492,21 @@ size_t topk_ws_bytes(int rows, int L, int k) {
     return align_up((size_t)rows * make_layout(rows, L).row_words() * sizeof(uint32_t), 256);
 }
 
+ZeroRange topk_state_range(void* ws, int rows, int L) {
+    (void)rows;
+    const Layout lo = make_layout(rows, L);
+    ZeroRange z;
+    z.base = reinterpret_cast<uint32_t*>(ws);  // each row's words start with hist1, then the counters
+    z.stride = (int64_t)lo.row_words();
+    z.count = kBins + kCtrWords;
+    return z;
+}
+
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool state_zeroed) {
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
-    hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
+    if (!state_zeroed) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_resolve_kernel, dim3(rows), dim3(kResolveThreads), 0, stream, scores, q_pos, L, k, lo,
