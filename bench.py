@@ -12,6 +12,12 @@ roofline of the dominant kernel (the index-key scan), a per-phase breakdown
 and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Other workloads (--workload): decode_1m_b4 and tiny_decode_8k time the same
+group step; prefill_4096_at_128k times it for a 4096-query chunk and reports
+the fraction of the bf16 MFMA peak; mtp_draft_b16_128k times one MTP draft
+round (step-1 indexer and top-k over the backbone index keys, 7 attention
+steps over the backbone latent cache with the step-1 list, verification).
 """
 import argparse
 import json
@@ -23,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "query-tokens/sec per 4-layer DSA group at 128K ctx; % of HBM roofline"
 
 
@@ -36,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_128k_b32",
-                    help="decode_128k_b32 (default), decode_1m_b4, prefill_4096_at_128k, tiny_decode_8k")
+                    help="decode_128k_b32 (default), decode_1m_b4, prefill_4096_at_128k, tiny_decode_8k, "
+                         "mtp_draft_b16_128k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
@@ -77,7 +85,9 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.workload]
-    assert isinstance(cfg, synth.GroupConfig)
+    if isinstance(cfg, synth.MtpConfig):
+        bench_mtp(cfg, args)
+        return
     dev = torch.device("cuda:0")
     B, T, L, k, nl = cfg.B, cfg.T, cfg.L, cfg.k, cfg.n_layers
     log("bench: workload %s B=%d T=%d L=%d k=%d layers=%d" % (cfg.name, B, T, L, k, nl))
@@ -175,8 +185,17 @@ def main():
 
     qtok = B * T
     value = qtok / (ms / 1e3)
-    step_bytes = qtok * synth.group_bytes_per_query(cfg)
+    if T == 1:
+        step_bytes = qtok * synth.group_bytes_per_query(cfg)
+    else:
+        # a chunk of queries shares one key scan and gathers rows out of the same
+        # cached layers: count each cache byte once, plus per-query inputs and outputs
+        step_bytes = (B * L * cfg.D * 2 + qtok * (cfg.H * cfg.D * 2 + cfg.H * 4 + k * 4)
+                      + nl * (B * min(L, T * k) * cfg.Dqk * 2 + qtok * cfg.Hq * (cfg.Dqk + cfg.Dv) * 2))
     achieved = idx_bytes / (idx_ms / 1e3) / 1e9
+    pos = cfg.q_pos().astype(np.int64)
+    idx_flops = int(((np.minimum(pos, L - 1) + 1) * cfg.H * cfg.D * 2).sum())
+    attn_flops = nl * qtok * cfg.Hq * k * (cfg.Dqk + cfg.Dv) * 2
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -202,6 +221,11 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": None,
     }
+    if T > 1:  # a prefill chunk is a dense contraction: report the matrix-core fraction as well
+        tflops = (idx_flops + attn_flops) / (ms / 1e3) / 1e12
+        line["mfma"] = {"flops_per_step": idx_flops + attn_flops, "achieved_tflops": round(tflops, 1),
+                        "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "indexer_tflops": round(idx_flops / (idx_ms / 1e3) / 1e12, 1)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -232,23 +256,162 @@ def cpu_baseline(cfg, target_s):
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
     done, spent = 0, 0.0
     b = 0
+    rows_per_call = min(cfg.T, 4)  # long chunks: a few query rows at a time, scaled by query tokens
+    t_next = 0
     while spent < target_s and b < cfg.B:
-        qi = cfg.q_idx()[b:b + 1]
-        w = cfg.w()[b:b + 1]
+        t1 = min(cfg.T, t_next + rows_per_call)
+        sl = slice(t_next, t1)
+        qi = cfg.q_idx()[b:b + 1, sl]
+        w = cfg.w()[b:b + 1, sl]
         ki = cfg.k_idx_rows(b)[None]
-        pos = cfg.q_pos()[b:b + 1]
-        qs = [cfg.q_attn(l)[b:b + 1] for l in range(cfg.n_layers)]
+        pos = cfg.q_pos()[b:b + 1, sl]
+        qs = [cfg.q_attn(l)[b:b + 1, sl] for l in range(cfg.n_layers)]
         kvs = [cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
         t0 = time.perf_counter()
         oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
         spent += time.perf_counter() - t0
-        done += cfg.T
-        b += 1
-        log("bench: cpu oracle %d sequence(s), %.2f s" % (b, spent))
+        done += t1 - t_next
+        t_next = t1
+        if t_next >= cfg.T:
+            b, t_next = b + 1, 0
+        log("bench: cpu oracle %d query token(s), %.2f s" % (done, spent))
     return {"value": round(done / spent, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (%d query tokens) of %s, whole pipeline per sequence: indexer over "
-                      "all %d keys, top-%d, %d attention layers; fp64 plain C with OpenMP"
-                      % (b, cfg.B, done, cfg.name, cfg.L, cfg.k, cfg.n_layers)}
+            "sample": "%d query tokens of %s (%d sequences x %d tokens), the whole pipeline per token: indexer over "
+                      "the visible keys, top-%d, %d attention layers; fp64 plain C with OpenMP"
+                      % (done, cfg.name, cfg.B, cfg.T, cfg.k, cfg.n_layers)}
+
+
+def bench_mtp(cfg, args):
+    """One MTP draft round per step, B sequences: the step-1 indexer and top-k
+    over the backbone index keys, attention of the 7 draft steps over the
+    backbone latent rows with the step-1 list, then verification of the 7
+    drafts (sum-min, accept loop, resample) over the full vocabulary."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_scores_amd as dsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    B, L, S, V, k = cfg.B, cfg.L, cfg.S, cfg.V, cfg.k
+    log("bench: workload %s B=%d L=%d steps=%d V=%d" % (cfg.name, B, L, S, V))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.time()
+    q_idx, w, pos = bf(cfg.q_idx()), torch.from_numpy(cfg.w()).to(dev), torch.from_numpy(cfg.q_pos()).to(dev)
+    k_idx, kv = bf(cfg.k_idx()), bf(cfg.kv())
+    q_steps = [bf(np.ascontiguousarray(cfg.q_steps()[:, s:s + 1])) for s in range(S)]
+    target = cfg.target_logits()
+    draft = cfg.draft_logits(target)
+    tok = cfg.draft_tokens(draft)
+    t_d, d_d = torch.from_numpy(target).to(dev), torch.from_numpy(draft).to(dev)
+    tok_d = torch.from_numpy(tok).to(dev)
+    u_d, ur_d = torch.from_numpy(cfg.u_accept()).to(dev), torch.from_numpy(cfg.u_resample()).to(dev)
+    torch.cuda.synchronize()
+    log("bench: inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
+
+    scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, 1, cfg.Hq, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    topk_ws = torch.empty(dsa.topk_workspace_size(B, 1, L, k), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, 1, k)), dtype=torch.uint8, device=dev)
+    ver_ws = torch.empty(dsa.verify_workspace_size(B, S, V), dtype=torch.uint8, device=dev)
+
+    def indexer_step():
+        dsa.indexer_scores(q_idx, w, k_idx, pos, scores=scores)
+
+    def round_step():
+        indexer_step()
+        dsa.topk(scores, pos, k, idx=idx, ws=topk_ws)
+        for s in range(S):
+            dsa.sparse_mla_attn(q_steps[s], kv, idx, cfg.sm_scale, out=outs[s], ws=attn_ws)
+        return dsa.mtp_draft_verify(t_d, d_d, tok_d, u_d, ur_d, ws=ver_ws)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(round_step, args.steps)
+    idx_ms = timed(indexer_step, args.steps)
+    # per-phase breakdown, each entry point timed on its own
+    topk_ms = timed(lambda: dsa.topk(scores, pos, k, idx=idx, ws=topk_ws), args.steps)
+    attn_ms = timed(lambda: dsa.sparse_mla_attn(q_steps[1], kv, idx, cfg.sm_scale, out=outs[1], ws=attn_ws), args.steps)
+    ver_ms = timed(lambda: dsa.mtp_draft_verify(t_d, d_d, tok_d, u_d, ur_d, ws=ver_ws), args.steps)
+    breakdown = {"indexer_ms": round(idx_ms, 4), "topk_ms": round(topk_ms, 4), "attn_ms_per_step": round(attn_ms, 4),
+                 "verify_ms": round(ver_ms, 4)}
+    log("bench: breakdown %s" % breakdown)
+    _, n_acc, _ = round_step()
+    accept_len = float(n_acc.float().mean().item()) + 1.0
+    step1 = L * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4 + k * 4
+    attn_step = k * cfg.Dqk * 2 + cfg.Hq * cfg.Dqk * 2 + cfg.Hq * cfg.Dv * 2 + k * 4
+    verify = (2 * S + 1) * V * 4 + S * 4 * 3 + 4
+    seq_bytes = step1 + S * attn_step + verify
+    idx_bytes = B * (L * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4)
+    achieved = idx_bytes / (idx_ms / 1e3) / 1e9
+    log("bench: round %.3f ms, indexer %.3f ms" % (ms, idx_ms))
+    line = {
+        "metric": "MTP draft rounds (sequence-rounds/s) at 128K ctx, 7 steps; % of HBM roofline",
+        "value": round(B / (ms / 1e3), 1),
+        "unit": "sequence-rounds/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; GLM-5.2 shapes)",
+        "config": {"workload": cfg.name, "batch": B, "context": L, "draft_steps": S, "vocab": V, "topk": k},
+        "draft_steps_per_s": round(B * S / (ms / 1e3), 1),
+        "mean_acceptance_length": round(accept_len, 3),
+        "hbm_roofline_frac": round(B * seq_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": B * seq_bytes,
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("indexer", cfg.name), "bytes_per_launch": idx_bytes,
+                     "avg_launch_ms": round(idx_ms, 4)},
+        "breakdown": breakdown,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_mtp(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_mtp(cfg, target_s):
+    """The CPU oracle on whole sequences of the MTP round: indexer over all
+    keys, top-k, the 7 attention steps, verification."""
+    import oracle
+    import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    target = cfg.target_logits()
+    draft = cfg.draft_logits(target)
+    tok = cfg.draft_tokens(draft)
+    u, ur = cfg.u_accept(), cfg.u_resample()
+    qsteps = cfg.q_steps()
+    done, spent = 0, 0.0
+    while spent < target_s and done < cfg.B:
+        b = done
+        t0 = time.perf_counter()
+        sc = oracle.indexer_scores(cfg.q_idx()[b:b + 1], cfg.w()[b:b + 1], cfg.k_idx_rows(b)[None],
+                                   cfg.q_pos()[b:b + 1])
+        idx = oracle.topk(sc, cfg.q_pos()[b:b + 1], cfg.k)
+        kv = synth.normal_bf16(cfg.seed, synth.T_KV, (1, cfg.L, cfg.Dqk), start=b * cfg.L * cfg.Dqk)
+        for s in range(cfg.S):
+            oracle.sparse_mla_attn(qsteps[b:b + 1, s:s + 1], kv, idx, cfg.sm_scale)
+        oracle.mtp_verify(target[b:b + 1], draft[b:b + 1], tok[b:b + 1], u[b:b + 1], ur[b:b + 1])
+        spent += time.perf_counter() - t0
+        done += 1
+        log("bench: cpu oracle %d sequence-round(s), %.2f s" % (done, spent))
+    return {"value": round(done / spent, 4), "unit": "sequence-rounds/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences of %s, the whole round per sequence; fp64 plain C with OpenMP"
+                      % (done, cfg.B, cfg.name)}
 
 
 if __name__ == "__main__":
