@@ -131,6 +131,137 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     }
 }
 
+// ------------------------------------------------------------------ multi-query (prefill) chunks
+// A chunk of T >= 8 queries of one sequence is a dense contraction: 32*T query
+// heads against every key, 2*32*128 flops per (query, key).  One 256-thread
+// workgroup takes 16 queries of one sequence and a range of keys; wave w holds
+// queries 4w..4w+3 (32 heads x 128 dims each) as MFMA A operands in registers.
+// Key tiles of 64 keys go through a double-buffered, swizzled LDS stage and
+// every B operand read from it feeds 8 MFMAs (4 queries x 2 head blocks).  The
+// ReLU, the head weights and the sum over heads are folded into the epilogue;
+// a 3-shuffle transpose-reduce leaves query 4w+g's score in lane group g, so
+// one store covers a 16-key sub-tile for the wave's 4 queries.
+constexpr int kPfQueries = 16;                 // queries per workgroup
+constexpr int kPfQPerWave = 4;
+constexpr int kPfTileKeys = 64;                // keys per LDS tile
+constexpr int kPfTileBytes = kPfTileKeys * kD * 2;   // 16 KiB
+constexpr int kPfKeysPerBlock = 2048;          // keys per workgroup
+constexpr int kPrefillMinQueries = 8;          // chunks of at least this many queries per sequence
+
+__global__ __launch_bounds__(256) void indexer_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb,
+    float* __restrict__ scores, ZeroRange zero) {
+    __shared__ __attribute__((aligned(16))) uint16_t stage[2 * kPfTileBytes / 2];
+    const int kb_i = blockIdx.x % nkb;           // key block
+    const int qg = (blockIdx.x / nkb) % nqg;     // query group within the sequence
+    const int b = blockIdx.x / (nkb * nqg);
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int t0 = qg * kPfQueries + kPfQPerWave * wave;  // this wave's first query
+
+    if (zero.base && kb_i == 0)  // rows of this group, once
+        for (int i = threadIdx.x; i < kPfQueries * zero.count; i += 256) {
+            const int t = qg * kPfQueries + i / zero.count;
+            if (t < T) zero.base[((int64_t)b * T + t) * zero.stride + i % zero.count] = 0u;
+        }
+
+    // A operands and head weights of the wave's 4 queries (past the end: the last query, never stored)
+    bf16x8_t qa[kPfQPerWave][2][4];
+    float wv[kPfQPerWave][2][4];
+    int64_t prow[kPfQPerWave];
+#pragma unroll
+    for (int i = 0; i < kPfQPerWave; ++i) {
+        const int t = min(t0 + i, T - 1);
+        const int64_t row = (int64_t)b * T + t;
+        const uint16_t* qrow = q_idx + row * kH * kD;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qa[i][ht][kk] = *reinterpret_cast<const bf16x8_t*>(qrow + (16 * ht + c) * kD + 32 * kk + 8 * g);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[i][ht][r] = w[row * kH + 16 * ht + 4 * g + r];
+        prow[i] = row;
+    }
+    // this lane stores query 4w+g
+    const int my_t = t0 + g;
+    const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
+    const int64_t my_p = q_pos[my_row];
+    float* my_out = scores + my_row * L;
+
+    const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
+    const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
+    const int ntiles = (int)((min((int64_t)L, key0 + kPfKeysPerBlock) - key0 + kPfTileKeys - 1) / kPfTileKeys);
+    // tile loads: thread (wave st, lane) brings chunk lane%16 of keys 16*st + 4i + lane/16, i < 4
+    u32x4_t ld[4];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t key = key0 + (int64_t)j * kPfTileKeys + 16 * wave + 4 * i + (lane >> 4);
+            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
+            ld[i] = *reinterpret_cast<const u32x4_t*>(kb + key * kD + 8 * (lane & 15));
+        }
+    };
+    auto store_tile = [&](int j) {  // chunk s of key k (within a 16-key sub-tile) at 16k + (s ^ k)
+        uint16_t* sub = stage + (j & 1) * (kPfTileBytes / 2) + wave * (16 * kD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 4 * i + (lane >> 4);
+            *reinterpret_cast<u32x4_t*>(sub + 8 * (16 * k + ((lane & 15) ^ k))) = ld[i];
+        }
+    };
+    load_tile(0);
+    store_tile(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int j = 0; j < ntiles; ++j) {
+        if (j + 1 < ntiles) load_tile(j + 1);  // in flight while tile j is computed
+        const uint16_t* tile = stage + (j & 1) * (kPfTileBytes / 2);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const uint16_t* sub = tile + st * (16 * kD);
+            bf16x8_t kv[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kv[kk] = *reinterpret_cast<const bf16x8_t*>(sub + 8 * (16 * c + ((4 * kk + g) ^ c)));
+            float part[kPfQPerWave];
+#pragma unroll
+            for (int i = 0; i < kPfQPerWave; ++i) {
+                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    a0 = mfma16x16x32(qa[i][0][kk], kv[kk], a0);
+                    a1 = mfma16x16x32(qa[i][1][kk], kv[kk], a1);
+                }
+                float v = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v = fmaf(wv[i][0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
+                    v = fmaf(wv[i][1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                }
+                part[i] = v;
+            }
+            // transpose-reduce over the 4 lane groups: group g ends with query g's total
+            const bool hi = (g & 2) != 0, lo = (g & 1) != 0;
+            const float r0 = __shfl_xor(hi ? part[0] : part[2], 32, kWave);
+            const float r1 = __shfl_xor(hi ? part[1] : part[3], 32, kWave);
+            const float k0 = (hi ? part[2] : part[0]) + r0;
+            const float k1 = (hi ? part[3] : part[1]) + r1;
+            const float rr = __shfl_xor(lo ? k0 : k1, 16, kWave);
+            const float score = (lo ? k1 : k0) + rr;
+            const int64_t key = key0 + (int64_t)j * kPfTileKeys + 16 * st + c;
+            if (my_t < T && key < L) my_out[key] = key <= my_p ? score : -INFINITY;
+        }
+        if (j + 1 < ntiles) store_tile(j + 1);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    (void)prow;
+}
+
 }  // namespace
 
 template <int W, int N>
@@ -148,6 +279,13 @@ hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint1
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                           const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
                           ZeroRange zero) {
+    if (T >= kPrefillMinQueries) {
+        const int nqg = (T + kPfQueries - 1) / kPfQueries;
+        const int nkb = (L + kPfKeysPerBlock - 1) / kPfKeysPerBlock;
+        hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)((int64_t)B * nqg * nkb)), dim3(256), 0, stream,
+                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
+        return hipGetLastError();
+    }
     return launch_indexer_cfg<INDEXER_WAVES, INDEXER_TILES>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores,
                                                             stream, zero);
 }

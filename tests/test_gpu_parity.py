@@ -43,6 +43,20 @@ def test_indexer_ragged_strided(dsa):
     np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+def test_indexer_multi_query_ragged(dsa):
+    # chunks of >= 8 queries take the multi-query path: a partial last group of 16
+    # queries, a ragged key tail, a strided cache and positions all over the range
+    B, T, L, Lc = 2, 21, 5000, 5104
+    say("indexer multi-query B=%d T=%d L=%d" % (B, T, L))
+    qi = synth.int_bf16(33, 1, (B, T, 32, 128))
+    w = synth.pow2_f32(33, 2, (B, T, 32))
+    ki = synth.int_bf16(33, 3, (B, Lc, 128))
+    pos = np.stack([np.arange(T, dtype=np.int32) * 211 + 7, np.arange(T, dtype=np.int32) + 4979]).astype(np.int32)
+    got = host(dsa.indexer_scores(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), L=L))
+    ref = oracle.indexer_scores(qi, w, ki, pos, L=L)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 def test_indexer_negative_weights(dsa):
     # general weights (not the test distribution): still exact for integer inputs
     B, T, L = 1, 2, 777
