@@ -37,8 +37,16 @@ constexpr int kTileChunks = kRows * kChunks;      // 2304 chunks = 36 KiB per ti
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLoads = 9;                         // direct-to-LDS loads per wave per tile: 8 row mains + 1 tail block
-constexpr int kStages = 4;                        // LDS tile buffers (3 tiles in flight + 1 computing)
-constexpr int kMaxSplitRows = 2048;
+// Splits of a query's list (decode): 4 tile buffers (3 tiles in flight) and
+// row lists of up to 1024 entries.  Whole lists (a query per workgroup, prefill
+// sized batches): 3 buffers and up to 2048 entries; that path is bound by the
+// matrix work, not by how many gathers are in flight.
+template <bool DIRECT> struct Cfg {
+    static constexpr int kStages = DIRECT ? 3 : 4;
+    static constexpr int kMaxRows = DIRECT ? 2048 : 1024;
+};
+constexpr int kMaxSplitRows = Cfg<false>::kMaxRows;
+constexpr int kMaxSplits = 2048 / kRows;          // k <= 2048
 constexpr int kTargetBlocks = 256;                // one resident block per CU
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs, block ids dealt round-robin
 #ifndef QK_AHEAD
@@ -152,10 +160,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work split inside the workgroup (wave w = 2*hh + kk):
+//   Q.K^T  wave w computes partial S^T for the 32 heads of head blocks 2hh and
+//          2hh+1 over k-steps 9kk .. 9kk+8 (latent dims 288kk .. +287), q in
+//          registers; partner waves w and w^1 swap the halves of the block the
+//          other one owns through LDS, so wave w ends with S^T of head block w.
+//   softmax  wave w, head block w (heads 16w .. 16w+15), into P^T (bf16) in LDS.
+//   P.V    wave w, value dims 128w .. 128w+127 of all 64 heads, with the four
+//          P^T blocks read from LDS.
+// Every tile is then read from LDS about 1.5 times per workgroup (Q.K^T
+// twice over half the dims, P.V once) instead of 4 times per phase.
 struct SoftmaxState {
-    f32x4_t o[kDv / 16];  // O^T accumulators: dims 16*db + 4g + r of head 16w + c
-    float m_ref;          // reference maximum (log2 units) of head 16w + c
-    float lsum;           // this lane's share of the softmax denominator
+    float m_ref;  // reference maximum (log2 units) of head 16w + c
+    float lsum;   // this lane's share of the softmax denominator of head 16w + c
+};
+
+struct PvAcc {
+    f32x4_t o[8][4];  // O^T: value dims 128w + 16d + 4g + r of head 16hb + c
 };
 
 // Per-lane LDS read addresses of one tile (bytes, relative to the tile), split
@@ -189,47 +210,29 @@ __device__ __forceinline__ int qk_offset(const TileAddr& ad, int ks) {
     return ks < 16 ? ad.qk[ks & 3] + 256 * (ks >> 2) : ad.qt[ks - 16];
 }
 
-// S^T for one tile resident in LDS at `tl`: rows (rb*16 + 4g + r) x head (16w + c).
-// Two independent accumulator chains (row blocks) share each q operand; the operand
-// reads run kAhead k-steps ahead of the MFMAs.
-__device__ __forceinline__ void qk_tile(const uint16_t* tl, const TileAddr& ad, const bf16x8_t (&qb)[kDqk / 32],
-                                        f32x4_t (&s)[2]) {
-    constexpr int kSteps = kDqk / 32;
-    constexpr int kAhead = QK_AHEAD;
-    s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a[kSteps][2];
-    auto load_a = [&](int ks) {
-        const char* p = reinterpret_cast<const char*>(tl) + qk_offset(ad, ks);
-        a[ks][0] = *reinterpret_cast<const bf16x8_t*>(p);
-        a[ks][1] = *reinterpret_cast<const bf16x8_t*>(p + 16 * (ks < 16 ? 1024 : 128));
-    };
-#pragma unroll
-    for (int ks = 0; ks < kAhead; ++ks) load_a(ks);
-#pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
-        if (ks + kAhead < kSteps) load_a(ks + kAhead);
-        s[0] = mfma16x16x32(a[ks][0], qb[ks], s[0]);
-        s[1] = mfma16x16x32(a[ks][1], qb[ks], s[1]);
-    }
-}
+// Rescale factors of a tile's softmax live in that tile's K-tail region once
+// Q.K^T has read it: float fac[4][16] (per head block, per head), then uint32
+// flag[4] (block hb moved its reference).  P.V of the same tile reads them.
+constexpr int kFacOffset = kMainBytes;
+constexpr int kFlagOffset = kMainBytes + 4 * 16 * 4;
 
-// Online softmax of one S^T tile (bit r of `valid`: row r of the tile is visible):
-// updates the running reference maximum and denominator share, rescales the
-// accumulators if the reference moves, and returns this lane's P^T operand
-// (k-slot 8g+e holds row e<4 ? 4g+e : 16+4g+e-4, i.e. its own S^T values) in bf16.
-__device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, float scale_log2, int lane,
-                                                 SoftmaxState& st) {
-    const int g = lane >> 4;
+// Online softmax of the S^T block of head block w for one tile (bit e of
+// `valid`: value e of this lane is a visible row).  Updates the reference
+// maximum and denominator share; when the reference moves, records the factor
+// the P.V accumulators of these heads must be scaled by.  Returns P^T (k-slot
+// 8g+e holds row e<4 ? 4g+e : 16+4g+e-4) in bf16.
+__device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, float scale_log2,
+                                                 SoftmaxState& st, float& factor, bool& moved) {
     float x[8];
     bool over = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int rr = (e >> 2) * 16 + 4 * g + (e & 3);
-        const float v = ((valid >> rr) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        const float v = ((valid >> e) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
         x[e] = v;
         over |= v > st.m_ref + kRescaleSlack;
     }
+    factor = 1.0f;
+    moved = false;
     // The exact tile maximum is only needed when the reference has to move
     // (the first tile with a visible row, or a jump beyond the slack).
     if (__ballot(over)) {
@@ -243,13 +246,9 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
         // finite old reference needs the accumulators rescaled.
         const bool scale = st.m_ref != -INFINITY && m_new != st.m_ref;
         if (__ballot(scale)) {
-            const float f = scale ? exp2f(st.m_ref - m_new) : 1.0f;
-#pragma unroll
-            for (int db = 0; db < kDv / 16; ++db) {
-                st.o[db] *= f;
-                __builtin_amdgcn_sched_barrier(0);  // one 4-register block at a time
-            }
-            st.lsum *= f;
+            factor = scale ? exp2f(st.m_ref - m_new) : 1.0f;
+            st.lsum *= factor;
+            moved = true;
         }
         st.m_ref = m_new;
     }
@@ -264,61 +263,116 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
     return __builtin_bit_cast(bf16x8_t, pw);
 }
 
-// P.V of the tile in `tv` fused with Q.K^T of the next tile in `tq`: the two are
-// independent, so alternating chunks of them (8 value blocks, then 4-5 k-steps)
-// gives the wave two instruction streams to overlap; the scheduling barriers
-// keep each chunk's operand reads from being hoisted all at once.  When `gp` is
-// active, its nine loads are issued two per chunk (plus one up front), each
-// behind a few matrix instructions that keep the matrix unit busy while the
-// wave waits for the address unit to accept the load.
-__device__ __forceinline__ void pv_then_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad, bf16x8_t pb,
-                                           const bf16x8_t (&qb)[kDqk / 32], int lane, SoftmaxState& st,
-                                           f32x4_t (&s)[2], const GatherPlan& gp, const uint16_t* kvb) {
-    s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int kChunksPv = 4;
-    constexpr int kDbPer = kDv / 16 / kChunksPv;  // 8 value blocks per chunk
+// Bits e of this lane's values (rows (e>>2)*16 + 4g + (e&3) of tile t) that are visible.
+__device__ __forceinline__ uint32_t valid_bits(const int* rows_lds, int t, int g, int L) {
+    const int4 ra = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 4 * g);
+    const int4 rb = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 16 + 4 * g);
+    const int r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v |= (r8[e] >= 0 && r8[e] < L) ? (1u << e) : 0u;
+    return v;
+}
+
+// Apply the rescale factors recorded with tile tv's softmax to the accumulators.
+__device__ __forceinline__ void apply_rescale(const uint16_t* tv, int c, PvAcc& acc) {
+    const char* base = reinterpret_cast<const char*>(tv);
+    const u32x4_t fl = *reinterpret_cast<const u32x4_t*>(base + kFlagOffset);
+    const uint32_t any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+    if (any) {
+        const float* fac = reinterpret_cast<const float*>(base + kFacOffset);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            if (__builtin_amdgcn_readfirstlane(fl[hb])) {
+                const float f = fac[16 * hb + c];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    acc.o[d][hb] *= f;
+                    __builtin_amdgcn_sched_barrier(0);  // one 4-register block at a time
+                }
+            }
+        }
+    }
+}
+
+// Q.K^T partial of tile `tq` (this wave's half of the dims, both head blocks of
+// its pair) fused with P.V of tile `tv` (this wave's 128 value dims, all four
+// head blocks): two independent instruction streams, alternated in chunks.
+// When `gp` is active its nine loads are issued between matrix instructions.
+template <bool PV, bool QK>
+__device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad,
+                                      const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
+                                      int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const GatherPlan& gp,
+                                      const uint16_t* kvb) {
+    bf16x8_t pbv[4];
+    if (PV) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
+        apply_rescale(tv, lane & 15, acc);
+    }
+    if (QK) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     issue_gather(gp, kvb, 8, lane);
 #pragma unroll
-    for (int ch = 0; ch < kChunksPv; ++ch) {
+    for (int ch = 0; ch < 4; ++ch) {
+        if (PV) {
 #pragma unroll
-        for (int i = 0; i < kDbPer; ++i) {
-            const int db = ch * kDbPer + i;
-            const char* p = reinterpret_cast<const char*>(tv) + ad.tr[db & 7] + 256 * (db >> 3);
-            const bf16x4_t lo = lds_read_tr16(p);
-            const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
-            st.o[db] = mfma16x16x32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, st.o[db]);
-            if (i == 3) issue_gather(gp, kvb, 2 * ch, lane);
+            for (int i = 0; i < 2; ++i) {
+                const int d = 2 * ch + i;
+                const char* p = reinterpret_cast<const char*>(tv) + ad.tr[d] + 256 * wave;
+                const bf16x4_t lo = lds_read_tr16(p);
+                const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
+                const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+                if (i == 0) issue_gather(gp, kvb, 2 * ch, lane);
+            }
         }
-        // k-steps [ks0, ks1) of the next tile: 5, 5, 4, 4
-        const int ks0 = ch == 0 ? 0 : (ch == 1 ? 5 : (ch == 2 ? 10 : 14));
-        const int ks1 = ch == 0 ? 5 : (ch == 1 ? 10 : (ch == 2 ? 14 : 18));
+        if (QK) {
+            // local k-steps [k0, k1): 2, 2, 2, 3
+            const int k0 = 2 * ch;
+            const int k1 = ch == 3 ? 9 : 2 * ch + 2;
 #pragma unroll
-        for (int ks = ks0; ks < ks1; ++ks) {
-            const char* p = reinterpret_cast<const char*>(tq) + qk_offset(ad, ks);
-            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
-            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + 16 * (ks < 16 ? 1024 : 128));
-            s[0] = mfma16x16x32(a0, qb[ks], s[0]);
-            s[1] = mfma16x16x32(a1, qb[ks], s[1]);
-            if (ks == ks0 + 1) issue_gather(gp, kvb, 2 * ch + 1, lane);
+            for (int kl = k0; kl < k1; ++kl) {
+                // k-step 9kk + kl: both candidates index the offset table at compile time
+                const int off_lo = ad.qk[kl & 3] + 256 * (kl >> 2);  // kk = 0: always in the main part
+                const int off_hi = kl < 7 ? ad.qk[(kl + 1) & 3] + 256 * ((9 + kl) >> 2) : ad.qt[kl - 7];
+                const int off = kk ? off_hi : off_lo;
+                const int rb1 = (kk && kl >= 7) ? 16 * 128 : 16 * 1024;  // next row block: tail rows are 128 B
+                const char* p = reinterpret_cast<const char*>(tq) + off;
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + rb1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
+                    sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
+                }
+                if (kl == k0) issue_gather(gp, kvb, 2 * ch + 1, lane);
+            }
+        } else if (!PV) {
+            issue_gather(gp, kvb, 2 * ch, lane);
+            issue_gather(gp, kvb, 2 * ch + 1, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// O^T[dims 16db.. x heads] += V^T[16 dims x 32 rows] . P^T[32 rows x 16 heads] for one tile.
-// Transpose-read addressing: lane (g, 4j+q) points at row 4g+j (+16), dims 4q..4q+3 of the block,
-// i.e. chunk 2db + q/2, byte offset 8*(q&1).
-__device__ __forceinline__ void pv_tile(const uint16_t* tl, const TileAddr& ad, bf16x8_t pb, int lane,
-                                        SoftmaxState& st) {
+// Partner exchange of the Q.K^T partials: this wave keeps the half of head block
+// w and sends the half of head block w^1; afterwards s holds S^T of head block w.
+__device__ __forceinline__ void send_partial(const f32x4_t (&sp)[2][2], f32x4_t* sx, int wave, int kk, int lane) {
+    // sp[.][h] covers head block 2hh + h; the partner owns block 2hh + (1 - kk)
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
-        const char* p = reinterpret_cast<const char*>(tl) + ad.tr[db & 7] + 256 * (db >> 3);
-        const bf16x4_t lo = lds_read_tr16(p);
-        const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
-        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        st.o[db] = mfma16x16x32(a, pb, st.o[db]);
-    }
+    for (int rb = 0; rb < 2; ++rb) sx[((wave ^ 1) * 2 + rb) * kWave + lane] = kk ? sp[rb][0] : sp[rb][1];
+}
+
+__device__ __forceinline__ void own_scores(const f32x4_t (&sp)[2][2], const f32x4_t* sx, int wave, int kk, int lane,
+                                           f32x4_t (&s)[2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) s[rb] = (kk ? sp[rb][1] : sp[rb][0]) + sx[(wave * 2 + rb) * kWave + lane];
 }
 
 // One workgroup (one wave per SIMD) fills a CU's LDS, so the scheduler may use
@@ -338,103 +392,140 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (bt >= rows) return;
     const int b = bt / T;
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps role selects scalar
+    const int kk = wave & 1;   // contraction half for Q.K^T
+    const int hh = wave >> 1;  // head pair for Q.K^T
     const int c = lane & 15;
     const int g = lane >> 4;
     const int j0 = split * rows_per_split;
     const int nrows = min(k, j0 + rows_per_split) - j0;
     const int ntiles = (nrows + kRows - 1) / kRows;
 
+    constexpr int kStages = Cfg<DIRECT>::kStages;
     __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
-    __shared__ __attribute__((aligned(16))) int rows_lds[kMaxSplitRows];
-    __shared__ uint32_t valid_lds[kMaxSplitRows / kRows];
+    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
+    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
+    __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
 
-    // B operand of S^T: q[head 16w+c][32*ks + 8*g .. +7], loaded while the row
-    // list is fetched so that the two latencies overlap.
-    bf16x8_t qb[kDqk / 32];
-    {
-        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * wave + c) * kDqk + 8 * g;
+    // B operands of S^T: q[head 16*(2hh+h) + c][32*(9kk+kl) + 8g .. +7], loaded
+    // while the row list is fetched so that the two latencies overlap.
+    bf16x8_t qb[2][9];
 #pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
+    for (int h = 0; h < 2; ++h) {
+        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
     }
     const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) {
-        const int rid = j < nrows ? sel[j] : -1;
-        rows_lds[j] = rid;
-        // bit r of valid_lds[tile]: row r of that tile exists and indexes the cache
-        const uint64_t m = __ballot(rid >= 0 && rid < L);
-        if (lane == 0) {
-            valid_lds[j / kRows] = (uint32_t)m;
-            valid_lds[j / kRows + 1] = (uint32_t)(m >> 32);
-        }
-    }
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
     // Consume q here so the compiler's own wait for these loads (it cannot see the
     // gathers, which are issued from asm) stays ahead of the first gather.
 #pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" ::"v"(qb[ks]));
-    __syncthreads();  // rows_lds, valid_lds ready
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
+    __syncthreads();  // rows_lds ready
 
-    // Start the first gathers.
     const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
     const TileAddr ad = tile_addr(lane);
+    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
-        const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, tiles + t * (kTileChunks * 8), wave, lane);
+        const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
     }
 
-    SoftmaxState st;
+    PvAcc acc;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) st.o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st;
     st.m_ref = -INFINITY;
     st.lsum = 0.0f;
+    GatherPlan no_gather;
+    no_gather.active = false;
 
-    // Software pipeline over tiles: iteration t runs P.V of tile t and Q.K^T of tile t+1
-    // side by side (independent work for the same wave), then the softmax of t+1.
-    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
-    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
+    // softmax of tile t from the exchanged partials, P^T and rescale record to LDS
+    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
+        f32x4_t s[2];
+        own_scores(sp, sx, wave, kk, lane, s);
+        float factor;
+        bool moved;
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
+        pl[wave * kWave + lane] = pb;
+        char* tail = reinterpret_cast<char*>(buf(t));
+        if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * wave + c] = factor;
+        if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[wave] = moved ? 1u : 0u;
+    };
+
+    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
     {
         const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
         if (later >= 2) wait_vmem<2 * kLoads>();
         else if (later == 1) wait_vmem<kLoads>();
         else wait_vmem<0>();
+        static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
     }
     lds_barrier();
-    f32x4_t s[2];
-    qk_tile(buf(0), ad, qb, s);
-    bf16x8_t pb = softmax_tile(s, valid_lds[0], scale_log2, lane, st);
-    // One code path per iteration (the last tile is peeled off below) so the
-    // accumulators stay in place across the loop back-edge.
+    {
+        f32x4_t sp[2][2];
+        pv_qk<false, true>(buf(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();
+        finish_scores(0, sp);
+    }
+    // Iteration t: P.V of tile t alongside Q.K^T of tile t+1 (and the gather of
+    // tile t+3), then the exchange and softmax of tile t+1.
+    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
     for (int t = 0; t + 1 < ntiles; ++t) {
         // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
         const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
         if (later >= 1) wait_vmem<kLoads>();
         else wait_vmem<0>();
-        lds_barrier();  // every thread's part of tile t+1 is in LDS; buffer (t+3) % 4 is free
-        const uint32_t valid = valid_lds[t + 1];
-        // tile t+3 (if any) is gathered while this iteration computes
+        lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer (t+3) % 4 free
         GatherPlan gp = plan_gather(kvb, rows_lds, min(t + kStages - 1, ntiles - 1), nrows, L, buf(t + kStages - 1),
                                     wave, lane);
         gp.active = t + kStages - 1 < ntiles;
-        pv_then_qk(buf(t), buf(t + 1), ad, pb, qb, lane, st, s, gp, kvb);
-        pb = softmax_tile(s, valid, scale_log2, lane, st);
-        lds_barrier();  // nobody reads buffer t % kStages any more
+        f32x4_t sp[2][2];
+        pv_qk<true, true>(buf(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp, kvb);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();  // partials exchanged; every wave is done reading P^T of tile t
+        finish_scores(t + 1, sp);
     }
-    pv_tile(buf(ntiles - 1), ad, pb, lane, st);
+    lds_barrier();  // P^T and rescale record of the last tile visible
+    {
+        f32x4_t sp[2][2];
+        pv_qk<true, false>(buf(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
+    }
 
+    // Denominators (and reference maxima) of all 64 heads, from their owner waves.
     float lsum = st.lsum;
-    const float m_ref = st.m_ref;
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
-    const int head = 16 * wave + c;
-    const f32x4_t* o = st.o;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    uint16_t* dst = DIRECT ? out + ((int64_t)bt * kHq + head) * kDv + 4 * g
-                           : part_o + (((int64_t)bt * nsplit + split) * kHq + head) * kDv + 4 * g;
+    const float m_ref = st.m_ref;
+    float* stats = reinterpret_cast<float*>(sx);  // free now: [0, 64) sums, [64, 128) maxima
+    if (g == 0) {
+        stats[16 * wave + c] = lsum;
+        stats[64 + 16 * wave + c] = m_ref;
+    }
+    lds_barrier();
+    float inv[4];
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db)
-        *reinterpret_cast<uint2*>(dst + 16 * db) =
-            make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
+    for (int hb = 0; hb < 4; ++hb) {
+        const float ls = stats[16 * hb + c];
+        inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
+    }
+    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const f32x4_t& o = acc.o[d][hb];
+            *reinterpret_cast<uint2*>(dst + (16 * hb + c) * kDv + 128 * wave + 16 * d + 4 * g) =
+                make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
+        }
+    const int head = 16 * wave + c;
     if (DIRECT) {
         if (lse && g == 0)
             lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (m_ref + log2f(lsum)) * 0.69314718055994531f : -INFINITY;
@@ -462,7 +553,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     const int head = rem / kXcds;
     const int bt = grp * kXcds + rem % kXcds;
     if (bt >= rows) return;
-    __shared__ float wl[kMaxSplitRows / kRows];  // per split: log2-sum-exp, then weight
+    __shared__ float wl[kMaxSplits];  // per split: log2-sum-exp, then weight
     __shared__ float stat[2];
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
     const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
@@ -518,6 +609,10 @@ struct SplitPlan {
 SplitPlan plan(int rows, int k) {
     const int tiles = (k + kRows - 1) / kRows;
     int ns = (kTargetBlocks + rows - 1) / rows;
+    if (ns > 1) {  // split lists: each split's row list fits the split kernel's LDS
+        const int min_ns = (tiles * kRows + kMaxSplitRows - 1) / kMaxSplitRows;
+        if (ns < min_ns) ns = min_ns;
+    }
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
     const int tiles_per = (tiles + ns - 1) / ns;
