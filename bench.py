@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
+    ap.add_argument("--no-nonshared", action="store_true", help="skip timing the group without IndexShare")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -183,6 +184,37 @@ def main():
                  "attn_ms_per_layer": [round(x, 4) for x in phase[2:]]}
     log("bench: breakdown %s" % breakdown)
 
+    # ---------------- without IndexShare: every layer runs its own indexer and top-k over its own
+    # index-key cache (the same kernels, called per layer); the measured saving of sharing
+    ns_ms = None
+    if not args.no_nonshared and T == 1:
+        k_idx_l = [k_idx] + [to_dev(synth.int_bf16(cfg.seed, synth.T_K_IDX + 100 + l, (B, L, cfg.D)))
+                             for l in range(1, nl)]
+        idx_l = [torch.empty_like(idx) for _ in range(nl)]
+        # one single-layer group per layer (the group entry point with n_layers = 1), args built once
+        args_l = [dsa.make_group_args(q_idx, w, k_idx_l[l], q_pos, k, [qs[l]], [kvs[l]], cfg.sm_scale, idx_l[l],
+                                      [outs[l]]) for l in range(nl)]
+        argp_l = [ctypes.byref(a) for a in args_l]
+
+        def nonshared_step():
+            for l in range(nl):
+                rc = lib.dsa_layer_group(argp_l[l], ws.data_ptr(), ws_bytes, stream)
+                if rc != 0:
+                    raise RuntimeError(dsa.last_error())
+
+        for _ in range(2):
+            nonshared_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            nonshared_step()
+        e1.record()
+        torch.cuda.synchronize()
+        ns_ms = e0.elapsed_time(e1) / reps
+        del k_idx_l, idx_l, args_l, argp_l
+        log("bench: without IndexShare %.3f ms per group (shared %.3f ms)" % (ns_ms, ms))
+
     qtok = B * T
     value = qtok / (ms / 1e3)
     if T == 1:
@@ -221,6 +253,11 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": None,
     }
+    if ns_ms is not None:
+        line["indexshare"] = {"shared_ms": round(ms, 4), "non_shared_ms": round(ns_ms, 4),
+                              "speedup": round(ns_ms / ms, 3),
+                              "note": "non-shared: a one-layer group per layer (indexer + top-k + attention), "
+                                      "each over its own index-key cache"}
     if T > 1:  # a prefill chunk is a dense contraction: report the matrix-core fraction as well
         tflops = (idx_flops + attn_flops) / (ms / 1e3) / 1e12
         line["mfma"] = {"flops_per_step": idx_flops + attn_flops, "achieved_tflops": round(tflops, 1),
