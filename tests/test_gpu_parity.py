@@ -179,6 +179,51 @@ def test_attn_many_queries_direct_path(dsa):
     assert_attn_close(got[:, sample], ref)
 
 
+def _growing_rows(seed, B, L):
+    """Latent rows whose magnitude doubles every 256 positions: with sorted index
+    lists the logits keep outgrowing the running reference maximum, so the
+    online softmax has to move it (and rescale the accumulators) many times."""
+    kv = synth.normal_bf16(seed, 2, (B, L, 576))
+    scale = np.exp2(np.arange(L) // 256).astype(np.float32)[None, :, None]
+    v = synth.bf16_to_f32(kv) * scale
+    return (v.view(np.uint32) >> 16).astype(np.uint16)  # exact: scaling by a power of two
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_attn_reference_moves(dsa, T):
+    # T=40: several splits of several tiles each; T=300: one workgroup per query
+    rng = np.random.default_rng(11 + T)
+    B, L, k = 1, 4096, 1024
+    say("attn reference moves T=%d" % T)
+    q = synth.normal_bf16(44, 1, (B, T, 64, 576))
+    kv = _growing_rows(44, B, L)
+    idx = np.sort(np.stack([rng.choice(L, size=k, replace=False) for _ in range(T)]), axis=1)[None].astype(np.int32)
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    sample = [0, T // 2, T - 1]
+    ref, ref_lse = oracle.sparse_mla_attn(q[:, sample], kv, idx[:, sample], 1 / 16)
+    assert_attn_close(host(out)[:, sample], ref)
+    np.testing.assert_allclose(host(lse)[:, sample], ref_lse, atol=LSE_TOL * np.abs(ref_lse).max(), rtol=0)
+
+
+def test_attn_direct_ragged_k(dsa):
+    # one workgroup per query with a list that ends inside a tile, some entries masked
+    rng = np.random.default_rng(12)
+    B, T, L, k = 1, 300, 3000, 100
+    say("attn direct ragged k=%d" % k)
+    q = synth.normal_bf16(45, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(45, 2, (B, L, 576))
+    idx = np.sort(rng.choice(L, size=(B, T, k)), axis=2).astype(np.int32)
+    idx[0, 7, 50:] = -1
+    idx[0, 8, :] = -1
+    assert dsa.attn_workspace_size(B, T, k) == 0
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    sample = [0, 7, 8, 299]
+    ref, ref_lse = oracle.sparse_mla_attn(q[:, sample], kv, idx[:, sample], 1 / 16)
+    got = host(out)[:, sample]
+    assert np.all(got[0, 2] == 0) and np.all(np.isneginf(host(lse)[0, 8]))
+    assert_attn_close(got, ref)
+
+
 # ------------------------------------------------------------------ IndexShare group
 def test_group_tiny(dsa):
     cfg = synth.TINY
@@ -200,6 +245,22 @@ def test_group_tiny(dsa):
         assert torch.equal(alone.view(torch.int16), outs[l].view(torch.int16))
 
 
+def test_group_eight_layers(dsa):
+    # the largest group the entry point takes: one index list feeding eight layers
+    cfg = synth.TINY
+    n = 8
+    say("group tiny, %d layers" % n)
+    qi, w, ki, pos = cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos()
+    qs = [cfg.q_attn(l) for l in range(n)]
+    kvs = [cfg.kv(l) for l in range(n)]
+    idx, outs, _ = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k,
+                                   [bf16_dev(q) for q in qs], [bf16_dev(kv) for kv in kvs], cfg.sm_scale)
+    _, ref_idx, ref_outs, _ = oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    for l in range(n):
+        assert_attn_close(host(outs[l]), ref_outs[l], "layer %d" % l)
+
+
 # ------------------------------------------------------------------ verification
 @pytest.mark.parametrize("rho", [0.0, 0.9, 1.0])
 def test_verify_small(dsa, rho):
@@ -210,6 +271,20 @@ def test_verify_small(dsa, rho):
     d = (rho * t[:, :S] + np.sqrt(1 - rho * rho) * rng.standard_normal((B, S, V)) * 2).astype(np.float32)
     tok = rng.integers(0, V, (B, S)).astype(np.int32)
     tok[:, 0] = np.argmax(d[:, 0], -1)
+    u = rng.random((B, S)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
+@pytest.mark.parametrize("S", [1, 20])
+def test_verify_draft_lengths(dsa, S):
+    rng = np.random.default_rng(60 + S)
+    B, V = 5, 3000
+    say("verify S=%d" % S)
+    t = (rng.standard_normal((B, S + 1, V)) * 2).astype(np.float32)
+    d = (0.95 * t[:, :S] + 0.3 * rng.standard_normal((B, S, V))).astype(np.float32)
+    tok = np.argmax(d + rng.gumbel(size=d.shape), axis=-1).astype(np.int32)
     u = rng.random((B, S)).astype(np.float32)
     ur = rng.random(B).astype(np.float32)
     ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
