@@ -17,6 +17,12 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                   one-hot logits; identical rows; permutation invariance.
   layer_group     pinned through its parts plus bitwise reuse of one index
                   list by every layer.
+  e4m3_decode     pinned: all 256 codes against torch's float8_e4m3fn
+                  dtype; OCP code points (1, 2, 3, 448, 2^-6, 2^-9, NaN, -0).
+  indexer_scores (fp8) / sparse_mla_attn (fp8 latent rows)
+                  pinned: equal to the bf16 functions on values that both
+                  formats hold exactly, plus the bf16 pins above; the E4M3
+                  decoding enters only through e4m3_decode's element reads.
   mtp_verify      pinned: sum-min identities (p=q -> 1, disjoint -> 0,
                   1 - TV distance), scipy softmax, Monte-Carlo check of the
                   speculative-sampling theorem (acceptance rate = sum-min,
@@ -46,11 +52,15 @@ def lib():
         L.oracle_topk.argtypes = [p, p, i32, i32, i32, i32, p]
         L.oracle_sparse_mla_attn.argtypes = [p, p, i64, p, i32, i32, i32, i32, i32, i32, i32, f64, p, p]
         L.oracle_layer_group.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i32, i32, i32,
-                                         p, p, p, i32, i32, i32, f64, p, p, p, p]
+                                         p, p, p, i32, i32, i32, f64, i32, i32, p, p, p, p]
+        L.oracle_indexer_scores_fp8.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i32, p]
+        L.oracle_sparse_mla_attn_fp8kv.argtypes = [p, p, i64, p, i32, i32, i32, i32, i32, i32, i32, f64, p, p]
+        L.oracle_e4m3_decode.argtypes = [p, i64, p]
         L.oracle_softmax_row.argtypes = [p, i32, p]
         L.oracle_mtp_verify.argtypes = [p, p, p, p, p, i32, i32, i32, p, p, p, p]
         for fn in ("oracle_indexer_scores", "oracle_topk", "oracle_sparse_mla_attn", "oracle_layer_group",
-                   "oracle_softmax_row", "oracle_mtp_verify"):
+                   "oracle_softmax_row", "oracle_mtp_verify", "oracle_indexer_scores_fp8",
+                   "oracle_sparse_mla_attn_fp8kv", "oracle_e4m3_decode"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -65,12 +75,22 @@ def _p(a) -> int:
     return a.ctypes.data
 
 
-def indexer_scores(q_idx, w, k_idx, q_pos, L=None) -> np.ndarray:
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 codes (uint8) -> float64 values (NaN for S.1111.111)."""
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    lib().oracle_e4m3_decode(_p(codes), codes.size, _p(out))
+    return out
+
+
+def indexer_scores(q_idx, w, k_idx, q_pos, L=None, fp8=False) -> np.ndarray:
     """q_idx [B,T,H,D] bf16 bits (uint16), w [B,T,H] f32, k_idx [B,Lk,D] uint16,
-    q_pos [B,T] int32 -> scores [B,T,L] f32 (-inf where s > p)."""
-    q_idx = _c(q_idx, np.uint16)
+    q_pos [B,T] int32 -> scores [B,T,L] f32 (-inf where s > p).
+    fp8=True: q_idx and k_idx are E4M3 codes (uint8)."""
+    et = np.uint8 if fp8 else np.uint16
+    q_idx = _c(q_idx, et)
     w = _c(w, np.float32)
-    k_idx = _c(k_idx, np.uint16)
+    k_idx = _c(k_idx, et)
     q_pos = _c(q_pos, np.int32)
     B, T, H, D = q_idx.shape
     assert D <= 1024 and k_idx.shape[0] == B and k_idx.shape[2] == D and w.shape == (B, T, H)
@@ -78,7 +98,8 @@ def indexer_scores(q_idx, w, k_idx, q_pos, L=None) -> np.ndarray:
     L = Lk if L is None else L
     assert L <= Lk
     out = np.empty((B, T, L), np.float32)
-    lib().oracle_indexer_scores(_p(q_idx), _p(w), _p(k_idx), Lk * D, _p(q_pos), B, T, L, H, D, _p(out))
+    fn = lib().oracle_indexer_scores_fp8 if fp8 else lib().oracle_indexer_scores
+    fn(_p(q_idx), _p(w), _p(k_idx), Lk * D, _p(q_pos), B, T, L, H, D, _p(out))
     return out
 
 
@@ -92,11 +113,11 @@ def topk(scores, q_pos, k) -> np.ndarray:
     return out
 
 
-def sparse_mla_attn(q, kv, idx, sm_scale, Dv=512, L=None):
-    """q [B,T,Hq,Dqk] uint16, kv [B,Lk,Dqk] uint16, idx [B,T,k] int32
-    -> (out [B,T,Hq,Dv] f64, lse [B,T,Hq] f64)."""
+def sparse_mla_attn(q, kv, idx, sm_scale, Dv=512, L=None, kv_fp8=False):
+    """q [B,T,Hq,Dqk] uint16, kv [B,Lk,Dqk] uint16 (E4M3 codes, uint8, when
+    kv_fp8), idx [B,T,k] int32 -> (out [B,T,Hq,Dv] f64, lse [B,T,Hq] f64)."""
     q = _c(q, np.uint16)
-    kv = _c(kv, np.uint16)
+    kv = _c(kv, np.uint8 if kv_fp8 else np.uint16)
     idx = _c(idx, np.int32)
     B, T, Hq, Dqk = q.shape
     Lk = kv.shape[1]
@@ -105,20 +126,21 @@ def sparse_mla_attn(q, kv, idx, sm_scale, Dv=512, L=None):
     assert kv.shape[0] == B and kv.shape[2] == Dqk and idx.shape[:2] == (B, T)
     out = np.empty((B, T, Hq, Dv), np.float64)
     lse = np.empty((B, T, Hq), np.float64)
-    lib().oracle_sparse_mla_attn(_p(q), _p(kv), Lk * Dqk, _p(idx), B, T, L, Hq, Dqk, Dv, k, float(sm_scale),
-                                 _p(out), _p(lse))
+    fn = lib().oracle_sparse_mla_attn_fp8kv if kv_fp8 else lib().oracle_sparse_mla_attn
+    fn(_p(q), _p(kv), Lk * Dqk, _p(idx), B, T, L, Hq, Dqk, Dv, k, float(sm_scale), _p(out), _p(lse))
     return out, lse
 
 
-def layer_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, Dv=512):
-    """One IndexShare group.  qs/kvs: lists (one per layer).  Returns
-    (scores, idx, [out_l], [lse_l])."""
-    q_idx = _c(q_idx, np.uint16)
+def layer_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, Dv=512, idx_fp8=False, kv_fp8=False):
+    """One IndexShare group.  qs/kvs: lists (one per layer).  idx_fp8: q_idx
+    and k_idx are E4M3 codes; kv_fp8: the latent rows are E4M3 codes.
+    Returns (scores, idx, [out_l], [lse_l])."""
+    q_idx = _c(q_idx, np.uint8 if idx_fp8 else np.uint16)
     w = _c(w, np.float32)
-    k_idx = _c(k_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint8 if idx_fp8 else np.uint16)
     q_pos = _c(q_pos, np.int32)
     qs = [_c(q, np.uint16) for q in qs]
-    kvs = [_c(kv, np.uint16) for kv in kvs]
+    kvs = [_c(kv, np.uint8 if kv_fp8 else np.uint16) for kv in kvs]
     B, T, H, D = q_idx.shape
     L = k_idx.shape[1]
     n = len(qs)
@@ -136,7 +158,7 @@ def layer_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, Dv=512):
     lib().oracle_layer_group(_p(q_idx), _p(w), _p(k_idx), L * D, _p(q_pos), B, T, L, H, D, k, n,
                              ctypes.cast(q_ptrs, ctypes.c_void_p), ctypes.cast(kv_ptrs, ctypes.c_void_p),
                              ctypes.cast(strides, ctypes.c_void_p), Hq, Dqk, Dv, float(sm_scale),
-                             _p(scores), _p(idx), ctypes.cast(out_ptrs, ctypes.c_void_p),
+                             int(idx_fp8), int(kv_fp8), _p(scores), _p(idx), ctypes.cast(out_ptrs, ctypes.c_void_p),
                              ctypes.cast(lse_ptrs, ctypes.c_void_p))
     return scores, idx, outs, lses
 

@@ -34,7 +34,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }
 
 /* bf16 bit pattern -> double: the bf16 value is the top half of an fp32. */
 static double bf16_to_double(uint16_t h) {
@@ -42,6 +42,30 @@ static double bf16_to_double(uint16_t h) {
     float f;
     memcpy(&f, &u, 4);
     return (double)f;
+}
+
+/* E4M3 code -> double, from the OCP 8-bit floating point definition (the
+ * FP8 cache format named in [CTXFR, "Entraînement par renforcement de l'agent
+ * intelligent"]): bit 7 sign, bits 6..3 exponent E with bias 7, bits 2..0
+ * mantissa M.  E = 0: (-1)^s * (M/8) * 2^-6 (zero and subnormals);
+ * E = 1..15: (-1)^s * (1 + M/8) * 2^(E-7), except E = 15, M = 7, which is
+ * NaN.  There are no infinities. */
+static double e4m3_to_double(uint8_t c) {
+    const int s = c >> 7, E = (c >> 3) & 15, M = c & 7;
+    if (E == 15 && M == 7) return NAN;
+    double mag = (E == 0) ? ldexp((double)M / 8.0, -6) : ldexp(1.0 + (double)M / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+void oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_double(codes[i]);
+}
+
+/* Element i of a cache or query array stored either as bf16 bit patterns
+ * (fmt 0) or as E4M3 codes (fmt 1). */
+enum { FMT_BF16 = 0, FMT_E4M3 = 1 };
+static double elem(const void* base, int64_t i, int fmt) {
+    return fmt == FMT_E4M3 ? e4m3_to_double(((const uint8_t*)base)[i]) : bf16_to_double(((const uint16_t*)base)[i]);
 }
 
 /* ------------------------------------------------------------------ indexer
@@ -53,15 +77,17 @@ static double bf16_to_double(uint16_t h) {
  * accumulated in fp64 and rounded once to fp32.  Keys s > p get -inf.
  * Layouts: q_idx [B,T,H,D], w [B,T,H], k_idx row s of batch b at
  * k_idx + b*k_bstride + s*D, q_pos [B,T], scores [B,T,L].
+ * The FP8 variant reads q_idx and k_idx as E4M3 codes; the arithmetic is the
+ * same (the decoded values enter the fp64 sums).
  */
-void oracle_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                           const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores) {
+static void indexer_scores_fmt(const void* q_idx, const float* w, const void* k_idx, int64_t k_bstride,
+                               const int32_t* q_pos, int B, int T, int L, int H, int D, int fmt, float* scores) {
     for (int b = 0; b < B; ++b) {
         for (int t = 0; t < T; ++t) {
             const int64_t bt = (int64_t)b * T + t;
             const int64_t p = q_pos[bt];
             double* q = (double*)malloc(sizeof(double) * (size_t)H * (size_t)D);
-            for (int i = 0; i < H * D; ++i) q[i] = bf16_to_double(q_idx[bt * H * D + i]);
+            for (int i = 0; i < H * D; ++i) q[i] = elem(q_idx, bt * H * D + i, fmt);
             float* row = scores + bt * (int64_t)L;
 #pragma omp parallel for schedule(static)
             for (int64_t s = 0; s < L; ++s) {
@@ -69,9 +95,9 @@ void oracle_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t
                     row[s] = -INFINITY;
                     continue;
                 }
-                const uint16_t* key = k_idx + (int64_t)b * k_bstride + s * D;
+                const int64_t key = (int64_t)b * k_bstride + s * D;
                 double kd[1024];
-                for (int d = 0; d < D; ++d) kd[d] = bf16_to_double(key[d]);
+                for (int d = 0; d < D; ++d) kd[d] = elem(k_idx, key + d, fmt);
                 double acc = 0.0;
                 for (int h = 0; h < H; ++h) {
                     double dot = 0.0;
@@ -85,6 +111,16 @@ void oracle_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t
             free(q);
         }
     }
+}
+
+void oracle_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                           const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores) {
+    indexer_scores_fmt(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, FMT_BF16, scores);
+}
+
+void oracle_indexer_scores_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                               const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores) {
+    indexer_scores_fmt(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, FMT_E4M3, scores);
 }
 
 /* ------------------------------------------------------------------ top-k
@@ -145,10 +181,11 @@ void oracle_topk(const float* scores, const int32_t* q_pos, int B, int T, int L,
  *     lse[b,t,h]   = log sum_j exp(z_j)            (-inf if no valid j)
  * in fp64.  Layouts: q [B,T,Hq,Dqk], kv row r of batch b at
  * kv + b*kv_bstride + r*Dqk, idx [B,T,k], out [B,T,Hq,Dv], lse [B,T,Hq].
+ * The FP8 variant reads the cached rows as E4M3 codes (the query stays bf16).
  */
-void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx,
-                            int B, int T, int L, int Hq, int Dqk, int Dv, int k, double sm_scale,
-                            double* out, double* lse) {
+static void sparse_mla_attn_fmt(const uint16_t* q, const void* kv, int kv_fmt, int64_t kv_bstride,
+                                const int32_t* idx, int B, int T, int L, int Hq, int Dqk, int Dv, int k,
+                                double sm_scale, double* out, double* lse) {
 #pragma omp parallel for schedule(dynamic)
     for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
         const int64_t b = bt / T;
@@ -160,8 +197,8 @@ void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bs
         for (int j = 0; j < k; ++j) {
             int32_t r = sel[j];
             if (r < 0 || r >= L) continue;
-            const uint16_t* src = kv + b * kv_bstride + (int64_t)r * Dqk;
-            for (int d = 0; d < Dqk; ++d) rows[(int64_t)nv * Dqk + d] = bf16_to_double(src[d]);
+            const int64_t src = b * kv_bstride + (int64_t)r * Dqk;
+            for (int d = 0; d < Dqk; ++d) rows[(int64_t)nv * Dqk + d] = elem(kv, src + d, kv_fmt);
             ++nv;
         }
         for (int h = 0; h < Hq; ++h) {
@@ -198,6 +235,18 @@ void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bs
     }
 }
 
+void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx,
+                            int B, int T, int L, int Hq, int Dqk, int Dv, int k, double sm_scale,
+                            double* out, double* lse) {
+    sparse_mla_attn_fmt(q, kv, FMT_BF16, kv_bstride, idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out, lse);
+}
+
+void oracle_sparse_mla_attn_fp8kv(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx,
+                                  int B, int T, int L, int Hq, int Dqk, int Dv, int k, double sm_scale,
+                                  double* out, double* lse) {
+    sparse_mla_attn_fmt(q, kv, FMT_E4M3, kv_bstride, idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out, lse);
+}
+
 /* ------------------------------------------------------------------ IndexShare group
  * [TEARDOWN, 刀二 IndexShare] (index_topk_freq 4) and [CTXFR, "Attention
  * sparse IndexShare"]: the indexer sits in the first layer of each group of
@@ -205,17 +254,19 @@ void oracle_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bs
  * top-k run once.  scores ([B,T,L]) and idx ([B,T,k]) receive the shared
  * intermediate results; layer l reads q[l], kv[l], kv_bstride[l] and writes
  * out[l], lse[l] (lse[l] may be NULL).
+ * idx_fmt / kv_fmt: 0 when q_idx, k_idx / the latent rows are bf16, 1 when
+ * they are E4M3 codes.
  */
-void oracle_layer_group(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+void oracle_layer_group(const void* q_idx, const float* w, const void* k_idx, int64_t k_bstride,
                         const int32_t* q_pos, int B, int T, int L, int H, int D, int k, int n_layers,
-                        const uint16_t* const* q, const uint16_t* const* kv, const int64_t* kv_bstride,
-                        int Hq, int Dqk, int Dv, double sm_scale, float* scores, int32_t* idx,
-                        double* const* out, double* const* lse) {
-    oracle_indexer_scores(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, scores);
+                        const uint16_t* const* q, const void* const* kv, const int64_t* kv_bstride,
+                        int Hq, int Dqk, int Dv, double sm_scale, int idx_fmt, int kv_fmt, float* scores,
+                        int32_t* idx, double* const* out, double* const* lse) {
+    indexer_scores_fmt(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, idx_fmt, scores);
     oracle_topk(scores, q_pos, B, T, L, k, idx);
     for (int l = 0; l < n_layers; ++l)
-        oracle_sparse_mla_attn(q[l], kv[l], kv_bstride[l], idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out[l],
-                               lse ? lse[l] : NULL);
+        sparse_mla_attn_fmt(q[l], kv[l], kv_fmt, kv_bstride[l], idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out[l],
+                            lse ? lse[l] : NULL);
 }
 
 /* ------------------------------------------------------------------ verification

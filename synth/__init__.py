@@ -58,10 +58,11 @@ def lib():
         L.synth_raw_u64.argtypes = [u64, u64, i64, i64, p]
         L.synth_gumbel_argmax.argtypes = [u64, u64, p, i64, i64, p]
         L.synth_normal_bf16_rows.argtypes = [u64, u64, p, i64, i64, p]
+        L.synth_f32_to_e4m3.argtypes = [p, i64, p]
         L.synth_int_bf16_rows.argtypes = [u64, u64, p, i64, i64, i32, i32, p]
         for fn in ("synth_int_bf16", "synth_pow2_f32", "synth_normal_bf16", "synth_normal_f32",
                    "synth_mix_f32", "synth_uniform_f32", "synth_raw_u64", "synth_gumbel_argmax",
-                   "synth_normal_bf16_rows", "synth_int_bf16_rows"):
+                   "synth_normal_bf16_rows", "synth_int_bf16_rows", "synth_f32_to_e4m3"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -139,6 +140,14 @@ def int_bf16_rows(seed, tensor, starts: np.ndarray, rowlen: int, lo=-3, hi=3) ->
     return out
 
 
+def to_e4m3(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> OCP E4M3 codes (uint8), round to nearest even, saturating."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().synth_f32_to_e4m3(_ptr(x), x.size, _ptr(out))
+    return out
+
+
 def bf16_to_f32(x: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (x.astype(np.uint32) << 16).view(np.float32)
@@ -184,6 +193,16 @@ class GroupConfig:
         """k_idx[b] alone, [L, D]."""
         return int_bf16(self.seed, T_K_IDX, (self.L, self.D), start=b * self.L * self.D)
 
+    def q_idx_fp8(self) -> np.ndarray:
+        """q_idx as OCP E4M3 codes (the integer values are exact in E4M3)."""
+        return to_e4m3(bf16_to_f32(self.q_idx()))
+
+    def k_idx_fp8(self) -> np.ndarray:
+        return to_e4m3(bf16_to_f32(self.k_idx()))
+
+    def k_idx_rows_fp8(self, b: int) -> np.ndarray:
+        return to_e4m3(bf16_to_f32(self.k_idx_rows(b)))
+
     def q_attn(self, layer: int) -> np.ndarray:
         return normal_bf16(self.seed, T_Q_ATTN + layer, (self.B, self.T, self.Hq, self.Dqk))
 
@@ -202,6 +221,16 @@ class GroupConfig:
         rows = np.asarray(rows, np.int64)
         starts = (b * self.L + rows) * self.Dqk
         return normal_bf16_rows(self.seed, T_KV + layer, starts, self.Dqk)
+
+    # FP8 latent cache: the same N(0,1) draws stored as E4M3 codes.
+    def kv_fp8(self, layer: int) -> np.ndarray:
+        return to_e4m3(bf16_to_f32(self.kv(layer)))
+
+    def kv_seq_fp8(self, layer: int, b: int) -> np.ndarray:
+        return to_e4m3(bf16_to_f32(self.kv_seq(layer, b)))
+
+    def kv_rows_fp8(self, layer: int, b: int, rows: np.ndarray) -> np.ndarray:
+        return to_e4m3(bf16_to_f32(self.kv_rows(layer, b, rows)))
 
 
 @dataclass(frozen=True)

@@ -28,6 +28,10 @@
  *   gumbel_argmax  a token drawn from softmax(logits) of each row by the
  *                Gumbel-max trick, argmax_v (x_v - log(-log U_v)); used only to
  *                make draft tokens that follow the draft distribution
+ *   f32_to_e4m3  storage conversion of given values to the OCP 8-bit float
+ *                E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *                no infinities; S.1111.111 is NaN; largest finite 448),
+ *                round to nearest even, saturating at +-448
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC synth.c
  */
@@ -182,5 +186,38 @@ void synth_int_bf16_rows(uint64_t seed, uint64_t tensor, const int64_t* starts, 
             int32_t v = lo + (int32_t)(draw(key, (uint64_t)(starts[r] + j)) % span);
             out[r * rowlen + j] = f32_to_bf16_rne((float)v);
         }
+    }
+}
+
+/* OCP E4M3 encoding of each value (round to nearest even, saturating). */
+void synth_f32_to_e4m3(const float* in, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float x = in[i];
+        if (x != x) {
+            out[i] = 0x7F;
+            continue;
+        }
+        const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+        const double a = fabs((double)x);
+        int e, m;
+        if (a < 0.015625) { /* below 2^-6: subnormal steps of 2^-9 (m == 8 is the smallest normal) */
+            e = 0;
+            m = (int)nearbyint(a * 512.0);
+        } else {
+            int e2;
+            const double fr = frexp(a, &e2); /* a = fr * 2^e2, fr in [0.5, 1) */
+            e = e2 - 1 + 7;
+            m = (int)nearbyint((2.0 * fr - 1.0) * 8.0);
+            if (m == 8) {
+                m = 0;
+                e += 1;
+            }
+            if (e > 15 || (e == 15 && m == 7)) {
+                e = 15;
+                m = 6;
+            }
+        }
+        out[i] = (uint8_t)(sign | ((e << 3) + m));
     }
 }
