@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
+    ap.add_argument("--index-fp8", action="store_true", help="E4M3 index queries and keys (FP8 index cache)")
     ap.add_argument("--no-nonshared", action="store_true", help="skip timing the group without IndexShare")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
@@ -97,10 +98,15 @@ def main():
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
     t0 = time.time()
-    q_idx = to_dev(cfg.q_idx())
+    idx_elem = 1 if args.index_fp8 else 2   # bytes per index-cache element
+    if args.index_fp8:
+        q_idx = torch.from_numpy(cfg.q_idx_fp8()).to(dev)
+        k_idx = torch.from_numpy(cfg.k_idx_fp8()).to(dev)
+    else:
+        q_idx = to_dev(cfg.q_idx())
+        k_idx = to_dev(cfg.k_idx())
     w = torch.from_numpy(cfg.w()).to(dev)
     q_pos = torch.from_numpy(cfg.q_pos()).to(dev)
-    k_idx = to_dev(cfg.k_idx())
     qs = [to_dev(cfg.q_attn(l)) for l in range(nl)]
     host_kv = np.empty((B, L, cfg.Dqk), np.uint16)
     kvs = []
@@ -128,8 +134,10 @@ def main():
 
     scores = ws[: B * T * L * 4].view(torch.float32).view(B, T, L)
 
+    indexer_fn = dsa.indexer_scores_fp8 if args.index_fp8 else dsa.indexer_scores
+
     def indexer_step():
-        dsa.indexer_scores(q_idx, w, k_idx, q_pos, scores=scores)
+        indexer_fn(q_idx, w, k_idx, q_pos, scores=scores)
 
     # ---------------- timed group steps
     if not args.indexer_only:
@@ -156,7 +164,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     idx_ms = e0.elapsed_time(e1) / args.steps
-    idx_bytes = B * T * (L * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4)
+    idx_bytes = B * T * (L * cfg.D * idx_elem + cfg.H * cfg.D * idx_elem + cfg.H * 4)
     log("bench: indexer %.3f ms, %.1f GB/s" % (idx_ms, idx_bytes / idx_ms / 1e6))
     if args.indexer_only:
         return
@@ -188,8 +196,11 @@ def main():
     # index-key cache (the same kernels, called per layer); the measured saving of sharing
     ns_ms = None
     if not args.no_nonshared and T == 1:
-        k_idx_l = [k_idx] + [to_dev(synth.int_bf16(cfg.seed, synth.T_K_IDX + 100 + l, (B, L, cfg.D)))
-                             for l in range(1, nl)]
+        def layer_keys(l):
+            kb = synth.int_bf16(cfg.seed, synth.T_K_IDX + 100 + l, (B, L, cfg.D))
+            return torch.from_numpy(synth.to_e4m3(synth.bf16_to_f32(kb))).to(dev) if args.index_fp8 else to_dev(kb)
+
+        k_idx_l = [k_idx] + [layer_keys(l) for l in range(1, nl)]
         idx_l = [torch.empty_like(idx) for _ in range(nl)]
         # one single-layer group per layer (the group entry point with n_layers = 1), args built once
         args_l = [dsa.make_group_args(q_idx, w, k_idx_l[l], q_pos, k, [qs[l]], [kvs[l]], cfg.sm_scale, idx_l[l],
@@ -218,11 +229,11 @@ def main():
     qtok = B * T
     value = qtok / (ms / 1e3)
     if T == 1:
-        step_bytes = qtok * synth.group_bytes_per_query(cfg)
+        step_bytes = qtok * synth.group_bytes_per_query(cfg, idx_elem=idx_elem)
     else:
         # a chunk of queries shares one key scan and gathers rows out of the same
         # cached layers: count each cache byte once, plus per-query inputs and outputs
-        step_bytes = (B * L * cfg.D * 2 + qtok * (cfg.H * cfg.D * 2 + cfg.H * 4 + k * 4)
+        step_bytes = (B * L * cfg.D * idx_elem + qtok * (cfg.H * cfg.D * idx_elem + cfg.H * 4 + k * 4)
                       + nl * (B * min(L, T * k) * cfg.Dqk * 2 + qtok * cfg.Hq * (cfg.Dqk + cfg.Dv) * 2))
     achieved = idx_bytes / (idx_ms / 1e3) / 1e9
     pos = cfg.q_pos().astype(np.int64)
@@ -239,16 +250,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8(e4m3) index scan, bf16 attention" if args.index_fp8 else "bf16",
         "data": "synthetic (seeded counter-based generator; GLM-5.2 shapes)",
-        "config": {"workload": cfg.name, "batch": B, "query_tokens_per_seq": T, "context": L, "topk": k,
+        "config": {"workload": cfg.name, "index_cache": "e4m3" if args.index_fp8 else "bf16",
+                   "batch": B, "query_tokens_per_seq": T, "context": L, "topk": k,
                    "layers_per_group": nl, "index_heads": cfg.H, "index_dim": cfg.D, "attn_heads": cfg.Hq,
                    "latent_dim": cfg.Dqk, "value_dim": cfg.Dv},
         "hbm_roofline_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": step_bytes,
-        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "indexer_decode_fp8_kernel" if args.index_fp8 else "indexer_decode_kernel",
+                     "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles("indexer", cfg.name),
+                     "traffic": traffic_from_profiles("indexer_fp8" if args.index_fp8 else "indexer", cfg.name),
                      "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 4)},
         "breakdown": breakdown,
         "cpu_baseline": None,
@@ -264,7 +277,7 @@ def main():
                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                         "indexer_tflops": round(idx_flops / (idx_ms / 1e3) / 1e12, 1)}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, index_fp8=args.index_fp8)
     print(json.dumps(line), flush=True)
 
 
@@ -281,10 +294,11 @@ def copy_calibrate(torch):
     log("bench: 5 copies of %d bytes done" % n)
 
 
-def cpu_baseline(cfg, target_s):
+def cpu_baseline(cfg, target_s, index_fp8=False):
     """The CPU oracle (oracle/, plain C fp64 + OpenMP), untuned, on whole
     sequences of the same workload: indexer over all L keys, top-k, and the
-    attention of every layer.  Runs sequences until about target_s seconds."""
+    attention of every layer.  Runs sequences until about target_s seconds.
+    index_fp8: the oracle reads E4M3 index queries and keys, as the GPU run does."""
     import numpy as np
 
     import oracle
@@ -298,14 +312,14 @@ def cpu_baseline(cfg, target_s):
     while spent < target_s and b < cfg.B:
         t1 = min(cfg.T, t_next + rows_per_call)
         sl = slice(t_next, t1)
-        qi = cfg.q_idx()[b:b + 1, sl]
+        qi = (cfg.q_idx_fp8() if index_fp8 else cfg.q_idx())[b:b + 1, sl]
         w = cfg.w()[b:b + 1, sl]
-        ki = cfg.k_idx_rows(b)[None]
+        ki = (cfg.k_idx_rows_fp8(b) if index_fp8 else cfg.k_idx_rows(b))[None]
         pos = cfg.q_pos()[b:b + 1, sl]
         qs = [cfg.q_attn(l)[b:b + 1, sl] for l in range(cfg.n_layers)]
         kvs = [cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
         t0 = time.perf_counter()
-        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
+        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale, idx_fp8=index_fp8)
         spent += time.perf_counter() - t0
         done += t1 - t_next
         t_next = t1
@@ -408,9 +422,10 @@ def bench_mtp(cfg, args):
         "mean_acceptance_length": round(accept_len, 3),
         "hbm_roofline_frac": round(B * seq_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": B * seq_bytes,
-        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "indexer_decode_fp8_kernel" if args.index_fp8 else "indexer_decode_kernel",
+                     "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles("indexer", cfg.name), "bytes_per_launch": idx_bytes,
+                     "traffic": traffic_from_profiles("indexer_fp8" if args.index_fp8 else "indexer", cfg.name), "bytes_per_launch": idx_bytes,
                      "avg_launch_ms": round(idx_ms, 4)},
         "breakdown": breakdown,
         "cpu_baseline": None,

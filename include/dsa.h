@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* Shapes fixed by the GLM-5.2 config ([TEARDOWN, 刀一 DSA]: index_n_heads 32,
  * index_head_dim 128, index_topk 2048; [TEARDOWN, 刀三 MLA]: kv_lora_rank
@@ -126,7 +126,8 @@ int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstrid
  * writes the shared list to idx_out, then runs dsa_sparse_mla_attn for each
  * layer with that same list, all on `stream`.  Layers stay separate launches:
  * in a model each layer's query depends on the previous layer's output.
- * struct_size must be sizeof(dsa_group_args); fields added later go at the end. */
+ * struct_size must be sizeof(dsa_group_args) or DSA_GROUP_ARGS_V1_SIZE;
+ * fields added later go at the end. */
 typedef struct {
     uint32_t struct_size;
     int n_layers;                          /* 1..DSA_GROUP_LAYERS_MAX (4 for a group) */
@@ -145,11 +146,38 @@ typedef struct {
     int64_t kv_bstride[DSA_GROUP_LAYERS_MAX];
     uint16_t* out[DSA_GROUP_LAYERS_MAX];        /* [B,T,64,512] */
     float* lse[DSA_GROUP_LAYERS_MAX];           /* [B,T,64] or NULL */
+    /* ABI version 2: FP8 (E4M3) caches, see "FP8 caches" below.  When
+     * q_idx_fp8 and k_idx_fp8 are set, the indexer reads them and q_idx /
+     * k_idx must be NULL (k_bstride then counts bytes).  When kv_fp8[l] is
+     * set, layer l reads its latent rows there and kv[l] must be NULL
+     * (kv_bstride[l] then counts bytes). */
+    const uint8_t* q_idx_fp8;                   /* [B,T,32,128] E4M3 */
+    const uint8_t* k_idx_fp8;                   /* rows of 128 E4M3 codes */
+    const uint8_t* kv_fp8[DSA_GROUP_LAYERS_MAX];  /* rows of 576 E4M3 codes */
 } dsa_group_args;
+/* Size of the version-1 struct (without the FP8 fields); still accepted as
+ * struct_size, with every FP8 field taken as NULL. */
+#define DSA_GROUP_ARGS_V1_SIZE offsetof(dsa_group_args, q_idx_fp8)
 
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a);
 int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- FP8 caches
+ * [CTXFR, "Entraînement par renforcement de l'agent intelligent"] names an FP8
+ * KV cache (it keeps rollout memory within budget).  These entry points take
+ * OCP E4M3 codes as uint8_t, one byte per element: bit 7 sign, bits 6..3 the
+ * exponent with bias 7, bits 2..0 the mantissa; exponent 0 encodes zero and
+ * subnormals (M/8 * 2^-6), S.1111.111 is NaN, there are no infinities and the
+ * largest finite value is 448.  The layouts, the masking rules and the
+ * definitions are those of the bf16 entry points, over the decoded values;
+ * strides count elements, which are bytes here, and must be multiples of 16.
+ *
+ * dsa_indexer_scores_fp8: q_idx and k_idx are E4M3.  E4M3 x E4M3 products are
+ * exact in fp32 and are summed in fp32, so the scores equal the bf16 entry
+ * point's whenever the decoded values are the same and every partial sum is
+ * representable (e.g. small-integer inputs). */
+int dsa_indexer_scores_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                           const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores, void* stream);
 /* ---------------------------------------------------------------- MTP verification
  * [MTPBLOG, "Rejection Sampling"]: summing min(p_v, q_v) over the vocabulary
  * gives the probability that a draft token is accepted; [MTPBLOG, "MTP"] and

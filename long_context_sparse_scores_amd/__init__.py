@@ -54,6 +54,7 @@ class GroupArgs(ctypes.Structure):
         ("q_idx", _P), ("w", _P), ("k_idx", _P), ("k_bstride", _I64), ("q_pos", _P), ("idx_out", _P),
         ("q", _P * GROUP_LAYERS_MAX), ("kv", _P * GROUP_LAYERS_MAX), ("kv_bstride", _I64 * GROUP_LAYERS_MAX),
         ("out", _P * GROUP_LAYERS_MAX), ("lse", _P * GROUP_LAYERS_MAX),
+        ("q_idx_fp8", _P), ("k_idx_fp8", _P), ("kv_fp8", _P * GROUP_LAYERS_MAX),
     ]
 
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_last_error.argtypes = []
         L.dsa_indexer_scores.restype = _I
         L.dsa_indexer_scores.argtypes = [_P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _P, _P]
+        L.dsa_indexer_scores_fp8.restype = _I
+        L.dsa_indexer_scores_fp8.argtypes = [_P, _P, _P, _I64, _P, _I, _I, _I, _I, _I, _P, _P]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk_workspace_size.argtypes = [_I, _I, _I, _I]
         L.dsa_topk.restype = _I
@@ -123,6 +126,7 @@ def _dev(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None) -> int:
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)   # OCP E4M3 codes
 
 
 def _workspace(nbytes: int, like: torch.Tensor, ws: Optional[torch.Tensor]) -> torch.Tensor:
@@ -146,6 +150,22 @@ def indexer_scores(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_
                                     _dev(k_idx, "k_idx", _BF16, 3), k_idx.shape[1] * k_idx.shape[2],
                                     _dev(q_pos, "q_pos", (torch.int32,), 2), B, T, L, H, D,
                                     _dev(scores, "scores", (torch.float32,), 3), _stream(q_idx)))
+    return scores
+
+
+def indexer_scores_fp8(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos: torch.Tensor,
+                       L: Optional[int] = None, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_idx [B,T,32,128] E4M3, w [B,T,32] f32, k_idx [B,Lc,128] E4M3, q_pos [B,T] int32
+    -> scores [B,T,L] f32 (dsa_indexer_scores_fp8).  E4M3 tensors are uint8 codes
+    or torch.float8_e4m3fn."""
+    B, T, H, D = q_idx.shape
+    L = k_idx.shape[1] if L is None else L
+    if scores is None:
+        scores = torch.empty((B, T, L), dtype=torch.float32, device=q_idx.device)
+    _check(lib().dsa_indexer_scores_fp8(_dev(q_idx, "q_idx", _FP8, 4), _dev(w, "w", (torch.float32,), 3),
+                                        _dev(k_idx, "k_idx", _FP8, 3), k_idx.shape[1] * k_idx.shape[2],
+                                        _dev(q_pos, "q_pos", (torch.int32,), 2), B, T, L, H, D,
+                                        _dev(scores, "scores", (torch.float32,), 3), _stream(q_idx)))
     return scores
 
 
@@ -207,9 +227,13 @@ def make_group_args(q_idx, w, k_idx, q_pos, k: int, qs: Sequence[torch.Tensor], 
     a = GroupArgs()
     a.struct_size = ctypes.sizeof(GroupArgs)
     a.n_layers, a.B, a.T, a.L, a.k, a.sm_scale = n, B, T, L, k, float(sm_scale)
-    a.q_idx = _dev(q_idx, "q_idx", _BF16, 4)
+    if q_idx.dtype in _FP8:  # E4M3 index queries and keys
+        a.q_idx_fp8 = _dev(q_idx, "q_idx", _FP8, 4)
+        a.k_idx_fp8 = _dev(k_idx, "k_idx", _FP8, 3)
+    else:
+        a.q_idx = _dev(q_idx, "q_idx", _BF16, 4)
+        a.k_idx = _dev(k_idx, "k_idx", _BF16, 3)
     a.w = _dev(w, "w", (torch.float32,), 3)
-    a.k_idx = _dev(k_idx, "k_idx", _BF16, 3)
     a.k_bstride = k_idx.shape[1] * k_idx.shape[2]
     a.q_pos = _dev(q_pos, "q_pos", (torch.int32,), 2)
     a.idx_out = _dev(idx_out, "idx_out", (torch.int32,), 3)
@@ -232,7 +256,8 @@ def layer_group_workspace_size(args: GroupArgs) -> int:
 def layer_group(q_idx, w, k_idx, q_pos, k: int, qs, kvs, sm_scale: float, want_lse: bool = False,
                 ws: Optional[torch.Tensor] = None, idx_out=None, outs=None, lses=None):
     """One IndexShare group (dsa_layer_group): indexer and top-k once, then
-    attention for every layer with that one index list.  Returns
+    attention for every layer with that one index list.  q_idx and k_idx are
+    bf16, or both E4M3 (uint8 codes / float8_e4m3fn).  Returns
     (idx, [out_l], [lse_l] or None)."""
     B, T = q_idx.shape[:2]
     dev = q_idx.device

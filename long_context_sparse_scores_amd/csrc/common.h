@@ -90,6 +90,11 @@ hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t*
                           const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
                           ZeroRange zero = ZeroRange());
 
+// The same scores from E4M3 index queries and keys (one byte per element).
+hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                              const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                              ZeroRange zero = ZeroRange());
+
 size_t topk_ws_bytes(int rows, int L, int k);
 // The part of the top-k workspace that must be zero when the selection starts.
 ZeroRange topk_state_range(void* ws, int rows, int L);

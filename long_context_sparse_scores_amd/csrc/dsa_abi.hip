@@ -35,8 +35,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxBlocks = (int64_t)1 << 31;
 
-int check_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                  const int32_t* q_pos, int B, int T, int L, int H, int D, const float* scores) {
+bool group_size_ok(uint32_t n) { return n == sizeof(dsa_group_args) || n == DSA_GROUP_ARGS_V1_SIZE; }
+
+// elem_bytes: 2 for bf16 index queries/keys, 1 for E4M3.
+int check_indexer(const void* q_idx, const float* w, const void* k_idx, int64_t k_bstride, const int32_t* q_pos,
+                  int B, int T, int L, int H, int D, const float* scores, int elem_bytes = 2) {
     if (!q_idx || !w || !k_idx || !q_pos || !scores) return fail(DSA_ERR_NULL, "indexer: NULL pointer argument");
     if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "indexer: B=%d T=%d L=%d must be >= 1", B, T, L);
     if (H != DSA_INDEX_HEADS || D != DSA_INDEX_DIM)
@@ -45,8 +48,9 @@ int check_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, 
     if (B > 1 && k_bstride < (int64_t)L * D)
         return fail(DSA_ERR_SHAPE, "indexer: k_bstride %lld < L*D", (long long)k_bstride);
     if ((int64_t)B * T * ((L + 2047) / 2048) >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "indexer: grid too large");
-    if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(scores) || (k_bstride % 8) != 0)
-        return fail(DSA_ERR_ALIGN, "indexer: pointers and k_bstride*2 bytes must be 16-byte aligned");
+    if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(scores) ||
+        ((k_bstride * elem_bytes) % 16) != 0)
+        return fail(DSA_ERR_ALIGN, "indexer: pointers and the key batch stride in bytes must be 16-byte aligned");
     return DSA_OK;
 }
 
@@ -94,6 +98,15 @@ int dsa_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_
                       "dsa_indexer_scores");
 }
 
+int dsa_indexer_scores_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                           const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores, void* stream) {
+    int st = check_indexer(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, H, D, scores, 1);
+    if (st != DSA_OK) return st;
+    return hip_status(
+        dsa::launch_indexer_fp8(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, (hipStream_t)stream),
+        "dsa_indexer_scores_fp8");
+}
+
 size_t dsa_topk_workspace_size(int B, int T, int L, int k) {
     if (B < 1 || T < 1 || L < 1) return 0;
     return dsa::topk_ws_bytes(B * T, L, k);
@@ -129,29 +142,41 @@ int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstrid
 
 // Workspace of a group: [scores B*T*L fp32][top-k scratch][attention scratch], each 256-byte aligned.
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a) {
-    if (!a || a->struct_size != sizeof(dsa_group_args) || a->B < 1 || a->T < 1 || a->L < 1 || a->k < 1 ||
-        a->k > DSA_TOPK_MAX)
+    if (!a || !group_size_ok(a->struct_size) || a->B < 1 || a->T < 1 || a->L < 1 || a->k < 1 || a->k > DSA_TOPK_MAX)
         return 0;
     const int rows = a->B * a->T;
     return dsa::align_up((size_t)rows * a->L * sizeof(float), 256) + dsa::topk_ws_bytes(rows, a->L, a->k) +
            dsa::attn_ws_bytes(rows, a->k);
 }
 
-int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream) {
-    if (!a) return fail(DSA_ERR_NULL, "group: NULL args");
-    if (a->struct_size != sizeof(dsa_group_args))
-        return fail(DSA_ERR_SHAPE, "group: struct_size %u, expected %zu", a->struct_size, sizeof(dsa_group_args));
+int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void* stream) {
+    if (!args) return fail(DSA_ERR_NULL, "group: NULL args");
+    if (!group_size_ok(args->struct_size))
+        return fail(DSA_ERR_SHAPE, "group: struct_size %u, expected %zu or %zu", args->struct_size,
+                    sizeof(dsa_group_args), (size_t)DSA_GROUP_ARGS_V1_SIZE);
+    // a version-1 struct ends before the FP8 fields: read only its bytes, the rest stays NULL
+    dsa_group_args full;
+    std::memset(&full, 0, sizeof(full));
+    std::memcpy(&full, args, args->struct_size);
+    const dsa_group_args* a = &full;
     if (a->n_layers < 1 || a->n_layers > DSA_GROUP_LAYERS_MAX)
         return fail(DSA_ERR_SHAPE, "group: n_layers=%d outside [1, %d]", a->n_layers, DSA_GROUP_LAYERS_MAX);
     const int B = a->B, T = a->T, L = a->L, k = a->k;
     // validate everything before enqueueing anything
-    int st = check_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS, DSA_INDEX_DIM,
-                           reinterpret_cast<const float*>(ws ? ws : (void*)16));
+    const bool idx_fp8 = a->q_idx_fp8 || a->k_idx_fp8;
+    if (idx_fp8 && (!a->q_idx_fp8 || !a->k_idx_fp8 || a->q_idx || a->k_idx))
+        return fail(DSA_ERR_SHAPE, "group: set q_idx_fp8 and k_idx_fp8 together, with q_idx and k_idx NULL");
+    const float* ws_scores = reinterpret_cast<const float*>(ws ? ws : (void*)16);
+    int st = idx_fp8 ? check_indexer(a->q_idx_fp8, a->w, a->k_idx_fp8, a->k_bstride, a->q_pos, B, T, L,
+                                     DSA_INDEX_HEADS, DSA_INDEX_DIM, ws_scores, 1)
+                     : check_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS,
+                                     DSA_INDEX_DIM, ws_scores, 2);
     if (st != DSA_OK) return st;
     if (!a->idx_out) return fail(DSA_ERR_NULL, "group: NULL idx_out");
     st = check_topk(reinterpret_cast<const float*>(16), a->q_pos, B, T, L, k, a->idx_out);
     if (st != DSA_OK) return st;
     for (int l = 0; l < a->n_layers; ++l) {
+        if (a->kv_fp8[l]) return fail(DSA_ERR_UNSUPPORTED, "group: kv_fp8 is not supported by this build");
         st = check_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS, DSA_LATENT_DIM,
                         DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l]);
         if (st != DSA_OK) return st;
@@ -167,8 +192,11 @@ int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* st
     void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
     hipStream_t s = (hipStream_t)stream;
     // the indexer also clears the top-k state, which saves the selection a launch
-    hipError_t e = dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores, s,
-                                       dsa::topk_state_range(topk_ws, rows, L));
+    const dsa::ZeroRange topk_state = dsa::topk_state_range(topk_ws, rows, L);
+    hipError_t e = idx_fp8 ? dsa::launch_indexer_fp8(a->q_idx_fp8, a->w, a->k_idx_fp8, a->k_bstride, a->q_pos, B, T,
+                                                     L, scores, s, topk_state)
+                           : dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores,
+                                                 s, topk_state);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
     e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s, /*state_zeroed=*/true);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");

@@ -131,6 +131,131 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     }
 }
 
+// ------------------------------------------------------------------ FP8 (E4M3) index keys
+// The same scan over an index-key cache stored as OCP E4M3 codes ([CTXFR,
+// "Entraînement par renforcement de l'agent intelligent"] names an FP8 KV
+// cache), with the index queries in E4M3 too: 128 bytes per key, half the HBM
+// stream.  v_mfma_f32_16x16x32_fp8_fp8 takes the same operand layout as the
+// bf16 instruction with one byte per element (lane l: A[l%16][8*(l/16) .. +7],
+// B[8*(l/16) .. +7][l%16]) and accumulates exactly in fp32 for the values the
+// products and sums here produce.
+//
+// A wave's tile is 32 keys (4 KiB): each 16-byte load instruction covers eight
+// whole keys (1 KiB contiguous).  Lane l brings 16-byte chunk l%8 of key
+// 8i + l/8; in the wave's LDS slot chunk s of key k sits at 16-byte position
+// 8k + (s ^ ((k >> 1) & 7)), so each 16-lane write phase fills 256 contiguous
+// bytes and each 32-lane read phase of the 8-byte B operands (key 16*kb + l%16,
+// chunk 2*kk + (l/16)/2, half (l/16)%2) touches every bank once.
+constexpr int kTile8 = 32;                      // keys per tile (two MFMA column blocks)
+constexpr int kD8 = 128;                        // bytes per key
+constexpr int kTile8Bytes = kTile8 * kD8;       // 4 KiB
+constexpr int kLoads8 = kTile8Bytes / (kWave * 16);  // 4 loads of 1 KiB per tile
+
+#ifndef INDEXER8_WAVES
+#define INDEXER8_WAVES 4
+#define INDEXER8_TILES 8
+#define INDEXER8_AHEAD 4
+#endif
+
+__device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <int kWaves, int kTilesPerWave, int kAhead8>
+__global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
+    ZeroRange zero) {
+    constexpr int kKeysPerBlock = kWaves * kTile8 * kTilesPerWave;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * kTile8Bytes];
+    const int row = blockIdx.x / nblk;  // b*T + t
+    const int blk = blockIdx.x % nblk;
+    const int b = row / T;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int64_t p = q_pos[row];
+    if (zero.base && blk == 0)
+        for (int i = threadIdx.x; i < zero.count; i += kWaves * kWave) zero.base[row * zero.stride + i] = 0u;
+
+    // A operands: head 16*ht + c, dims 32*kk + 8*g .. +7 (8 codes).
+    long qa[2][4];
+    const uint8_t* qrow = q_idx + (int64_t)row * kH * kD8;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qa[ht][kk] = *reinterpret_cast<const long*>(qrow + (16 * ht + c) * kD8 + 32 * kk + 8 * g);
+    float wv[2][4];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[ht][r] = w[(int64_t)row * kH + 16 * ht + 4 * g + r];
+
+    const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
+    const int64_t block_start = (int64_t)blk * kKeysPerBlock;
+    auto tile_key0 = [&](int j) { return block_start + (int64_t)(kWaves * j + wave) * kTile8; };
+    uint8_t* my_stage = stage + wave * 2 * kTile8Bytes;
+
+    u32x4_t buf[kAhead8 + 1][kLoads8];
+    auto load_tile = [&](int j, u32x4_t (&dst)[kLoads8]) {
+#pragma unroll
+        for (int i = 0; i < kLoads8; ++i) {
+            int64_t key = tile_key0(j) + 8 * i + (lane >> 3);
+            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
+            dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + key * kD8 + 16 * (lane & 7)));
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < kAhead8; ++j) load_tile(j, buf[j]);
+
+    float sc[kTilesPerWave];
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave; ++j) {
+        if (j + kAhead8 < kTilesPerWave) load_tile(j + kAhead8, buf[(j + kAhead8) % (kAhead8 + 1)]);
+        uint8_t* slot = my_stage + (j & 1) * kTile8Bytes;
+#pragma unroll
+        for (int i = 0; i < kLoads8; ++i) {
+            const int k = 8 * i + (lane >> 3);
+            *reinterpret_cast<u32x4_t*>(slot + 16 * (8 * k + ((lane & 7) ^ ((k >> 1) & 7)))) =
+                buf[j % (kAhead8 + 1)][i];
+        }
+        float part[2];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+            const int k = 16 * kbk + c;
+            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int s = 2 * kk + (g >> 1);
+                const long kv = *reinterpret_cast<const long*>(slot + 16 * (8 * k + (s ^ ((k >> 1) & 7))) + 8 * (g & 1));
+                a0 = mfma16x16x32_fp8(qa[0][kk], kv, a0);
+                a1 = mfma16x16x32_fp8(qa[1][kk], kv, a1);
+            }
+            float v = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
+                v = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+            }
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            part[kbk] = v;
+        }
+        // every lane of column c now holds both sums; lane group g < 2 keeps key 16*g + c
+        sc[j] = (g & 1) ? part[1] : part[0];
+    }
+    float* out = scores + (int64_t)row * L;
+    if (g < 2) {
+#pragma unroll
+        for (int j = 0; j < kTilesPerWave; ++j) {
+            const int64_t key = tile_key0(j) + 16 * g + c;
+            if (key < L) out[key] = key <= p ? sc[j] : -INFINITY;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ multi-query (prefill) chunks
 // A chunk of T >= 8 queries of one sequence is a dense contraction: 32*T query
 // heads against every key, 2*32*128 flops per (query, key).  One 256-thread
@@ -274,6 +399,25 @@ hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint1
     hipLaunchKernelGGL((indexer_decode_kernel<W, N>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx, k_bstride,
                        q_pos, T, L, nblk, scores, zero);
     return hipGetLastError();
+}
+
+template <int W, int N, int A>
+hipError_t launch_indexer_fp8_cfg(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                                  const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                                  ZeroRange zero) {
+    constexpr int keys_per_block = W * kTile8 * N;
+    const int nblk = (L + keys_per_block - 1) / keys_per_block;
+    dim3 grid((unsigned)((int64_t)nblk * B * T));
+    hipLaunchKernelGGL((indexer_decode_fp8_kernel<W, N, A>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx,
+                       k_bstride, q_pos, T, L, nblk, scores, zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                              const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                              ZeroRange zero) {
+    return launch_indexer_fp8_cfg<INDEXER8_WAVES, INDEXER8_TILES, INDEXER8_AHEAD>(q_idx, w, k_idx, k_bstride, q_pos,
+                                                                                  B, T, L, scores, stream, zero);
 }
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,

@@ -306,15 +306,17 @@ MTP = MtpConfig("mtp_draft_b16_128k", seed=5, B=16, L=131072)
 CONFIGS = {c.name: c for c in (TINY, DECODE_128K, PREFILL, DECODE_1M, MTP)}
 
 
-def group_bytes_per_query(cfg: GroupConfig) -> int:
+def group_bytes_per_query(cfg: GroupConfig, idx_elem: int = 2, kv_elem: int = 2) -> int:
     """Algorithmic HBM bytes one query token costs in a decode group step:
     the whole index-key scan, the gathered latent rows of every layer, the
     attention queries and outputs, the indexer query/weights and the index
-    list.  The score buffer is an implementation detail and is excluded."""
-    k_scan = cfg.L * cfg.D * 2
-    gather = cfg.n_layers * cfg.k * cfg.Dqk * 2
+    list.  The score buffer is an implementation detail and is excluded.
+    idx_elem / kv_elem: bytes per element of the index and latent caches
+    (2 for bf16, 1 for E4M3)."""
+    k_scan = cfg.L * cfg.D * idx_elem
+    gather = cfg.n_layers * cfg.k * cfg.Dqk * kv_elem
     q_att = cfg.n_layers * cfg.Hq * cfg.Dqk * 2
     out = cfg.n_layers * cfg.Hq * cfg.Dv * 2
-    q_idx_w = cfg.H * cfg.D * 2 + cfg.H * 4
+    q_idx_w = cfg.H * cfg.D * idx_elem + cfg.H * 4
     idx = cfg.k * 4
     return k_scan + gather + q_att + out + q_idx_w + idx

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(dsa):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = dsa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(dsa):
 
 
 def test_version_and_error_string(dsa):
-    assert dsa.abi_version() == 1
+    assert dsa.abi_version() == 2
     assert isinstance(dsa.last_error(), str)
 
 
@@ -50,13 +50,15 @@ def test_group_struct_layout_matches_c(dsa, tmp_path):
                    'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(dsa_group_args),'
                    ' offsetof(dsa_group_args, q_idx), offsetof(dsa_group_args, idx_out),'
                    ' offsetof(dsa_group_args, q), offsetof(dsa_group_args, kv_bstride),'
-                   ' offsetof(dsa_group_args, lse)); return 0;}\n')
+                   ' offsetof(dsa_group_args, lse));'
+                   ' printf("%zu %zu %zu\\n", offsetof(dsa_group_args, q_idx_fp8),'
+                   ' offsetof(dsa_group_args, kv_fp8), (size_t)DSA_GROUP_ARGS_V1_SIZE); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
     vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
     G = dsa.GroupArgs
     assert vals == [ctypes.sizeof(G), G.q_idx.offset, G.idx_out.offset, G.q.offset, G.kv_bstride.offset,
-                    G.lse.offset]
+                    G.lse.offset, G.q_idx_fp8.offset, G.kv_fp8.offset, G.q_idx_fp8.offset]
 
 
 def test_validation_rejects_before_launch(dsa):
@@ -90,6 +92,50 @@ def test_validation_rejects_before_launch(dsa):
     assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
     a.struct_size = ctypes.sizeof(dsa.GroupArgs)
     a.n_layers = 0
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    # FP8 indexer: NULLs, byte strides that break 16-byte alignment
+    assert lib.dsa_indexer_scores_fp8(None, None, None, 0, None, 1, 1, 16, 32, 128, None, None) == -1
+    assert lib.dsa_indexer_scores_fp8(fake, fake, fake, 16 * 128 + 8, fake, 2, 1, 16, 32, 128, fake, None) == -4
+    assert lib.dsa_indexer_scores_fp8(fake, fake, fake, 16 * 128, fake, 1, 1, 16, 32, 64, fake, None) == -3
+
+
+def _small_group(dsa, fake):
+    a = dsa.GroupArgs()
+    a.struct_size = ctypes.sizeof(dsa.GroupArgs)
+    a.n_layers, a.B, a.T, a.L, a.k, a.sm_scale = 1, 1, 1, 64, 16, 0.0625
+    a.w, a.q_pos, a.idx_out = fake, fake, fake
+    a.k_bstride = 64 * 128
+    a.q[0], a.out[0], a.kv_bstride[0] = fake, fake, 64 * 576
+    return a
+
+
+def test_group_fp8_field_rules(dsa):
+    lib = dsa.lib()
+    fake = 4096
+    a = _small_group(dsa, fake)
+    a.q_idx, a.k_idx, a.kv[0] = fake, fake, fake
+    a.q_idx_fp8 = fake  # bf16 and E4M3 index inputs together
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    assert "q_idx_fp8" in dsa.last_error()
+    a.q_idx = a.k_idx = None
+    a.q_idx_fp8 = fake  # E4M3 queries without E4M3 keys
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    a.k_idx_fp8 = fake  # complete: now only the missing workspace is reported
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5
+
+
+def test_group_accepts_version1_struct(dsa):
+    # a caller built against the version-1 header passes the shorter struct;
+    # the FP8 fields past its end are never read (here they hold garbage)
+    lib = dsa.lib()
+    fake = 4096
+    a = _small_group(dsa, fake)
+    a.q_idx, a.k_idx, a.kv[0] = fake, fake, fake
+    a.q_idx_fp8, a.k_idx_fp8 = 8, 24
+    a.struct_size = dsa.GroupArgs.q_idx_fp8.offset
+    assert lib.dsa_layer_group_workspace_size(ctypes.byref(a)) > 0
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5
+    a.struct_size = dsa.GroupArgs.q_idx_fp8.offset + 8
     assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
 
 
