@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
     ap.add_argument("--index-fp8", action="store_true", help="E4M3 index queries and keys (FP8 index cache)")
+    ap.add_argument("--kv-fp8", action="store_true", help="E4M3 latent rows (FP8 latent cache)")
     ap.add_argument("--no-nonshared", action="store_true", help="skip timing the group without IndexShare")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
@@ -108,12 +109,19 @@ def main():
     w = torch.from_numpy(cfg.w()).to(dev)
     q_pos = torch.from_numpy(cfg.q_pos()).to(dev)
     qs = [to_dev(cfg.q_attn(l)) for l in range(nl)]
-    host_kv = np.empty((B, L, cfg.Dqk), np.uint16)
+    kv_elem = 1 if args.kv_fp8 else 2   # bytes per latent-cache element
     kvs = []
-    for l in range(nl):
-        cfg.kv(l, out=host_kv)
-        kvs.append(to_dev(host_kv))
-    del host_kv
+    if args.kv_fp8:  # E4M3 rows, converted one sequence at a time
+        for l in range(nl):
+            kvs.append(torch.empty((B, L, cfg.Dqk), dtype=torch.uint8, device=dev))
+            for b in range(B):
+                kvs[l][b].copy_(torch.from_numpy(cfg.kv_seq_fp8(l, b)[0]))
+    else:
+        host_kv = np.empty((B, L, cfg.Dqk), np.uint16)
+        for l in range(nl):
+            cfg.kv(l, out=host_kv)
+            kvs.append(to_dev(host_kv))
+        del host_kv
     torch.cuda.synchronize()
     log("bench: inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
 
@@ -229,12 +237,12 @@ def main():
     qtok = B * T
     value = qtok / (ms / 1e3)
     if T == 1:
-        step_bytes = qtok * synth.group_bytes_per_query(cfg, idx_elem=idx_elem)
+        step_bytes = qtok * synth.group_bytes_per_query(cfg, idx_elem=idx_elem, kv_elem=kv_elem)
     else:
         # a chunk of queries shares one key scan and gathers rows out of the same
         # cached layers: count each cache byte once, plus per-query inputs and outputs
         step_bytes = (B * L * cfg.D * idx_elem + qtok * (cfg.H * cfg.D * idx_elem + cfg.H * 4 + k * 4)
-                      + nl * (B * min(L, T * k) * cfg.Dqk * 2 + qtok * cfg.Hq * (cfg.Dqk + cfg.Dv) * 2))
+                      + nl * (B * min(L, T * k) * cfg.Dqk * kv_elem + qtok * cfg.Hq * (cfg.Dqk + cfg.Dv) * 2))
     achieved = idx_bytes / (idx_ms / 1e3) / 1e9
     pos = cfg.q_pos().astype(np.int64)
     idx_flops = int(((np.minimum(pos, L - 1) + 1) * cfg.H * cfg.D * 2).sum())
@@ -250,9 +258,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8(e4m3) index scan, bf16 attention" if args.index_fp8 else "bf16",
+        "dtype": {(False, False): "bf16", (True, False): "fp8(e4m3) index scan, bf16 attention",
+                  (False, True): "bf16 index scan, bf16 attention over e4m3 rows",
+                  (True, True): "fp8(e4m3) index scan, bf16 attention over e4m3 rows"}[(args.index_fp8, args.kv_fp8)],
         "data": "synthetic (seeded counter-based generator; GLM-5.2 shapes)",
         "config": {"workload": cfg.name, "index_cache": "e4m3" if args.index_fp8 else "bf16",
+                   "latent_cache": "e4m3" if args.kv_fp8 else "bf16",
                    "batch": B, "query_tokens_per_seq": T, "context": L, "topk": k,
                    "layers_per_group": nl, "index_heads": cfg.H, "index_dim": cfg.D, "attn_heads": cfg.Hq,
                    "latent_dim": cfg.Dqk, "value_dim": cfg.Dv},
@@ -277,7 +288,7 @@ def main():
                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                         "indexer_tflops": round(idx_flops / (idx_ms / 1e3) / 1e12, 1)}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, index_fp8=args.index_fp8)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, index_fp8=args.index_fp8, kv_fp8=args.kv_fp8)
     print(json.dumps(line), flush=True)
 
 
@@ -294,7 +305,7 @@ def copy_calibrate(torch):
     log("bench: 5 copies of %d bytes done" % n)
 
 
-def cpu_baseline(cfg, target_s, index_fp8=False):
+def cpu_baseline(cfg, target_s, index_fp8=False, kv_fp8=False):
     """The CPU oracle (oracle/, plain C fp64 + OpenMP), untuned, on whole
     sequences of the same workload: indexer over all L keys, top-k, and the
     attention of every layer.  Runs sequences until about target_s seconds.
@@ -317,9 +328,9 @@ def cpu_baseline(cfg, target_s, index_fp8=False):
         ki = (cfg.k_idx_rows_fp8(b) if index_fp8 else cfg.k_idx_rows(b))[None]
         pos = cfg.q_pos()[b:b + 1, sl]
         qs = [cfg.q_attn(l)[b:b + 1, sl] for l in range(cfg.n_layers)]
-        kvs = [cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
+        kvs = [cfg.kv_seq_fp8(l, b) if kv_fp8 else cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
         t0 = time.perf_counter()
-        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale, idx_fp8=index_fp8)
+        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale, idx_fp8=index_fp8, kv_fp8=kv_fp8)
         spent += time.perf_counter() - t0
         done += t1 - t_next
         t_next = t1
@@ -343,6 +354,8 @@ def bench_mtp(cfg, args):
     import long_context_sparse_scores_amd as dsa
     import synth
 
+    if args.index_fp8 or args.kv_fp8:
+        raise SystemExit("bench.py: --index-fp8 / --kv-fp8 apply to the group workloads, not to %s" % cfg.name)
     dev = torch.device("cuda:0")
     B, L, S, V, k = cfg.B, cfg.L, cfg.S, cfg.V, cfg.k
     log("bench: workload %s B=%d L=%d steps=%d V=%d" % (cfg.name, B, L, S, V))
@@ -422,10 +435,9 @@ def bench_mtp(cfg, args):
         "mean_acceptance_length": round(accept_len, 3),
         "hbm_roofline_frac": round(B * seq_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": B * seq_bytes,
-        "roofline": {"kernel": "indexer_decode_fp8_kernel" if args.index_fp8 else "indexer_decode_kernel",
-                     "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles("indexer_fp8" if args.index_fp8 else "indexer", cfg.name), "bytes_per_launch": idx_bytes,
+                     "traffic": traffic_from_profiles("indexer", cfg.name), "bytes_per_launch": idx_bytes,
                      "avg_launch_ms": round(idx_ms, 4)},
         "breakdown": breakdown,
         "cpu_baseline": None,

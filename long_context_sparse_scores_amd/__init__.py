@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_attn_workspace_size.argtypes = [_I, _I, _I]
         L.dsa_sparse_mla_attn.restype = _I
         L.dsa_sparse_mla_attn.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
+        L.dsa_sparse_mla_attn_fp8kv.restype = _I
+        L.dsa_sparse_mla_attn_fp8kv.argtypes = [_P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]
         L.dsa_layer_group_workspace_size.restype = _SZ
         L.dsa_layer_group_workspace_size.argtypes = [ctypes.POINTER(GroupArgs)]
         L.dsa_layer_group.restype = _I
@@ -197,7 +199,8 @@ def sparse_mla_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, sm_sca
                     L: Optional[int] = None, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     want_lse: bool = False, ws: Optional[torch.Tensor] = None):
     """q [B,T,64,576] bf16, kv [B,Lc,576] bf16, idx [B,T,k] int32 -> out [B,T,64,512] bf16
-    (and lse [B,T,64] f32 when want_lse or lse is given) (dsa_sparse_mla_attn)."""
+    (and lse [B,T,64] f32 when want_lse or lse is given) (dsa_sparse_mla_attn).
+    An E4M3 kv (uint8 codes / float8_e4m3fn) goes to dsa_sparse_mla_attn_fp8kv."""
     B, T, Hq, Dqk = q.shape
     k = idx.shape[2]
     L = kv.shape[1] if L is None else L
@@ -207,6 +210,13 @@ def sparse_mla_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, sm_sca
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
     n = attn_workspace_size(B, T, k)
     ws = _workspace(n, q, ws)
+    if kv.dtype in _FP8:  # E4M3 latent rows
+        _check(lib().dsa_sparse_mla_attn_fp8kv(_dev(q, "q", _BF16, 4), _dev(kv, "kv", _FP8, 3),
+                                               kv.shape[1] * kv.shape[2], _dev(idx, "idx", (torch.int32,), 3), B, T, L,
+                                               Hq, Dqk, VALUE_DIM, k, float(sm_scale), _dev(out, "out", _BF16, 4),
+                                               None if lse is None else _dev(lse, "lse", (torch.float32,), 3),
+                                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q)))
+        return (out, lse) if lse is not None else out
     _check(lib().dsa_sparse_mla_attn(_dev(q, "q", _BF16, 4), _dev(kv, "kv", _BF16, 3), kv.shape[1] * kv.shape[2],
                                      _dev(idx, "idx", (torch.int32,), 3), B, T, L, Hq, Dqk, VALUE_DIM, k,
                                      float(sm_scale), _dev(out, "out", _BF16, 4),
@@ -239,7 +249,10 @@ def make_group_args(q_idx, w, k_idx, q_pos, k: int, qs: Sequence[torch.Tensor], 
     a.idx_out = _dev(idx_out, "idx_out", (torch.int32,), 3)
     for l in range(n):
         a.q[l] = _dev(qs[l], "q[%d]" % l, _BF16, 4)
-        a.kv[l] = _dev(kvs[l], "kv[%d]" % l, _BF16, 3)
+        if kvs[l].dtype in _FP8:
+            a.kv_fp8[l] = _dev(kvs[l], "kv[%d]" % l, _FP8, 3)
+        else:
+            a.kv[l] = _dev(kvs[l], "kv[%d]" % l, _BF16, 3)
         if kvs[l].shape[1] < L:
             raise ValueError("kv[%d] has %d rows < L=%d" % (l, kvs[l].shape[1], L))
         a.kv_bstride[l] = kvs[l].shape[1] * kvs[l].shape[2]

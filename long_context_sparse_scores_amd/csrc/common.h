@@ -108,6 +108,11 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
                        int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
                        hipStream_t stream);
 
+// The same attention over latent rows stored as E4M3 codes (kv_bstride in bytes).
+hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
+                           int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
+                           hipStream_t stream);
+
 size_t verify_ws_bytes(int B, int S, int V);
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* draft_tokens, const float* u_acc,
                          const float* u_res, int B, int S, int V, float* min_sum, int32_t* n_acc,

@@ -63,8 +63,10 @@ int check_topk(const float* scores, const int32_t* q_pos, int B, int T, int L, i
     return DSA_OK;
 }
 
-int check_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T, int L,
-               int Hq, int Dqk, int Dv, int k, float sm_scale, const uint16_t* out, const float* lse) {
+// elem_bytes: 2 for bf16 latent rows, 1 for E4M3.
+int check_attn(const uint16_t* q, const void* kv, int64_t kv_bstride, const int32_t* idx, int B, int T, int L,
+               int Hq, int Dqk, int Dv, int k, float sm_scale, const uint16_t* out, const float* lse,
+               int elem_bytes = 2) {
     if (!q || !kv || !idx || !out) return fail(DSA_ERR_NULL, "attn: NULL pointer argument");
     if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "attn: B=%d T=%d L=%d must be >= 1", B, T, L);
     if (L > DSA_ATTN_CONTEXT_MAX) return fail(DSA_ERR_SHAPE, "attn: L=%d above %d", L, DSA_ATTN_CONTEXT_MAX);
@@ -77,8 +79,8 @@ int check_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const 
         return fail(DSA_ERR_SHAPE, "attn: kv_bstride %lld < L*Dqk", (long long)kv_bstride);
     if ((int64_t)B * T * 64 >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "attn: grid too large");
     if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(out) || (lse && !aligned16(lse)) ||
-        (kv_bstride % 8) != 0)
-        return fail(DSA_ERR_ALIGN, "attn: pointers and kv_bstride*2 bytes must be 16-byte aligned");
+        ((kv_bstride * elem_bytes) % 16) != 0)
+        return fail(DSA_ERR_ALIGN, "attn: pointers and the kv batch stride in bytes must be 16-byte aligned");
     return DSA_OK;
 }
 
@@ -140,6 +142,19 @@ int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstrid
         "dsa_sparse_mla_attn");
 }
 
+int dsa_sparse_mla_attn_fp8kv(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
+                              int T, int L, int Hq, int Dqk, int Dv, int k, float sm_scale, uint16_t* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+    int st = check_attn(q, kv, kv_bstride, idx, B, T, L, Hq, Dqk, Dv, k, sm_scale, out, lse, 1);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::attn_ws_bytes(B * T, k);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(DSA_ERR_WORKSPACE, "attn: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes, need);
+    return hip_status(
+        dsa::launch_attn_fp8(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, (hipStream_t)stream),
+        "dsa_sparse_mla_attn_fp8kv");
+}
+
 // Workspace of a group: [scores B*T*L fp32][top-k scratch][attention scratch], each 256-byte aligned.
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a) {
     if (!a || !group_size_ok(a->struct_size) || a->B < 1 || a->T < 1 || a->L < 1 || a->k < 1 || a->k > DSA_TOPK_MAX)
@@ -176,9 +191,12 @@ int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void*
     st = check_topk(reinterpret_cast<const float*>(16), a->q_pos, B, T, L, k, a->idx_out);
     if (st != DSA_OK) return st;
     for (int l = 0; l < a->n_layers; ++l) {
-        if (a->kv_fp8[l]) return fail(DSA_ERR_UNSUPPORTED, "group: kv_fp8 is not supported by this build");
-        st = check_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS, DSA_LATENT_DIM,
-                        DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l]);
+        if (a->kv_fp8[l] && a->kv[l])
+            return fail(DSA_ERR_SHAPE, "group: layer %d has both kv and kv_fp8; set one of them", l);
+        st = a->kv_fp8[l] ? check_attn(a->q[l], a->kv_fp8[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS,
+                                       DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 1)
+                          : check_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS,
+                                       DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 2);
         if (st != DSA_OK) return st;
     }
     const size_t need = dsa_layer_group_workspace_size(a);
@@ -201,8 +219,10 @@ int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void*
     e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s, /*state_zeroed=*/true);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
     for (int l = 0; l < a->n_layers; ++l) {
-        e = dsa::launch_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, k, a->sm_scale, a->out[l],
-                             a->lse[l], attn_ws, s);
+        e = a->kv_fp8[l] ? dsa::launch_attn_fp8(a->q[l], a->kv_fp8[l], a->kv_bstride[l], a->idx_out, B, T, L, k,
+                                                a->sm_scale, a->out[l], a->lse[l], attn_ws, s)
+                         : dsa::launch_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, k, a->sm_scale,
+                                            a->out[l], a->lse[l], attn_ws, s);
         if (e != hipSuccess) return hip_status(e, "dsa_layer_group/attention");
     }
     return ok();

@@ -151,10 +151,11 @@ constexpr int kD8 = 128;                        // bytes per key
 constexpr int kTile8Bytes = kTile8 * kD8;       // 4 KiB
 constexpr int kLoads8 = kTile8Bytes / (kWave * 16);  // 4 loads of 1 KiB per tile
 
+// Measured best on MI355X for 128K x 32 and 1M x 4: 4 waves x 16 tiles of 32 keys, 6 tiles ahead.
 #ifndef INDEXER8_WAVES
 #define INDEXER8_WAVES 4
-#define INDEXER8_TILES 8
-#define INDEXER8_AHEAD 4
+#define INDEXER8_TILES 16
+#define INDEXER8_AHEAD 6
 #endif
 
 __device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, f32x4_t c) {

@@ -193,3 +193,112 @@ def test_fullsize_decode_128k_fp8_index(dsa):
         ki = cfg.k_idx_rows_fp8(b)[None]
         ref = oracle.indexer_scores(qi8[b:b + 1], w[b:b + 1], ki, pos[b:b + 1], fp8=True)
         _bits_equal(sc[b, 0], ref[0, 0])
+
+
+# ------------------------------------------------------------------ attention over E4M3 latent rows
+def _e4m3_as_bf16_dev(codes: np.ndarray) -> torch.Tensor:
+    """E4M3 codes widened to bf16 on the device by torch (exact for finite codes)."""
+    return u8_dev(codes).view(torch.float8_e4m3fn).to(torch.bfloat16)
+
+
+def _kv8(seed, B, L):
+    """Latent rows ~N(0,1) stored as E4M3 codes (about 1 % of them subnormal)."""
+    return synth.to_e4m3(synth.bf16_to_f32(synth.normal_bf16(seed, 2, (B, L, 576))))
+
+
+def test_attn_fp8kv_tiny_layers(dsa):
+    cfg = synth.TINY
+    say("fp8 attn tiny")
+    scores = oracle.indexer_scores(cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos())
+    idx = oracle.topk(scores, cfg.q_pos(), cfg.k)
+    for l in range(2):
+        q, kv8 = cfg.q_attn(l), cfg.kv_fp8(l)
+        out, lse = dsa.sparse_mla_attn(bf16_dev(q), u8_dev(kv8), i32_dev(idx), cfg.sm_scale, want_lse=True)
+        ref, ref_lse = oracle.sparse_mla_attn(q, kv8, idx, cfg.sm_scale, kv_fp8=True)
+        assert_attn_close(host(out), ref, "layer %d" % l)
+        np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
+@pytest.mark.parametrize("T,k", [(2, 16), (2, 40), (3, 64), (64, 300), (16, 2048), (40, 1000), (300, 100), (300, 33),
+                                 (300, 1024)])
+def test_attn_fp8kv_equals_bf16_path(dsa, T, k):
+    # The E4M3 rows are widened exactly and feed the same matrix-core code, so
+    # the outputs equal the bf16 entry point's on the widened rows bit for bit:
+    # split lists (few queries) and whole lists (T=300), 1..64 tiles, ragged
+    # tails, masked and out-of-range entries, rows with subnormal and +-448 codes.
+    rng = np.random.default_rng(100 + k + T)
+    B, L = 1, 5000
+    say("fp8 attn vs bf16 path T=%d k=%d" % (T, k))
+    q = synth.normal_bf16(60 + k, 1, (B, T, 64, 576))
+    kv8 = _kv8(60 + k, B, L)
+    kv8[0, 7] = rng.integers(0, 256, 576).astype(np.uint8)
+    kv8[0, 7][(kv8[0, 7] & 0x7F) == 0x7F] ^= 1  # full code range, no NaN
+    kv8[0, 8] = 0x01  # the smallest subnormal everywhere
+    idx = np.sort(np.stack([rng.choice(L, size=k, replace=False) for _ in range(T)]), axis=1)[None].astype(np.int32)
+    idx[0, 0, : min(k, 2)] = [7, 8][: min(k, 2)]
+    idx[0, -1, k // 2:] = -1
+    if k > 3:
+        idx[0, 0, 3] = L + 5
+    d_q, d_idx = bf16_dev(q), i32_dev(idx)
+    out8, lse8 = dsa.sparse_mla_attn(d_q, u8_dev(kv8), d_idx, 1 / 16, want_lse=True)
+    out16, lse16 = dsa.sparse_mla_attn(d_q, _e4m3_as_bf16_dev(kv8), d_idx, 1 / 16, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+    assert torch.equal(lse8.view(torch.int32), lse16.view(torch.int32))
+    sample = [0, T - 1]
+    ref, ref_lse = oracle.sparse_mla_attn(q[:, sample], kv8, idx[:, sample], 1 / 16, kv_fp8=True)
+    assert_attn_close(host(out8)[:, sample], ref)
+    np.testing.assert_allclose(host(lse8)[:, sample], ref_lse, atol=LSE_TOL, rtol=0)
+
+
+def test_group_fp8_caches_tiny(dsa):
+    # E4M3 index cache and E4M3 latent rows in one group
+    cfg = synth.TINY
+    say("group tiny, E4M3 index and latent caches")
+    qi, w, ki, pos = cfg.q_idx_fp8(), cfg.w(), cfg.k_idx_fp8(), cfg.q_pos()
+    qs = [cfg.q_attn(l) for l in range(cfg.n_layers)]
+    kvs = [cfg.kv_fp8(l) for l in range(cfg.n_layers)]
+    dq, dkv = [bf16_dev(q) for q in qs], [u8_dev(kv) for kv in kvs]
+    idx, outs, lses = dsa.layer_group(u8_dev(qi), f32_dev(w), u8_dev(ki), i32_dev(pos), cfg.k, dq, dkv,
+                                      cfg.sm_scale, want_lse=True)
+    _, ref_idx, ref_outs, ref_lses = oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale, idx_fp8=True,
+                                                        kv_fp8=True)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    for l in range(cfg.n_layers):
+        assert_attn_close(host(outs[l]), ref_outs[l], "layer %d" % l)
+        np.testing.assert_allclose(host(lses[l]), ref_lses[l], atol=LSE_TOL, rtol=0)
+        alone = dsa.sparse_mla_attn(dq[l], dkv[l], idx, cfg.sm_scale)
+        assert torch.equal(alone.view(torch.int16), outs[l].view(torch.int16))
+
+
+def test_fullsize_decode_128k_fp8_group(dsa):
+    # the FP8-cache group at the decode size (B=32, L=131072, 4 layers):
+    # index list bit-exact on sampled rows, attention on sampled (layer, b)
+    cfg = synth.DECODE_128K
+    say("fp8 group decode 128K: inputs")
+    qi8, w, pos = cfg.q_idx_fp8(), cfg.w(), cfg.q_pos()
+    d_ki = u8_dev(cfg.k_idx_fp8())
+    qs = [cfg.q_attn(l) for l in range(cfg.n_layers)]
+    dkv = []
+    for l in range(cfg.n_layers):
+        dkv.append(torch.empty((cfg.B, cfg.L, cfg.Dqk), dtype=torch.uint8, device=DEV))
+        for b in range(cfg.B):
+            dkv[l][b].copy_(torch.from_numpy(cfg.kv_seq_fp8(l, b)[0]))
+    say("fp8 group decode 128K: dsa_layer_group")
+    idx, outs, lses = dsa.layer_group(u8_dev(qi8), f32_dev(w), d_ki, i32_dev(pos), cfg.k,
+                                      [bf16_dev(q) for q in qs], dkv, cfg.sm_scale, want_lse=True)
+    torch.cuda.synchronize()
+    ix = host(idx)
+    for b in (0, 31):
+        say("  oracle index row b=%d" % b)
+        ki = cfg.k_idx_rows_fp8(b)[None]
+        ref_s = oracle.indexer_scores(qi8[b:b + 1], w[b:b + 1], ki, pos[b:b + 1], fp8=True)
+        np.testing.assert_array_equal(ix[b, 0], oracle.topk(ref_s, pos[b:b + 1], cfg.k)[0, 0])
+    for l, b in ((0, 0), (1, 7), (2, 31), (3, 13)):
+        sel = ix[b, 0][ix[b, 0] >= 0]
+        kv_sel = cfg.kv_rows_fp8(l, b, sel)[None]
+        ident = np.arange(sel.size, dtype=np.int32)[None, None]
+        ref, ref_lse = oracle.sparse_mla_attn(qs[l][b:b + 1], kv_sel, ident, cfg.sm_scale, kv_fp8=True)
+        err, scale = assert_attn_close(host(outs[l])[b, 0], ref[0, 0], "layer %d b %d" % (l, b))
+        say("  attn layer %d b=%d: max err %.3g of scale %.3g" % (l, b, err, scale))
+        np.testing.assert_allclose(host(lses[l])[b, 0], ref_lse[0, 0], atol=LSE_TOL, rtol=0)
