@@ -23,6 +23,11 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                   pinned: equal to the bf16 functions on values that both
                   formats hold exactly, plus the bf16 pins above; the E4M3
                   decoding enters only through e4m3_decode's element reads.
+  mtp_verify_target_only
+                  pinned: numpy argmax brute force, closed-form cases
+                  (all drafts the argmax, first-position miss, ties).
+  mtp_commit      pinned: numpy slice assignment, untouched rows, capacity.
+  mtp_round       composition of the pinned functions above.
   mtp_verify      pinned: sum-min identities (p=q -> 1, disjoint -> 0,
                   1 - TV distance), scipy softmax, Monte-Carlo check of the
                   speculative-sampling theorem (acceptance rate = sum-min,
@@ -56,11 +61,14 @@ def lib():
         L.oracle_indexer_scores_fp8.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i32, p]
         L.oracle_sparse_mla_attn_fp8kv.argtypes = [p, p, i64, p, i32, i32, i32, i32, i32, i32, i32, f64, p, p]
         L.oracle_e4m3_decode.argtypes = [p, i64, p]
+        L.oracle_mtp_verify_target_only.argtypes = [p, p, i32, i32, i32, p, p]
+        L.oracle_mtp_commit.argtypes = [p, p, p, p, p, i64, p, i64, i32, i32, i32, i32, i32, i32, p]
         L.oracle_softmax_row.argtypes = [p, i32, p]
         L.oracle_mtp_verify.argtypes = [p, p, p, p, p, i32, i32, i32, p, p, p, p]
         for fn in ("oracle_indexer_scores", "oracle_topk", "oracle_sparse_mla_attn", "oracle_layer_group",
                    "oracle_softmax_row", "oracle_mtp_verify", "oracle_indexer_scores_fp8",
-                   "oracle_sparse_mla_attn_fp8kv", "oracle_e4m3_decode"):
+                   "oracle_sparse_mla_attn_fp8kv", "oracle_e4m3_decode", "oracle_mtp_verify_target_only",
+                   "oracle_mtp_commit"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -188,3 +196,57 @@ def mtp_verify(target, draft, draft_tokens, u_acc, u_res):
     lib().oracle_mtp_verify(_p(target), _p(draft), _p(draft_tokens), _p(u_acc), _p(u_res), B, S, V,
                             _p(min_sum), _p(n_acc), _p(nxt), _p(ratio))
     return {"min_sum": min_sum, "n_acc": n_acc, "next_tok": nxt, "ratio": ratio}
+
+
+def mtp_verify_target_only(target, draft_tokens):
+    """target [B,S+1,V] f32, draft_tokens [B,S] int32 -> (n_acc [B], next_tok [B]):
+    drafts kept while each is the target's argmax (lowest index on ties)."""
+    target = _c(target, np.float32)
+    draft_tokens = _c(draft_tokens, np.int32)
+    B, S1, V = target.shape
+    S = S1 - 1
+    assert draft_tokens.shape == (B, S)
+    n_acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    lib().oracle_mtp_verify_target_only(_p(target), _p(draft_tokens), B, S, V, _p(n_acc), _p(nxt))
+    return n_acc, nxt
+
+
+def mtp_commit(n_acc, q_pos, new_k, new_kv, k_cache, kv_cache):
+    """Append the kept rows in place: new_k [B,S+1,Dk], new_kv [B,S+1,Dv] (same
+    element type as the caches k_cache [B,L,Dk], kv_cache [B,L,Dv]); returns
+    the next round's positions [B]."""
+    n_acc = _c(n_acc, np.int32)
+    q_pos = _c(q_pos, np.int32)
+    assert k_cache.flags["C_CONTIGUOUS"] and kv_cache.flags["C_CONTIGUOUS"]
+    assert new_k.dtype == k_cache.dtype and new_kv.dtype == kv_cache.dtype == k_cache.dtype
+    new_k = np.ascontiguousarray(new_k)
+    new_kv = np.ascontiguousarray(new_kv)
+    B, S1, Dk = new_k.shape
+    Dv = new_kv.shape[2]
+    L = k_cache.shape[1]
+    assert kv_cache.shape[1] == L
+    out = np.empty(B, np.int32)
+    lib().oracle_mtp_commit(_p(n_acc), _p(q_pos), _p(new_k), _p(new_kv), _p(k_cache), L * Dk, _p(kv_cache),
+                            L * Dv, B, S1 - 1, L, Dk, Dv, k_cache.itemsize, _p(out))
+    return out
+
+
+def mtp_round(q_idx, w, k_cache, q_pos, k, q_steps, kv_cache, sm_scale, target, draft, draft_tokens,
+              u_acc, u_res, new_k, new_kv, rule="rejection", Dv=512):
+    """One multi-token-prediction round, composed from the functions above in
+    the order the pages give: the step-1 indexer and top-k over the cache
+    (positions 0..q_pos), S draft attention steps that all reuse that list,
+    verification of the S drafts (rejection sampling, or the target-only
+    rule), and the commit of the kept rows.  Caches are updated in place.
+    Returns dict(idx, outs, n_acc, next_tok, q_pos_next)."""
+    scores = indexer_scores(q_idx, w, k_cache, q_pos)
+    idx = topk(scores, q_pos, k)
+    outs = [sparse_mla_attn(q, kv_cache, idx, sm_scale, Dv=Dv)[0] for q in q_steps]
+    if rule == "rejection":
+        r = mtp_verify(target, draft, draft_tokens, u_acc, u_res)
+        n_acc, nxt = r["n_acc"], r["next_tok"]
+    else:
+        n_acc, nxt = mtp_verify_target_only(target, draft_tokens)
+    q_next = mtp_commit(n_acc, q_pos.reshape(-1), new_k, new_kv, k_cache, kv_cache)
+    return {"idx": idx, "outs": outs, "n_acc": n_acc, "next_tok": nxt, "q_pos_next": q_next}

@@ -357,3 +357,67 @@ void oracle_mtp_verify(const float* target, const float* draft, const int32_t* d
         free(qd);
     }
 }
+
+/* ------------------------------------------------------------------ target-only verification
+ * [MTPBLOG, "Rejection Sampling"]: the rule that rejection sampling replaced
+ * ("Target-Only") keeps a draft token only when it is the target model's own
+ * first choice.  Reading: the first choice is the argmax of the target
+ * logits (the lowest index among equal maxima); at the first draft that is
+ * not, the target's first choice there becomes the next token and the rest
+ * is dropped; when all S drafts are kept, the next token is the first choice
+ * of the target distribution after the last draft.
+ *   n_acc[b] = number of leading i with draft_tokens[b,i] == argmax target[b,i]
+ *   next_tok[b] = argmax target[b, n_acc[b]]
+ * Layouts: target [B,S+1,V], draft_tokens [B,S], n_acc/next_tok [B].
+ */
+static int32_t argmax_row(const float* x, int V) {
+    int32_t best = 0;
+    for (int v = 1; v < V; ++v)
+        if (x[v] > x[best]) best = v;
+    return best;
+}
+
+void oracle_mtp_verify_target_only(const float* target, const int32_t* draft_tokens, int B, int S, int V,
+                                   int32_t* n_acc, int32_t* next_tok) {
+    for (int b = 0; b < B; ++b) {
+        int i = 0;
+        while (i < S && draft_tokens[(int64_t)b * S + i] == argmax_row(target + ((int64_t)b * (S + 1) + i) * V, V))
+            ++i;
+        n_acc[b] = i;
+        next_tok[b] = argmax_row(target + ((int64_t)b * (S + 1) + i) * V, V);
+    }
+}
+
+/* ------------------------------------------------------------------ cache commit after verification
+ * [SPECYUN, MTP / KV Share]: the draft layers reuse the backbone's cache and
+ * only newly produced tokens get new cache rows; [MTPBLOG, "MTP"] and
+ * [TEARDOWN, 刀四 MTP]: drafts after the first rejection are dropped and the
+ * next round starts from the verified tokens.  Reading: a round starts with
+ * the rows of positions 0..q_pos[b] cached (q_pos[b] is the position of the
+ * last verified token, whose row is cached).  The verifying pass produces the
+ * rows of positions q_pos[b]+1 .. q_pos[b]+S+1 (new_k, new_kv; row j for
+ * position q_pos[b]+1+j); the n_acc[b] accepted drafts and the next token are
+ * kept, i.e. rows j = 0..n_acc[b], and the next round's position is
+ * q_pos[b] + n_acc[b] + 1.  Rows at positions >= L (the cache capacity) are
+ * not written and the position stops at L-1.
+ * Layouts: new_k [B,S+1,Dk], new_kv [B,S+1,Dv] (any element type of esz
+ * bytes), caches with batch strides k_bstride / kv_bstride in elements.
+ */
+void oracle_mtp_commit(const int32_t* n_acc, const int32_t* q_pos_in, const void* new_k, const void* new_kv,
+                       void* k_cache, int64_t k_bstride, void* kv_cache, int64_t kv_bstride, int B, int S, int L,
+                       int Dk, int Dv, int esz, int32_t* q_pos_out) {
+    for (int b = 0; b < B; ++b) {
+        const int64_t p = q_pos_in[b];
+        const int n = n_acc[b];
+        for (int j = 0; j <= n; ++j) {
+            const int64_t pos = p + 1 + j;
+            if (pos >= L) break;
+            memcpy((char*)k_cache + ((int64_t)b * k_bstride + pos * Dk) * esz,
+                   (const char*)new_k + (((int64_t)b * (S + 1) + j) * Dk) * esz, (size_t)Dk * esz);
+            memcpy((char*)kv_cache + ((int64_t)b * kv_bstride + pos * Dv) * esz,
+                   (const char*)new_kv + (((int64_t)b * (S + 1) + j) * Dv) * esz, (size_t)Dv * esz);
+        }
+        const int64_t np = p + n + 1;
+        q_pos_out[b] = (int32_t)(np < L ? np : L - 1);
+    }
+}
