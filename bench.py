@@ -17,7 +17,11 @@ Other workloads (--workload): decode_1m_b4 and tiny_decode_8k time the same
 group step; prefill_4096_at_128k times it for a 4096-query chunk and reports
 the fraction of the bf16 MFMA peak; mtp_draft_b16_128k times one MTP draft
 round (step-1 indexer and top-k over the backbone index keys, 7 attention
-steps over the backbone latent cache with the step-1 list, verification).
+steps over the backbone latent cache with the step-1 list, verification);
+mtp_rounds_b16_128k times 8 chained rounds of draft -> verify -> commit (the
+kept rows appended on the device) with rejection sampling and, for an A/B,
+with the target-only rule.  --index-fp8 / --kv-fp8 run the group workloads
+over E4M3 index-key / latent caches.
 """
 import argparse
 import json
@@ -44,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_128k_b32",
                     help="decode_128k_b32 (default), decode_1m_b4, prefill_4096_at_128k, tiny_decode_8k, "
-                         "mtp_draft_b16_128k")
+                         "mtp_draft_b16_128k, mtp_rounds_b16_128k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time for the oracle sample")
     ap.add_argument("--indexer-only", action="store_true", help="time only the indexer (for counter runs)")
@@ -90,6 +94,9 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     if isinstance(cfg, synth.MtpConfig):
         bench_mtp(cfg, args)
+        return
+    if isinstance(cfg, synth.MtpRoundsConfig):
+        bench_mtp_rounds(cfg, args)
         return
     dev = torch.device("cuda:0")
     B, T, L, k, nl = cfg.B, cfg.T, cfg.L, cfg.k, cfg.n_layers
@@ -445,6 +452,190 @@ def bench_mtp(cfg, args):
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_mtp(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def bench_mtp_rounds(cfg, args):
+    """A step is R chained MTP rounds for B sequences, all on the device: the
+    step-1 indexer and top-k over the cache up to each sequence's position, S
+    draft attention steps with that list, verification of the S drafts, and
+    the commit that appends the kept rows and advances the positions (the host
+    reads nothing between rounds).  Every step starts from the same positions;
+    the commit rewrites the same rows, so steps are identical.  The value is
+    verified tokens per second (sum over sequences and rounds of n_accepted+1)
+    with rejection sampling; the target-only rule is timed as an A/B."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_scores_amd as dsa
+    import synth
+
+    if args.index_fp8 or args.kv_fp8:
+        raise SystemExit("bench.py: --index-fp8 / --kv-fp8 apply to the group workloads, not to %s" % cfg.name)
+    dev = torch.device("cuda:0")
+    B, L, R, S, V, k = cfg.B, cfg.L, cfg.R, cfg.S, cfg.V, cfg.k
+    log("bench: workload %s B=%d L0=%d capacity=%d rounds=%d steps=%d V=%d" % (cfg.name, B, cfg.L0, L, R, S, V))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.time()
+    k_cache = bf(cfg.k_idx())
+    kv_cache = torch.empty((B, L, cfg.Dqk), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        kv_cache[b].copy_(bf(cfg.kv_seq(b)))
+    rounds = []
+    for r in range(R):
+        t = cfg.target_logits(r)
+        d = cfg.draft_logits(r, t)
+        qs = cfg.q_steps(r)
+        rounds.append({"q_idx": bf(cfg.q_idx(r)), "w": torch.from_numpy(cfg.w(r)).to(dev),
+                       "q_steps": [bf(np.ascontiguousarray(qs[:, s:s + 1])) for s in range(S)],
+                       "target": torch.from_numpy(t).to(dev), "draft": torch.from_numpy(d).to(dev),
+                       "tok": torch.from_numpy(cfg.draft_tokens(r, d)).to(dev),
+                       "u": torch.from_numpy(cfg.u_accept(r)).to(dev), "ur": torch.from_numpy(cfg.u_resample(r)).to(dev),
+                       "new_k": bf(cfg.new_k(r)), "new_kv": bf(cfg.new_kv(r))})
+        del t, d, qs
+    q_pos0 = torch.from_numpy(cfg.q_pos0()).to(dev)
+    torch.cuda.synchronize()
+    log("bench: inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
+
+    qp = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, 1, cfg.Hq, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    topk_ws = torch.empty(dsa.topk_workspace_size(B, 1, L, k), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, 1, k)), dtype=torch.uint8, device=dev)
+    ver_ws = torch.empty(max(dsa.verify_workspace_size(B, S, V), dsa.lib().mtp_verify_target_only_workspace_size(B, S, V)),
+                         dtype=torch.uint8, device=dev)
+    n_acc = torch.empty((R, B), dtype=torch.int32, device=dev)
+    nxt = torch.empty((R, B), dtype=torch.int32, device=dev)
+    min_sum = torch.empty((B, S), dtype=torch.float32, device=dev)
+    lib = dsa.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def run_step(rule):
+        qp[0].copy_(q_pos0)
+        for r in range(R):
+            rd, cur, nb = rounds[r], qp[r % 2], qp[(r + 1) % 2]
+            pos2 = cur.view(B, 1)
+            dsa.indexer_scores(rd["q_idx"], rd["w"], k_cache, pos2, scores=scores)
+            dsa.topk(scores, pos2, k, idx=idx, ws=topk_ws)
+            for s in range(S):
+                dsa.sparse_mla_attn(rd["q_steps"][s], kv_cache, idx, cfg.sm_scale, out=outs[s], ws=attn_ws)
+            if rule == "rejection":
+                rc = lib.mtp_draft_verify(rd["target"].data_ptr(), rd["draft"].data_ptr(), rd["tok"].data_ptr(),
+                                          rd["u"].data_ptr(), rd["ur"].data_ptr(), B, S, V, min_sum.data_ptr(),
+                                          n_acc[r].data_ptr(), nxt[r].data_ptr(), ver_ws.data_ptr(),
+                                          ver_ws.numel(), stream)
+            else:
+                rc = lib.mtp_verify_target_only(rd["target"].data_ptr(), rd["tok"].data_ptr(), B, S, V,
+                                                n_acc[r].data_ptr(), nxt[r].data_ptr(), ver_ws.data_ptr(),
+                                                ver_ws.numel(), stream)
+            if rc != 0:
+                raise RuntimeError(dsa.last_error())
+            dsa.mtp_commit(n_acc[r], cur, rd["new_k"], rd["new_kv"], k_cache, kv_cache, q_pos_out=nb)
+
+    def timed(rule, steps):
+        for _ in range(args.warmup):
+            run_step(rule)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run_step(rule)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tokens = int((n_acc.to(torch.int64) + 1).sum().item())
+        return ms, tokens, (n_acc.float() + 1).mean(dim=1).cpu().numpy()
+
+    res = {}
+    for rule in ("rejection", "target_only"):
+        ms, tokens, per_round = timed(rule, args.steps)
+        res[rule] = {"ms_per_step": round(ms, 4), "verified_tokens_per_step": tokens,
+                     "verified_tokens_per_s": round(tokens / (ms / 1e3), 1),
+                     "mean_acceptance_length": round(tokens / (B * R), 3),
+                     "acceptance_length_per_round": [round(float(x), 3) for x in per_round]}
+        log("bench: %s: %.3f ms per %d rounds, %d verified tokens, mean acceptance length %.3f"
+            % (rule, ms, R, tokens, tokens / (B * R)))
+    # the index-key scan of one round, timed alone (the roofline figure)
+    rd0 = rounds[0]
+    qp[0].copy_(q_pos0)
+
+    def indexer_step():
+        dsa.indexer_scores(rd0["q_idx"], rd0["w"], k_cache, qp[0].view(B, 1), scores=scores)
+
+    for _ in range(args.warmup):
+        indexer_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        indexer_step()
+    e1.record()
+    torch.cuda.synchronize()
+    idx_ms = e0.elapsed_time(e1) / args.steps
+    idx_bytes = B * (L * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4)
+    achieved = idx_bytes / (idx_ms / 1e3) / 1e9
+    main = res["rejection"]
+    line = {
+        "metric": "verified tokens/s in chained MTP rounds (draft 7 -> verify -> commit) at 128K ctx",
+        "value": main["verified_tokens_per_s"],
+        "unit": "verified-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; GLM-5.2 shapes; favoured-token logits)",
+        "config": {"workload": cfg.name, "batch": B, "context_start": cfg.L0, "capacity": L, "rounds": R,
+                   "draft_steps": S, "vocab": V, "topk": k, "rho": cfg.rho, "boost": cfg.boost},
+        "rejection_sampling": res["rejection"],
+        "target_only": res["target_only"],
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_mtp_rounds(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_mtp_rounds(cfg, target_s):
+    """The oracle's composed round (indexer, top-k, S attention steps,
+    rejection-sampling verification, commit) on whole sequences, one at a
+    time, over the rounds until about target_s seconds; verified tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    spent, tokens, done = 0.0, 0, 0
+    for b in range(cfg.B):
+        k_cache = cfg.k_idx()[b:b + 1].copy() if b == 0 else None
+        if k_cache is None:
+            break  # one sequence is enough for the bounded sample
+        kv_cache = cfg.kv_seq(b)[None].copy()
+        q_pos = cfg.q_pos0()[b:b + 1].copy()
+        for r in range(cfg.R):
+            t = cfg.target_logits(r)
+            d = cfg.draft_logits(r, t)
+            tok = cfg.draft_tokens(r, d)
+            qs = cfg.q_steps(r)
+            t0 = time.perf_counter()
+            out = oracle.mtp_round(cfg.q_idx(r)[b:b + 1], cfg.w(r)[b:b + 1], k_cache, q_pos.reshape(1, 1), cfg.k,
+                                   [np.ascontiguousarray(qs[b:b + 1, s:s + 1]) for s in range(cfg.S)], kv_cache,
+                                   cfg.sm_scale, t[b:b + 1], d[b:b + 1], tok[b:b + 1], cfg.u_accept(r)[b:b + 1],
+                                   cfg.u_resample(r)[b:b + 1], cfg.new_k(r)[b:b + 1], cfg.new_kv(r)[b:b + 1])
+            spent += time.perf_counter() - t0
+            tokens += int(out["n_acc"][0]) + 1
+            q_pos = out["q_pos_next"]
+            done += 1
+            log("bench: cpu oracle round %d of sequence %d, %.2f s" % (r, b, spent))
+            if spent >= target_s:
+                break
+    return {"value": round(tokens / spent, 3), "unit": "verified-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d round(s) of sequence 0 of %s, each the whole round: indexer over the visible keys, top-%d, "
+                      "%d draft attention steps, rejection-sampling verification over V=%d, commit; fp64 plain C "
+                      "with OpenMP" % (done, cfg.name, cfg.k, cfg.S, cfg.V)}
 
 
 def cpu_baseline_mtp(cfg, target_s):

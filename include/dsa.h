@@ -216,6 +216,39 @@ int mtp_draft_verify(const float* target_logits, const float* draft_logits, cons
                      const float* u_accept, const float* u_resample, int B, int S, int V, float* min_sum,
                      int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- multi-round MTP loop
+ * [MTPBLOG, "MTP"] and [TEARDOWN, 刀四 MTP]: generation runs in rounds of
+ * draft -> verify -> keep the accepted prefix, the next round starting from
+ * the verified tokens.
+ *
+ * mtp_verify_target_only: the rule rejection sampling replaced ([MTPBLOG,
+ * "Rejection Sampling"], "Target-Only"): a draft is kept while it is the
+ * target model's first choice,
+ *   n_accepted[b] = number of leading i with draft_tokens[b,i] == argmax_v target_logits[b,i,v]
+ *   next_token[b] = argmax_v target_logits[b, n_accepted[b], v]
+ * with the lowest index among equal maxima.  Logits must be finite.
+ *   target_logits [B,S+1,V] fp32, draft_tokens [B,S] int32; n_accepted,
+ *   next_token [B] int32 (outputs).  1 <= S <= 64. */
+size_t mtp_verify_target_only_workspace_size(int B, int S, int V);
+int mtp_verify_target_only(const float* target_logits, const int32_t* draft_tokens, int B, int S, int V,
+                           int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream);
+/* dsa_mtp_commit: [SPECYUN, MTP / KV Share]: the draft layers read the
+ * backbone's cache and only new tokens get new cache rows.  A round starts
+ * with positions 0..q_pos_in[b] cached; the verifying pass has produced the
+ * rows of positions q_pos_in[b]+1 .. q_pos_in[b]+S+1 (new_k_idx, new_kv: row j
+ * for position q_pos_in[b]+1+j).  Rows j = 0..n_accepted[b] (the accepted
+ * drafts and the next token) are written into the caches, the rest dropped,
+ * and q_pos_out[b] = q_pos_in[b] + n_accepted[b] + 1, the position of the next
+ * round's first query.  Positions >= L (the capacity) are not written and
+ * q_pos_out stops at L-1.  Everything happens on the device: n_accepted is
+ * read there, so rounds chain without a host round trip.  q_pos_out must not
+ * alias q_pos_in (alternate two buffers).
+ *   new_k_idx [B,S+1,128] and k_idx_cache rows of k_elem_bytes (2 bf16, 1 E4M3);
+ *   new_kv [B,S+1,576] and kv_cache rows of kv_elem_bytes; strides in elements.
+ *   0 <= n_accepted[b] <= S and 0 <= q_pos_in[b] < L are required. */
+int dsa_mtp_commit(const int32_t* n_accepted, const int32_t* q_pos_in, const void* new_k_idx, const void* new_kv,
+                   void* k_idx_cache, int64_t k_bstride, int k_elem_bytes, void* kv_cache, int64_t kv_bstride,
+                   int kv_elem_bytes, int B, int S, int L, int32_t* q_pos_out, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.dsa_layer_group_workspace_size.argtypes = [ctypes.POINTER(GroupArgs)]
         L.dsa_layer_group.restype = _I
         L.dsa_layer_group.argtypes = [ctypes.POINTER(GroupArgs), _P, _SZ, _P]
+        L.mtp_verify_target_only_workspace_size.restype = _SZ
+        L.mtp_verify_target_only_workspace_size.argtypes = [_I, _I, _I]
+        L.mtp_verify_target_only.restype = _I
+        L.mtp_verify_target_only.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]
+        L.dsa_mtp_commit.restype = _I
+        L.dsa_mtp_commit.argtypes = [_P, _P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _P, _P]
         L.mtp_verify_workspace_size.restype = _SZ
         L.mtp_verify_workspace_size.argtypes = [_I, _I, _I]
         L.mtp_draft_verify.restype = _I
@@ -312,3 +318,55 @@ def mtp_draft_verify(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
                                   n_acc.data_ptr(), nxt.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                                   _stream(target)))
     return min_sum, n_acc, nxt
+
+
+# ------------------------------------------------------------------ multi-round MTP loop
+def mtp_verify_target_only(target: torch.Tensor, draft_tokens: torch.Tensor, n_acc: Optional[torch.Tensor] = None,
+                           next_tok: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """target [B,S+1,V] f32, draft_tokens [B,S] int32 -> (n_accepted [B], next_token [B]) int32
+    (mtp_verify_target_only: drafts kept while each is the target's argmax)."""
+    B, S1, V = target.shape
+    S = S1 - 1
+    dev = target.device
+    if n_acc is None:
+        n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(lib().mtp_verify_target_only_workspace_size(B, S, V), target, ws)
+    _check(lib().mtp_verify_target_only(_dev(target, "target", (torch.float32,), 3),
+                                        _dev(draft_tokens, "draft_tokens", (torch.int32,), 2), B, S, V,
+                                        _dev(n_acc, "n_acc", (torch.int32,), 1),
+                                        _dev(next_tok, "next_tok", (torch.int32,), 1), ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), _stream(target)))
+    return n_acc, next_tok
+
+
+def _elem_bytes(t: torch.Tensor, name: str) -> int:
+    if t.dtype in _FP8:
+        return 1
+    if t.dtype in _BF16:
+        return 2
+    raise TypeError("%s has dtype %s: bf16 or E4M3 expected" % (name, t.dtype))
+
+
+def mtp_commit(n_acc: torch.Tensor, q_pos_in: torch.Tensor, new_k_idx: torch.Tensor, new_kv: torch.Tensor,
+               k_idx_cache: torch.Tensor, kv_cache: torch.Tensor, q_pos_out: Optional[torch.Tensor] = None):
+    """Keep the rows of the accepted drafts and of the next token (dsa_mtp_commit):
+    new_k_idx [B,S+1,128] and new_kv [B,S+1,576] (element types of the caches
+    k_idx_cache [B,L,128], kv_cache [B,L,576]) -> q_pos_out [B] int32."""
+    B, S1, _ = new_k_idx.shape
+    L = k_idx_cache.shape[1]
+    if kv_cache.shape[1] != L:
+        raise ValueError("the two caches must hold the same number of rows")
+    ek, ekv = _elem_bytes(k_idx_cache, "k_idx_cache"), _elem_bytes(kv_cache, "kv_cache")
+    if _elem_bytes(new_k_idx, "new_k_idx") != ek or _elem_bytes(new_kv, "new_kv") != ekv:
+        raise TypeError("new rows must have the element types of their caches")
+    if q_pos_out is None:
+        q_pos_out = torch.empty((B,), dtype=torch.int32, device=n_acc.device)
+    allt = (torch.uint8, torch.float8_e4m3fn) + _BF16
+    _check(lib().dsa_mtp_commit(_dev(n_acc, "n_acc", (torch.int32,), 1), _dev(q_pos_in, "q_pos_in", (torch.int32,)),
+                                _dev(new_k_idx, "new_k_idx", allt, 3), _dev(new_kv, "new_kv", allt, 3),
+                                _dev(k_idx_cache, "k_idx_cache", allt, 3), L * k_idx_cache.shape[2], ek,
+                                _dev(kv_cache, "kv_cache", allt, 3), L * kv_cache.shape[2], ekv, B, S1 - 1, L,
+                                _dev(q_pos_out, "q_pos_out", (torch.int32,)), _stream(n_acc)))
+    return q_pos_out

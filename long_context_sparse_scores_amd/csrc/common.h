@@ -118,6 +118,13 @@ hipError_t launch_verify(const float* target, const float* draft, const int32_t*
                          const float* u_res, int B, int S, int V, float* min_sum, int32_t* n_acc,
                          int32_t* next_tok, void* ws, hipStream_t stream);
 
+size_t target_only_ws_bytes(int B, int S, int V);
+hipError_t launch_target_only(const float* target, const int32_t* draft_tokens, int B, int S, int V,
+                              int32_t* n_acc, int32_t* next_tok, void* ws, hipStream_t stream);
+hipError_t launch_mtp_commit(const int32_t* n_acc, const int32_t* q_pos_in, const void* new_k, const void* new_kv,
+                             void* k_cache, int64_t k_bstride_bytes, void* kv_cache, int64_t kv_bstride_bytes, int B,
+                             int S, int L, int k_row_bytes, int kv_row_bytes, int32_t* q_pos_out, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace dsa

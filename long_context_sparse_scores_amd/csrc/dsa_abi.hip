@@ -252,4 +252,48 @@ int mtp_draft_verify(const float* target_logits, const float* draft_logits, cons
                       "mtp_draft_verify");
 }
 
+size_t mtp_verify_target_only_workspace_size(int B, int S, int V) {
+    if (B < 1 || S < 1 || V < 1) return 0;
+    return dsa::target_only_ws_bytes(B, S, V);
+}
+
+int mtp_verify_target_only(const float* target_logits, const int32_t* draft_tokens, int B, int S, int V,
+                           int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream) {
+    if (!target_logits || !draft_tokens || !n_accepted || !next_token)
+        return fail(DSA_ERR_NULL, "target-only verify: NULL pointer argument");
+    if (B < 1 || S < 1 || S > 64 || V < 1)
+        return fail(DSA_ERR_SHAPE, "target-only verify: B=%d S=%d V=%d (1 <= S <= 64)", B, S, V);
+    if ((int64_t)B * (S + 1) * ((V + 8191) / 8192) >= kMaxBlocks)
+        return fail(DSA_ERR_SHAPE, "target-only verify: too large");
+    const size_t need = dsa::target_only_ws_bytes(B, S, V);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(DSA_ERR_WORKSPACE, "target-only verify: workspace %zu bytes given, %zu needed (16-byte aligned)",
+                    ws_bytes, need);
+    return hip_status(dsa::launch_target_only(target_logits, draft_tokens, B, S, V, n_accepted, next_token, ws,
+                                              (hipStream_t)stream),
+                      "mtp_verify_target_only");
+}
+
+int dsa_mtp_commit(const int32_t* n_accepted, const int32_t* q_pos_in, const void* new_k_idx, const void* new_kv,
+                   void* k_idx_cache, int64_t k_bstride, int k_elem_bytes, void* kv_cache, int64_t kv_bstride,
+                   int kv_elem_bytes, int B, int S, int L, int32_t* q_pos_out, void* stream) {
+    if (!n_accepted || !q_pos_in || !new_k_idx || !new_kv || !k_idx_cache || !kv_cache || !q_pos_out)
+        return fail(DSA_ERR_NULL, "commit: NULL pointer argument");
+    if (B < 1 || S < 1 || S > 64 || L < 1) return fail(DSA_ERR_SHAPE, "commit: B=%d S=%d L=%d (1 <= S <= 64)", B, S, L);
+    if ((k_elem_bytes != 1 && k_elem_bytes != 2) || (kv_elem_bytes != 1 && kv_elem_bytes != 2))
+        return fail(DSA_ERR_UNSUPPORTED, "commit: element sizes %d/%d, supported 1 (E4M3) or 2 (bf16)",
+                    k_elem_bytes, kv_elem_bytes);
+    if (B > 1 && (k_bstride < (int64_t)L * DSA_INDEX_DIM || kv_bstride < (int64_t)L * DSA_LATENT_DIM))
+        return fail(DSA_ERR_SHAPE, "commit: batch strides smaller than L rows");
+    if (q_pos_out == q_pos_in) return fail(DSA_ERR_SHAPE, "commit: q_pos_out must not alias q_pos_in");
+    if (!aligned16(new_k_idx) || !aligned16(new_kv) || !aligned16(k_idx_cache) || !aligned16(kv_cache) ||
+        ((k_bstride * k_elem_bytes) % 16) != 0 || ((kv_bstride * kv_elem_bytes) % 16) != 0)
+        return fail(DSA_ERR_ALIGN, "commit: row arrays and caches must be 16-byte aligned, strides in bytes too");
+    return hip_status(dsa::launch_mtp_commit(n_accepted, q_pos_in, new_k_idx, new_kv, k_idx_cache,
+                                             k_bstride * k_elem_bytes, kv_cache, kv_bstride * kv_elem_bytes, B, S, L,
+                                             DSA_INDEX_DIM * k_elem_bytes, DSA_LATENT_DIM * kv_elem_bytes, q_pos_out,
+                                             (hipStream_t)stream),
+                      "dsa_mtp_commit");
+}
+
 }  // extern "C"

@@ -38,6 +38,7 @@ T_U_ACC = 67
 T_U_RES = 68
 T_Q_MTP_IDX = 69
 T_W_MTP = 70
+T_ROUND = 4096       # + 64 * round + field: per-round inputs of the multi-round loop
 
 
 def lib():
@@ -297,13 +298,105 @@ class MtpConfig:
         return uniform_f32(self.seed, T_U_RES, (self.B,))
 
 
+@dataclass(frozen=True)
+class MtpRoundsConfig:
+    """R rounds of draft -> verify -> commit over a cache that starts with L0
+    rows per sequence (first query at position L0-1) and has room for every
+    row the rounds can keep.  Target logits are N(0, 2^2) with one favoured
+    token per position raised by `boost` (so that the target's first choice is
+    the favoured token about 70 % of the time at this vocabulary size); draft
+    logits are rho*target + sqrt(1-rho^2)*N(0, 2^2); draft tokens are drawn
+    from the draft distribution."""
+    name: str
+    seed: int
+    B: int
+    L0: int
+    R: int = 8
+    S: int = 7
+    V: int = 151552
+    k: int = 2048
+    H: int = 32
+    D: int = 128
+    Hq: int = 64
+    Dqk: int = 576
+    Dv: int = 512
+    sm_scale: float = 1.0 / 16.0
+    rho: float = 0.9
+    logit_std: float = 2.0
+    boost: float = 14.8
+
+    @property
+    def L(self) -> int:  # cache capacity: the initial rows plus R*(S+1), in whole 64-row blocks
+        return (self.L0 + self.R * (self.S + 1) + 63) // 64 * 64
+
+    def q_pos0(self) -> np.ndarray:
+        return np.full(self.B, self.L0 - 1, np.int32)
+
+    def k_idx(self) -> np.ndarray:
+        """[B, L, 128]: the first L0 rows of each sequence generated, the rest zero."""
+        out = np.zeros((self.B, self.L, self.D), np.uint16)
+        for b in range(self.B):
+            out[b, : self.L0] = int_bf16(self.seed, T_K_IDX, (self.L0, self.D), start=b * self.L0 * self.D)
+        return out
+
+    def kv_seq(self, b: int) -> np.ndarray:
+        """[L, 576] of sequence b: L0 generated rows, then zeros."""
+        out = np.zeros((self.L, self.Dqk), np.uint16)
+        out[: self.L0] = normal_bf16(self.seed, T_KV, (self.L0, self.Dqk), start=b * self.L0 * self.Dqk)
+        return out
+
+    def _t(self, r: int, field: int) -> int:
+        return T_ROUND + 64 * r + field
+
+    def q_idx(self, r):
+        return int_bf16(self.seed, self._t(r, 0), (self.B, 1, self.H, self.D))
+
+    def w(self, r):
+        return pow2_f32(self.seed, self._t(r, 1), (self.B, 1, self.H))
+
+    def q_steps(self, r):
+        """[B, S, Hq, Dqk]: round r's query of draft step s is q_steps(r)[:, s]."""
+        return normal_bf16(self.seed, self._t(r, 2), (self.B, self.S, self.Hq, self.Dqk))
+
+    def target_logits(self, r):
+        t = normal_f32(self.seed, self._t(r, 3), (self.B, self.S + 1, self.V), scale=self.logit_std)
+        fav = (raw_u64(self.seed, self._t(r, 4), self.B * (self.S + 1)) % np.uint64(self.V)).astype(np.int64)
+        flat = t.reshape(-1, self.V)
+        flat[np.arange(flat.shape[0]), fav] += np.float32(self.boost)
+        return t
+
+    def draft_logits(self, r, target):
+        a = np.float32(self.rho)
+        b = np.float32(math.sqrt(max(0.0, 1.0 - self.rho * self.rho)))
+        return mix_f32(self.seed, self._t(r, 5), np.ascontiguousarray(target[:, : self.S]), float(a), float(b),
+                       self.logit_std)
+
+    def draft_tokens(self, r, draft):
+        return gumbel_argmax(self.seed, self._t(r, 6), draft)
+
+    def u_accept(self, r):
+        return uniform_f32(self.seed, self._t(r, 7), (self.B, self.S))
+
+    def u_resample(self, r):
+        return uniform_f32(self.seed, self._t(r, 8), (self.B,))
+
+    def new_k(self, r):
+        """[B, S+1, 128]: index-key rows of the positions the verifying pass covers."""
+        return int_bf16(self.seed, self._t(r, 9), (self.B, self.S + 1, self.D))
+
+    def new_kv(self, r):
+        return normal_bf16(self.seed, self._t(r, 10), (self.B, self.S + 1, self.Dqk))
+
+
 TINY = GroupConfig("tiny_decode_8k", seed=1, B=1, T=8, L=8192, first_pos=8184)
 DECODE_128K = GroupConfig("decode_128k_b32", seed=2, B=32, T=1, L=131072, first_pos=131071)
 PREFILL = GroupConfig("prefill_4096_at_128k", seed=3, B=1, T=4096, L=131072, first_pos=126976)
 DECODE_1M = GroupConfig("decode_1m_b4", seed=4, B=4, T=1, L=1048576, first_pos=1048575)
 MTP = MtpConfig("mtp_draft_b16_128k", seed=5, B=16, L=131072)
 
-CONFIGS = {c.name: c for c in (TINY, DECODE_128K, PREFILL, DECODE_1M, MTP)}
+MTP_ROUNDS = MtpRoundsConfig("mtp_rounds_b16_128k", seed=6, B=16, L0=131072)
+
+CONFIGS = {c.name: c for c in (TINY, DECODE_128K, PREFILL, DECODE_1M, MTP, MTP_ROUNDS)}
 
 
 def group_bytes_per_query(cfg: GroupConfig, idx_elem: int = 2, kv_elem: int = 2) -> int:

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(dsa):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     lib = dsa.lib()
     for n in names:
         assert hasattr(lib, n), n
