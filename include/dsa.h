@@ -232,7 +232,7 @@ int mtp_draft_verify(const float* target_logits, const float* draft_logits, cons
 size_t mtp_verify_target_only_workspace_size(int B, int S, int V);
 int mtp_verify_target_only(const float* target_logits, const int32_t* draft_tokens, int B, int S, int V,
                            int32_t* n_accepted, int32_t* next_token, void* ws, size_t ws_bytes, void* stream);
-/* dsa_mtp_commit: [SPECYUN, MTP / KV Share]: the draft layers read the
+/* dsa_mtp_commit: [MTPBLOG, "KV Share"]: the draft layers read the
  * backbone's cache and only new tokens get new cache rows.  A round starts
  * with positions 0..q_pos_in[b] cached; the verifying pass has produced the
  * rows of positions q_pos_in[b]+1 .. q_pos_in[b]+S+1 (new_k_idx, new_kv: row j

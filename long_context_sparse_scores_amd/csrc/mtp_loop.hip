@@ -3,9 +3,8 @@
 // [MTPBLOG, "MTP"] and [TEARDOWN, 刀四 MTP] (4sapi.ai GLM-5.2 MTP / IndexShare
 // write-up; clawlihai.cn architecture teardown): generation proceeds in rounds
 // of draft -> verify -> keep the accepted prefix, the next round starting from
-// the verified tokens.  [SPECYUN, MTP / KV Share] (yun88.com speculative
-// decoding report): the draft layers read the backbone's cache and only new
-// tokens get new cache rows.
+// the verified tokens.  [MTPBLOG, "KV Share"]: the draft layers read the
+// backbone's cache and only new tokens get new cache rows.
 //
 //   target-only verification ([MTPBLOG, "Rejection Sampling"]: the rule that
 //   rejection sampling replaced): a draft is kept while it is the target's

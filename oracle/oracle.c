@@ -389,7 +389,7 @@ void oracle_mtp_verify_target_only(const float* target, const int32_t* draft_tok
 }
 
 /* ------------------------------------------------------------------ cache commit after verification
- * [SPECYUN, MTP / KV Share]: the draft layers reuse the backbone's cache and
+ * [MTPBLOG, "KV Share"]: the draft layers reuse the backbone's cache and
  * only newly produced tokens get new cache rows; [MTPBLOG, "MTP"] and
  * [TEARDOWN, 刀四 MTP]: drafts after the first rejection are dropped and the
  * next round starts from the verified tokens.  Reading: a round starts with
