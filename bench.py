@@ -457,14 +457,17 @@ def bench_mtp(cfg, args):
 def bench_mtp_rounds(cfg, args):
     """A step is R chained MTP rounds for B sequences, all on the device: the
     step-1 indexer and top-k over the cache up to each sequence's position, S
-    draft attention steps with that list, verification of the S drafts, and
-    the commit that appends the kept rows and advances the positions (the host
-    reads nothing between rounds).  Every step starts from the same positions;
-    the commit rewrites the same rows, so steps are identical.  The value is
+    draft attention steps with that list (one dsa_layer_group call whose
+    layers are the draft steps), verification of the S drafts, and the commit
+    that appends the kept rows and advances the positions (the host reads
+    nothing between rounds).  Every step starts from the same positions; the
+    commit rewrites the same rows, so steps are identical.  The value is
     verified tokens per second (sum over sequences and rounds of n_accepted+1)
     with rejection sampling; the target-only rule is timed as an A/B."""
     import numpy as np
     import torch
+
+    import ctypes
 
     import long_context_sparse_scores_amd as dsa
     import synth
@@ -499,12 +502,19 @@ def bench_mtp_rounds(cfg, args):
     torch.cuda.synchronize()
     log("bench: inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
 
+    # positions: round 0 reads q_pos0, round r > 0 reads qp[r % 2]; the commit of
+    # round r writes qp[(r + 1) % 2], so no copy resets them between steps
     qp = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
+    pos_in = [q_pos0] + [qp[r % 2] for r in range(1, R)]
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
     outs = [torch.empty((B, 1, cfg.Hq, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(S)]
-    topk_ws = torch.empty(dsa.topk_workspace_size(B, 1, L, k), dtype=torch.uint8, device=dev)
-    attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, 1, k)), dtype=torch.uint8, device=dev)
+    # the draft path of a round is one dsa_layer_group call with the S draft steps as
+    # its layers: indexer and top-k once, S attention launches over the one cache
+    gargs = [dsa.make_group_args(rounds[r]["q_idx"], rounds[r]["w"], k_cache, pos_in[r].view(B, 1), k,
+                                 rounds[r]["q_steps"], [kv_cache] * S, cfg.sm_scale, idx, outs) for r in range(R)]
+    gptr = [ctypes.byref(a) for a in gargs]
+    g_bytes = max(dsa.layer_group_workspace_size(a) for a in gargs)
+    g_ws = torch.empty(g_bytes, dtype=torch.uint8, device=dev)
     ver_ws = torch.empty(max(dsa.verify_workspace_size(B, S, V), dsa.lib().mtp_verify_target_only_workspace_size(B, S, V)),
                          dtype=torch.uint8, device=dev)
     n_acc = torch.empty((R, B), dtype=torch.int32, device=dev)
@@ -514,14 +524,11 @@ def bench_mtp_rounds(cfg, args):
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def run_step(rule):
-        qp[0].copy_(q_pos0)
         for r in range(R):
-            rd, cur, nb = rounds[r], qp[r % 2], qp[(r + 1) % 2]
-            pos2 = cur.view(B, 1)
-            dsa.indexer_scores(rd["q_idx"], rd["w"], k_cache, pos2, scores=scores)
-            dsa.topk(scores, pos2, k, idx=idx, ws=topk_ws)
-            for s in range(S):
-                dsa.sparse_mla_attn(rd["q_steps"][s], kv_cache, idx, cfg.sm_scale, out=outs[s], ws=attn_ws)
+            rd = rounds[r]
+            rc = lib.dsa_layer_group(gptr[r], g_ws.data_ptr(), g_bytes, stream)
+            if rc != 0:
+                raise RuntimeError(dsa.last_error())
             if rule == "rejection":
                 rc = lib.mtp_draft_verify(rd["target"].data_ptr(), rd["draft"].data_ptr(), rd["tok"].data_ptr(),
                                           rd["u"].data_ptr(), rd["ur"].data_ptr(), B, S, V, min_sum.data_ptr(),
@@ -533,7 +540,8 @@ def bench_mtp_rounds(cfg, args):
                                                 ver_ws.numel(), stream)
             if rc != 0:
                 raise RuntimeError(dsa.last_error())
-            dsa.mtp_commit(n_acc[r], cur, rd["new_k"], rd["new_kv"], k_cache, kv_cache, q_pos_out=nb)
+            dsa.mtp_commit(n_acc[r], pos_in[r], rd["new_k"], rd["new_kv"], k_cache, kv_cache,
+                           q_pos_out=qp[(r + 1) % 2])
 
     def timed(rule, steps):
         for _ in range(args.warmup):
@@ -560,10 +568,10 @@ def bench_mtp_rounds(cfg, args):
             % (rule, ms, R, tokens, tokens / (B * R)))
     # the index-key scan of one round, timed alone (the roofline figure)
     rd0 = rounds[0]
-    qp[0].copy_(q_pos0)
+    scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
 
     def indexer_step():
-        dsa.indexer_scores(rd0["q_idx"], rd0["w"], k_cache, qp[0].view(B, 1), scores=scores)
+        dsa.indexer_scores(rd0["q_idx"], rd0["w"], k_cache, q_pos0.view(B, 1), scores=scores)
 
     for _ in range(args.warmup):
         indexer_step()

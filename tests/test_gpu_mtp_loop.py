@@ -118,24 +118,31 @@ def _oracle_rounds(cfg, rd, k_cache, kv_cache, q_pos, rule):
     return res, q_pos
 
 
-@pytest.mark.parametrize("rule", ["rejection", "target_only"])
-def test_rounds_chained_on_device_match_oracle(dsa, rule):
+@pytest.mark.parametrize("rule,entry", [("rejection", "separate"), ("target_only", "separate"),
+                                        ("rejection", "group")])
+def test_rounds_chained_on_device_match_oracle(dsa, rule, entry):
+    # entry "group": the draft path of a round is one dsa_layer_group call whose
+    # layers are the draft steps (all over the one latent cache), as bench.py runs it
     B, R, S, V, L = 3, 4, 7, 3000, 6144
     cfg = synth.GroupConfig("rounds", seed=12, B=B, T=1, L=L, first_pos=0, k=256)
     rd = Rounds(77, B, R, S, V)
     rd.clear_margins(np.random.default_rng(1))
     q_pos0 = np.array([4000, 5200, 3000], np.int32)
     k_cache, kv_cache = cfg.k_idx().copy(), cfg.kv(0).copy()
-    say("rounds %s: GPU" % rule)
+    say("rounds %s via %s entry points: GPU" % (rule, entry))
     dk, dkv = bf16_dev(k_cache), bf16_dev(kv_cache)
     qp = [i32_dev(q_pos0), torch.empty(B, dtype=torch.int32, device=DEV)]
     gpu = []
     for r in range(R):
         cur, nxt_buf = qp[r % 2], qp[(r + 1) % 2]
         pos2 = cur.view(B, 1)
-        scores = dsa.indexer_scores(bf16_dev(rd.q_idx[r]), f32_dev(rd.w[r]), dk, pos2)
-        idx = dsa.topk(scores, pos2, cfg.k)
-        outs = [dsa.sparse_mla_attn(bf16_dev(q), dkv, idx, cfg.sm_scale) for q in rd.q_steps[r]]
+        if entry == "group":
+            idx, outs, _ = dsa.layer_group(bf16_dev(rd.q_idx[r]), f32_dev(rd.w[r]), dk, pos2, cfg.k,
+                                           [bf16_dev(q) for q in rd.q_steps[r]], [dkv] * S, cfg.sm_scale)
+        else:
+            scores = dsa.indexer_scores(bf16_dev(rd.q_idx[r]), f32_dev(rd.w[r]), dk, pos2)
+            idx = dsa.topk(scores, pos2, cfg.k)
+            outs = [dsa.sparse_mla_attn(bf16_dev(q), dkv, idx, cfg.sm_scale) for q in rd.q_steps[r]]
         if rule == "rejection":
             _, n_acc, nt = dsa.mtp_draft_verify(f32_dev(rd.target[r]), f32_dev(rd.draft[r]), i32_dev(rd.tok[r]),
                                                 f32_dev(rd.u[r]), f32_dev(rd.ur[r]))

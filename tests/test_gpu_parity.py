@@ -115,6 +115,42 @@ def test_topk_short_rows(dsa):
     _topk_case(dsa, s, pos, 2048)
 
 
+def test_topk_candidate_overflow(dsa):
+    # a row's candidate list (keys sharing the threshold's top digit) holds
+    # max(4096, L/8) entries; fully tied rows overflow it and are resolved
+    # from the whole row instead
+    rng = np.random.default_rng(13)
+    B, T, L = 1, 4, 40000
+    say("topk candidate overflow")
+    s = rng.standard_normal((B, T, L)).astype(np.float32)
+    s[0, 0] = 2.0                                                          # 40000 tied candidates
+    s[0, 1] = np.where(rng.random(L) < 0.5, 1.0, 1.25).astype(np.float32)  # two values
+    s[0, 2, ::2] = -0.0
+    pos = np.array([[L - 1, L - 1, 30000, 20000]], np.int32)
+    _topk_case(dsa, s, pos, 2048)
+
+
+@pytest.mark.parametrize("L", [262144, 262145])
+def test_topk_long_rows(dsa, L):
+    rng = np.random.default_rng(L)
+    say("topk L=%d" % L)
+    s = (rng.integers(0, 64, size=(1, 2, L)) / 8).astype(np.float32)
+    pos = np.array([[L - 1, 100000]], np.int32)
+    _topk_case(dsa, s, pos, 2048)
+
+
+def test_topk_many_rows(dsa):
+    # 600 rows of ragged visible lengths, tied rows overflowing the candidate list
+    rng = np.random.default_rng(14)
+    B, T, L = 1, 600, 5000
+    say("topk %d rows" % (B * T))
+    s = (rng.integers(0, 16, size=(B, T, L)) / 4).astype(np.float32)
+    s[0, ::7] = 3.0
+    pos = (np.arange(T, dtype=np.int32) * 37 % L)[None]
+    pos[0, :5] = L - 1
+    _topk_case(dsa, s, pos, 1000)
+
+
 # ------------------------------------------------------------------ attention
 def test_attn_tiny_layers(dsa):
     cfg = synth.TINY
