@@ -24,13 +24,11 @@
 // one block per (query, head), merges them in split order.  A query whose
 // list fits one split is normalised and written directly.
 //
-// FP8 latent cache ([CTXFR, "Entraînement par renforcement de l'agent
-// intelligent"] names an FP8 KV cache): rows of 576 OCP E4M3 codes are
-// gathered into a ring of E4M3 staging tiles (18 KiB per 32 rows) and each
-// tile is converted once, exactly (every E4M3 value is a bf16 value), into the
-// bf16 tile layout above; the matrix-core code is the bf16 one.  Two bf16
-// tiles alternate (P.V of tile t and Q.K^T of tile t+1), and tile t+2 is
-// converted into the buffer of tile t once its P.V is done.
+// E4M3 latent rows ([CTXFR, "Entraînement par renforcement de l'agent
+// intelligent"] names an FP8 KV cache) take a kernel of their own below: with
+// 576-byte rows the LDS holds a ring of seven 18 KiB tiles, twice the rows in
+// flight, and every operand is widened exactly to bf16 in registers as it is
+// read, so the matrix cores compute as in the bf16 kernel.
 #include "common.h"
 
 namespace dsa {
@@ -49,15 +47,10 @@ constexpr int kLoads = 9;                         // direct-to-LDS loads per wav
 // row lists of up to 1024 entries.  Whole lists (a query per workgroup, prefill
 // sized batches): 3 buffers and up to 2048 entries; that path is bound by the
 // matrix work, not by how many gathers are in flight.
-template <bool DIRECT, bool FP8 = false> struct Cfg {
-    static constexpr int kStages = FP8 ? 2 : (DIRECT ? 3 : 4);   // bf16 tile buffers
-    static constexpr int kStages8 = FP8 ? (DIRECT ? 3 : 4) : 0;  // E4M3 staging tiles
+template <bool DIRECT> struct Cfg {
+    static constexpr int kStages = DIRECT ? 3 : 4;
     static constexpr int kMaxRows = DIRECT ? 2048 : 1024;
 };
-constexpr int kRow8 = kDqk;                        // bytes per E4M3 latent row
-constexpr int kChunks8 = kRow8 / 16;              // 36 16-byte chunks per E4M3 row
-constexpr int kTile8Bytes = kRows * kRow8;        // 18 KiB per E4M3 tile
-constexpr int kLoads8Max = 5;                     // 18 wave loads of 1 KiB per tile: 5, 5, 4, 4 over the waves
 constexpr int kMaxSplitRows = Cfg<false>::kMaxRows;
 constexpr int kMaxSplits = 2048 / kRows;          // k <= 2048
 constexpr int kTargetBlocks = 256;                // one resident block per CU
@@ -144,86 +137,12 @@ __device__ __forceinline__ GatherPlan plan_gather(const uint16_t* __restrict__ k
 }
 
 // Load i of the plan: i < 8 the main part of row 8w+i, i == 8 the tails.
-__device__ __forceinline__ void issue_gather(const GatherPlan& gp, const void* kv_base, int i, int lane) {
+__device__ __forceinline__ void issue_gather(const GatherPlan& gp, const uint16_t* kvb, int i, int lane) {
     if (!gp.active) return;
-    const uint16_t* kvb = reinterpret_cast<const uint16_t*>(kv_base);
     if (i < 8)
         lds_dma16_sbase(gp.row[i], (uint32_t)((lane ^ (gp.xr + i)) << 4), gp.lds[i]);
     else
         lds_dma16(kvb + gp.tail_off, gp.lds_tail);
-}
-
-// Gather of E4M3 tile t into a staging tile: the tile's 1152 16-byte chunks
-// (chunk c8 of row r at byte 576r + 16c8) are filled by 18 wave loads of 1 KiB,
-// load n covering chunks 64n .. 64n+63; wave w issues loads w, w+4, w+8, w+12
-// (and w+16 for waves 0 and 1).  Every lane has its own row, so each load takes
-// a per-lane offset from the sequence's base.
-struct GatherPlan8 {
-    const uint8_t* base;         // wave-uniform: the sequence's first row
-    uint32_t off[kLoads8Max];    // this lane's byte offsets
-    uint32_t lds[kLoads8Max];    // wave-uniform LDS byte address of each load
-    int nload;                   // wave-uniform: 5 or 4
-    bool active;
-};
-
-__device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ kvb, const int* __restrict__ rows_lds,
-                                                    int t, int nrows, int L, const uint8_t* stage, int wave,
-                                                    int lane) {
-    GatherPlan8 gp;
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(stage));
-    gp.base = kvb;
-    gp.nload = wave < 2 ? 5 : 4;
-#pragma unroll
-    for (int i = 0; i < kLoads8Max; ++i) {
-        const int n = wave + 4 * i;                  // < 18 for the loads this wave issues
-        const int ch = 64 * n + lane;
-        const int r = min(ch / kChunks8, kRows - 1);  // (clamped for the unused fifth slot of waves 2, 3)
-        const int j = t * kRows + r;
-        int rid = j < nrows ? rows_lds[j] : 0;
-        rid = (rid >= 0 && rid < L) ? rid : 0;       // masked or missing rows read row 0
-        gp.off[i] = (uint32_t)rid * kRow8 + 16u * (uint32_t)(ch - kChunks8 * r);  // L <= 2^22 rows: fits
-        gp.lds[i] = __builtin_amdgcn_readfirstlane(base + 1024u * n);
-    }
-    gp.active = true;
-    return gp;
-}
-
-__device__ __forceinline__ void issue_gather(const GatherPlan8& gp, const void*, int i, int lane) {
-    if (!gp.active || i >= gp.nload) return;
-    lds_dma16_sbase(gp.base, gp.off[i], gp.lds[i]);
-}
-
-// 8 E4M3 codes -> 8 bf16, exactly: v_cvt_pk_f32_fp8 widens two codes to fp32,
-// whose upper halves are the bf16 values (an E4M3 value has at most 4
-// significant bits and its exponent lies within bf16's range).
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint2 v) {
-    typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-    const f32x2v_t a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);
-    const f32x2v_t b = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, true);
-    const f32x2v_t c = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, false);
-    const f32x2v_t d = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
-    u32x4_t r;
-    r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-    r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-    r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-    r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
-    return r;
-}
-
-// A staged E4M3 tile -> the bf16 tile layout (main part and tail of each row).
-// Thread i converts the 8-value chunks x = i + 256m (m < 9): row x / 72,
-// chunk x % 72.
-__device__ __forceinline__ void convert_tile(const uint8_t* stage, uint16_t* tile, int tid) {
-    char* dst_tile = reinterpret_cast<char*>(tile);
-#pragma unroll
-    for (int m = 0; m < kTileChunks / kThreads; ++m) {
-        const int x = tid + kThreads * m;
-        const int r = x / kChunks;
-        const int c = x - kChunks * r;
-        const uint2 v = *reinterpret_cast<const uint2*>(stage + kRow8 * r + 8 * c);
-        const int off = c < 64 ? r * 1024 + 16 * (c ^ (r & 15)) : kMainBytes + r * 128 + 16 * ((c - 64) ^ (r & 7));
-        *reinterpret_cast<u32x4_t*>(dst_tile + off) = e4m3x8_to_bf16x8(v);
-    }
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -237,22 +156,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most `tiles` E4M3 tile gathers of this wave (nload loads each,
-// 5 or 4; both wave-uniform) are still in flight.
-__device__ __forceinline__ void wait_tiles8(int tiles, int nload) {
-    if (nload == 5) {
-        if (tiles <= 0) wait_vmem<0>();
-        else if (tiles == 1) wait_vmem<5>();
-        else if (tiles == 2) wait_vmem<10>();
-        else wait_vmem<15>();
-    } else {
-        if (tiles <= 0) wait_vmem<0>();
-        else if (tiles == 1) wait_vmem<4>();
-        else if (tiles == 2) wait_vmem<8>();
-        else wait_vmem<12>();
-    }
 }
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
@@ -402,11 +305,11 @@ __device__ __forceinline__ void apply_rescale(const uint16_t* tv, int c, PvAcc& 
 // its pair) fused with P.V of tile `tv` (this wave's 128 value dims, all four
 // head blocks): two independent instruction streams, alternated in chunks.
 // When `gp` is active its nine loads are issued between matrix instructions.
-template <bool PV, bool QK, class Plan>
+template <bool PV, bool QK>
 __device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad,
                                       const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
-                                      int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const Plan& gp,
-                                      const void* kvb) {
+                                      int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const GatherPlan& gp,
+                                      const uint16_t* kvb) {
     bf16x8_t pbv[4];
     if (PV) {
 #pragma unroll
@@ -478,187 +381,16 @@ __device__ __forceinline__ void own_scores(const f32x4_t (&sp)[2][2], const f32x
     for (int rb = 0; rb < 2; ++rb) s[rb] = (kk ? sp[rb][1] : sp[rb][0]) + sx[(wave * 2 + rb) * kWave + lane];
 }
 
-// One workgroup (one wave per SIMD) fills a CU's LDS, so the scheduler may use
-// every register to run operand loads ahead.
-template <bool DIRECT, bool FP8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const void* __restrict__ kv, int64_t kv_bstride,
-    const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    // Blocks are numbered so that every split of query bt lands on XCD bt % 8
-    // (consecutive block ids go to consecutive XCDs): the splits' partials and
-    // the combine that reads them share one L2.
-    const int grp = blockIdx.x / (kXcds * nsplit);
-    const int rem = blockIdx.x % (kXcds * nsplit);
-    const int split = rem / kXcds;
-    const int bt = grp * kXcds + rem % kXcds;
-    if (bt >= rows) return;
-    const int b = bt / T;
-    const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps role selects scalar
-    const int kk = wave & 1;   // contraction half for Q.K^T
-    const int hh = wave >> 1;  // head pair for Q.K^T
+// Epilogue of both kernels: denominators (and reference maxima) of all 64
+// heads from their owner waves, then the normalised output of this split (or
+// of the whole list) and its log-sum-exp.
+template <bool DIRECT>
+__device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxState& st, f32x4_t* sx, int wave,
+                                             int lane, int bt, int split, int nsplit, uint16_t* __restrict__ part_o,
+                                             float* __restrict__ part_lse, uint16_t* __restrict__ out,
+                                             float* __restrict__ lse) {
     const int c = lane & 15;
     const int g = lane >> 4;
-    const int j0 = split * rows_per_split;
-    const int nrows = min(k, j0 + rows_per_split) - j0;
-    const int ntiles = (nrows + kRows - 1) / kRows;
-
-    constexpr int kStages = Cfg<DIRECT, FP8>::kStages;
-    constexpr int kStages8 = Cfg<DIRECT, FP8>::kStages8;
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
-    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
-    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
-    __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
-    uint8_t* stage8 = nullptr;  // E4M3 staging ring (FP8 only)
-    if constexpr (FP8) {
-        __shared__ __attribute__((aligned(16))) uint8_t stage8_lds[kStages8 * kTile8Bytes];
-        stage8 = stage8_lds;
-    }
-
-    // B operands of S^T: q[head 16*(2hh+h) + c][32*(9kk+kl) + 8g .. +7], loaded
-    // while the row list is fetched so that the two latencies overlap.
-    bf16x8_t qb[2][9];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
-    }
-    const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
-    // Consume q here so the compiler's own wait for these loads (it cannot see the
-    // gathers, which are issued from asm) stays ahead of the first gather.
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
-    __syncthreads();  // rows_lds ready
-
-    // kv_bstride counts elements: bf16 values, or bytes for E4M3 rows
-    const uint16_t* kvb = reinterpret_cast<const uint16_t*>(kv) + (FP8 ? 0 : (int64_t)b * kv_bstride);
-    const uint8_t* kvb8 = reinterpret_cast<const uint8_t*>(kv) + (FP8 ? (int64_t)b * kv_bstride : 0);
-    const void* kv_seq = FP8 ? static_cast<const void*>(kvb8) : static_cast<const void*>(kvb);
-    const TileAddr ad = tile_addr(lane);
-    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
-    auto stage = [&](int t) { return stage8 + (t % (FP8 ? kStages8 : 1)) * kTile8Bytes; };
-    if constexpr (FP8) {
-        for (int t = 0; t < kStages8 && t < ntiles; ++t) {
-            const GatherPlan8 gp = plan_gather8(kvb8, rows_lds, t, nrows, L, stage(t), wave, lane);
-#pragma unroll
-            for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, kvb8, i, lane);
-        }
-    } else {
-        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
-            const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
-        }
-    }
-
-    PvAcc acc;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState st;
-    st.m_ref = -INFINITY;
-    st.lsum = 0.0f;
-    GatherPlan no_gather;
-    no_gather.active = false;
-
-    // softmax of tile t from the exchanged partials, P^T and rescale record to LDS
-    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
-        f32x4_t s[2];
-        own_scores(sp, sx, wave, kk, lane, s);
-        float factor;
-        bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
-        pl[wave * kWave + lane] = pb;
-        char* tail = reinterpret_cast<char*>(buf(t));
-        if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * wave + c] = factor;
-        if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[wave] = moved ? 1u : 0u;
-    };
-
-    if constexpr (FP8) {
-        // Tiles 0 and 1: wait for their gathers, convert both, issue the gather of
-        // tile kStages8 into the staging tile tile 0 has left; then tile 0's
-        // Q.K^T, exchange and softmax.
-        const int nload = wave < 2 ? 5 : 4;
-        wait_tiles8(max(0, min(ntiles - 1, kStages8 - 1) - 1), nload);
-        lds_barrier();
-        convert_tile(stage(0), buf(0), threadIdx.x);
-        if (ntiles > 1) convert_tile(stage(1), buf(1), threadIdx.x);
-        lds_barrier();
-        if (kStages8 < ntiles) {
-            const GatherPlan8 gp = plan_gather8(kvb8, rows_lds, kStages8, nrows, L, stage(kStages8), wave, lane);
-#pragma unroll
-            for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, kvb8, i, lane);
-        }
-        f32x4_t sp[2][2];
-        pv_qk<false, true>(buf(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kv_seq);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();
-        finish_scores(0, sp);
-        // Iteration t: P.V of tile t and Q.K^T of tile t+1 (both converted), with the
-        // gather of tile t+kStages8+1 into the staging tile tile t+1 has left; then
-        // the exchange, the softmax of tile t+1 and the conversion of tile t+2 into
-        // the buffer of tile t.
-        for (int t = 0; t + 1 < ntiles; ++t) {
-            lds_barrier();  // tile t+1 converted; P^T of tile t visible; staging tile of t+1 free
-            const int u = t + kStages8 + 1;
-            GatherPlan8 gp = plan_gather8(kvb8, rows_lds, min(u, ntiles - 1), nrows, L, stage(u), wave, lane);
-            gp.active = u < ntiles;
-            pv_qk<true, true>(buf(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp, kv_seq);
-            send_partial(sp, sx, wave, kk, lane);
-            if (t + 2 < ntiles) wait_tiles8(min(ntiles - 1, u) - (t + 2), nload);
-            lds_barrier();  // partials exchanged; P.V of tile t done; gathers of tile t+2 landed
-            finish_scores(t + 1, sp);
-            if (t + 2 < ntiles) convert_tile(stage(t + 2), buf(t + 2), threadIdx.x);
-        }
-    } else {
-    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
-    {
-        const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
-        if (later >= 2) wait_vmem<2 * kLoads>();
-        else if (later == 1) wait_vmem<kLoads>();
-        else wait_vmem<0>();
-        static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
-    }
-    lds_barrier();
-    {
-        f32x4_t sp[2][2];
-        pv_qk<false, true>(buf(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kv_seq);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();
-        finish_scores(0, sp);
-    }
-    // Iteration t: P.V of tile t alongside Q.K^T of tile t+1 (and the gather of
-    // tile t+3), then the exchange and softmax of tile t+1.
-    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
-        const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
-        if (later >= 1) wait_vmem<kLoads>();
-        else wait_vmem<0>();
-        lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer (t+3) % 4 free
-        GatherPlan gp = plan_gather(kvb, rows_lds, min(t + kStages - 1, ntiles - 1), nrows, L, buf(t + kStages - 1),
-                                    wave, lane);
-        gp.active = t + kStages - 1 < ntiles;
-        f32x4_t sp[2][2];
-        pv_qk<true, true>(buf(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp, kv_seq);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();  // partials exchanged; every wave is done reading P^T of tile t
-        finish_scores(t + 1, sp);
-    }
-    }
-    lds_barrier();  // P^T and rescale record of the last tile visible
-    {
-        f32x4_t sp[2][2];
-        pv_qk<true, false>(buf(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kv_seq);
-    }
-
-    // Denominators (and reference maxima) of all 64 heads, from their owner waves.
     float lsum = st.lsum;
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
@@ -692,6 +424,445 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     // Normalised partial output (bf16) and its log2-sum-exp; an empty split has lse -inf.
     if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
+}
+
+// One workgroup (one wave per SIMD) fills a CU's LDS, so the scheduler may use
+// every register to run operand loads ahead.
+template <bool DIRECT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_mla_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t kv_bstride,
+    const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    // Blocks are numbered so that every split of query bt lands on XCD bt % 8
+    // (consecutive block ids go to consecutive XCDs): the splits' partials and
+    // the combine that reads them share one L2.
+    const int grp = blockIdx.x / (kXcds * nsplit);
+    const int rem = blockIdx.x % (kXcds * nsplit);
+    const int split = rem / kXcds;
+    const int bt = grp * kXcds + rem % kXcds;
+    if (bt >= rows) return;
+    const int b = bt / T;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps role selects scalar
+    const int kk = wave & 1;   // contraction half for Q.K^T
+    const int hh = wave >> 1;  // head pair for Q.K^T
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int j0 = split * rows_per_split;
+    const int nrows = min(k, j0 + rows_per_split) - j0;
+    const int ntiles = (nrows + kRows - 1) / kRows;
+
+    constexpr int kStages = Cfg<DIRECT>::kStages;
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
+    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
+    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
+    __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
+
+    // B operands of S^T: q[head 16*(2hh+h) + c][32*(9kk+kl) + 8g .. +7], loaded
+    // while the row list is fetched so that the two latencies overlap.
+    bf16x8_t qb[2][9];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+    }
+    const int32_t* sel = idx + (int64_t)bt * k + j0;
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
+    // Consume q here so the compiler's own wait for these loads (it cannot see the
+    // gathers, which are issued from asm) stays ahead of the first gather.
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
+    __syncthreads();  // rows_lds ready
+
+    const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
+    const TileAddr ad = tile_addr(lane);
+    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
+    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
+        const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
+    }
+
+    PvAcc acc;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st;
+    st.m_ref = -INFINITY;
+    st.lsum = 0.0f;
+    GatherPlan no_gather;
+    no_gather.active = false;
+
+    // softmax of tile t from the exchanged partials, P^T and rescale record to LDS
+    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
+        f32x4_t s[2];
+        own_scores(sp, sx, wave, kk, lane, s);
+        float factor;
+        bool moved;
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
+        pl[wave * kWave + lane] = pb;
+        char* tail = reinterpret_cast<char*>(buf(t));
+        if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * wave + c] = factor;
+        if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[wave] = moved ? 1u : 0u;
+    };
+
+    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
+    {
+        const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
+        if (later >= 2) wait_vmem<2 * kLoads>();
+        else if (later == 1) wait_vmem<kLoads>();
+        else wait_vmem<0>();
+        static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
+    }
+    lds_barrier();
+    {
+        f32x4_t sp[2][2];
+        pv_qk<false, true>(buf(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();
+        finish_scores(0, sp);
+    }
+    // Iteration t: P.V of tile t alongside Q.K^T of tile t+1 (and the gather of
+    // tile t+3), then the exchange and softmax of tile t+1.
+    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
+    for (int t = 0; t + 1 < ntiles; ++t) {
+        // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
+        const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
+        if (later >= 1) wait_vmem<kLoads>();
+        else wait_vmem<0>();
+        lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer (t+3) % 4 free
+        GatherPlan gp = plan_gather(kvb, rows_lds, min(t + kStages - 1, ntiles - 1), nrows, L, buf(t + kStages - 1),
+                                    wave, lane);
+        gp.active = t + kStages - 1 < ntiles;
+        f32x4_t sp[2][2];
+        pv_qk<true, true>(buf(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp, kvb);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();  // partials exchanged; every wave is done reading P^T of tile t
+        finish_scores(t + 1, sp);
+    }
+    lds_barrier();  // P^T and rescale record of the last tile visible
+    {
+        f32x4_t sp[2][2];
+        pv_qk<true, false>(buf(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
+    }
+
+    store_output<DIRECT>(acc, st, sx, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
+}
+
+// ------------------------------------------------------------------ E4M3 latent rows
+// A 32-row tile of 576-byte E4M3 rows is 18 KiB, so the LDS holds a ring of
+// seven: six tiles in flight while one is read, twice the rows in flight of
+// the bf16 kernel (whose gathers are limited by rows in flight, not bytes).
+// The work split, softmax and combine are the bf16 kernel's; only the operand
+// reads differ, each widened exactly to bf16 in registers (v_cvt_pk_f32_fp8;
+// the upper halves of the fp32 results are the bf16 values):
+//   Q.K^T  A operand, 8 dims of a row: one ds_read_b64;
+//   P.V    A operand, 8 rows of one dim: one ds_read_b64_tr_b8 (in each
+//          16-lane group, lane 8q + r receives byte r of the 8-byte chunks
+//          addressed by lanes 2j + q, as value j = 0..7), with the rows in the
+//          order of the P^T k-slots.
+// Chunk s (16 bytes) of row r sits at byte 16 * (36r + (s ^ f(r))),
+// f(r) = ((r >> 2) + 2(r >> 4)) & 3: both reads touch every LDS bank once per
+// 32-lane phase (checked by enumeration).  A tile's rescale record lives in a
+// small array beside the ring.
+constexpr int kRow8 = kDqk;                       // bytes per E4M3 row
+constexpr int kChunks8 = kRow8 / 16;              // 36
+constexpr int kTile8Bytes = kRows * kRow8;        // 18 KiB
+constexpr int kStages8 = 7;
+constexpr int kLoads8Max = 5;                     // 18 wave loads of 1 KiB per tile: 5, 5, 4, 4 over the waves
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 2) + 2 * (r >> 4)) & 3; }
+
+// Gather of E4M3 tile t: load n (wave n % 4) fills slots 64n .. 64n+63 of the
+// tile (1 KiB); the lane writing slot P fetches the chunk stored there.
+struct GatherPlan8 {
+    const uint8_t* base;       // wave-uniform: the sequence's first row
+    uint32_t off[kLoads8Max];  // this lane's byte offsets from base
+    uint32_t lds[kLoads8Max];  // wave-uniform LDS byte address of each load
+    int nload;                 // wave-uniform: 5 or 4
+    bool active;
+};
+
+__device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ kvb, const int* __restrict__ rows_lds,
+                                                    int t, int nrows, int L, const uint8_t* tile, int wave,
+                                                    int lane) {
+    GatherPlan8 gp;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
+    gp.base = kvb;
+    gp.nload = wave < 2 ? 5 : 4;
+#pragma unroll
+    for (int i = 0; i < kLoads8Max; ++i) {
+        const int n = wave + 4 * i;                 // < 18 for the loads this wave issues
+        const int slot = 64 * n + lane;
+        const int r = min(slot / kChunks8, kRows - 1);
+        const int j = t * kRows + r;
+        int rid = j < nrows ? rows_lds[j] : 0;
+        rid = (rid >= 0 && rid < L) ? rid : 0;      // masked or missing rows read row 0 (finite values, P = 0)
+        const int s = (slot - kChunks8 * r) ^ swz8(r);
+        gp.off[i] = slot < kRows * kChunks8 ? (uint32_t)rid * kRow8 + 16u * (uint32_t)s : 0u;  // L <= 2^22 rows
+        gp.lds[i] = __builtin_amdgcn_readfirstlane(base + 1024u * n);
+    }
+    gp.active = true;
+    return gp;
+}
+
+__device__ __forceinline__ void issue_gather(const GatherPlan8& gp, const void*, int i, int) {
+    if (!gp.active || i >= gp.nload) return;
+    lds_dma16_sbase(gp.base, gp.off[i], gp.lds[i]);
+}
+
+// Wait until at most `tiles` (0..5) E4M3 tile gathers of this wave, of nload
+// loads each (5 or 4; both wave-uniform), are still in flight.
+__device__ __forceinline__ void wait_tiles8(int tiles, int nload) {
+    if (nload == 5) {
+        if (tiles <= 0) wait_vmem<0>();
+        else if (tiles == 1) wait_vmem<5>();
+        else if (tiles == 2) wait_vmem<10>();
+        else if (tiles == 3) wait_vmem<15>();
+        else if (tiles == 4) wait_vmem<20>();
+        else wait_vmem<25>();
+    } else {
+        if (tiles <= 0) wait_vmem<0>();
+        else if (tiles == 1) wait_vmem<4>();
+        else if (tiles == 2) wait_vmem<8>();
+        else if (tiles == 3) wait_vmem<12>();
+        else if (tiles == 4) wait_vmem<16>();
+        else wait_vmem<20>();
+    }
+}
+
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (low byte first) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    const f32x2v_t a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const f32x2v_t b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const f32x2v_t c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2v_t d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    u32x4_t r;
+    r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+    r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+    r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Per-lane parts of the operand addresses (bytes within a tile).
+struct TileAddr8 {
+    int qk;    // 576c + 8(g & 1): rows c and c + 16, half g & 1 of their chunks
+    int fq0;   // swz8(c), swz8(c + 16)
+    int fq1;
+    int pv;    // 576 r + 8 (m & 1) for the P.V row r of this lane
+    int fpv;   // swz8(r)
+};
+
+__device__ __forceinline__ TileAddr8 tile_addr8(int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    TileAddr8 a;
+    a.qk = kRow8 * c + 8 * (g & 1);
+    a.fq0 = swz8(c);
+    a.fq1 = swz8(c + 16);
+    // lane m of group g addresses k-slot j = m >> 1 of the P^T ordering:
+    // row 4g + j for j < 4, row 16 + 4g + j - 4 otherwise; half m & 1
+    const int m = lane & 15, j = m >> 1;
+    const int r = j < 4 ? 4 * g + j : 16 + 4 * g + j - 4;
+    a.pv = kRow8 * r + 8 * (m & 1);
+    a.fpv = swz8(r);
+    return a;
+}
+
+struct Rescale8 {
+    float fac[4 * 16];  // per head block, per head
+    uint32_t flag[4];   // block hb moved its reference
+};
+
+__device__ __forceinline__ void apply_rescale8(const Rescale8& rs, int c, PvAcc& acc) {
+    const u32x4_t fl = *reinterpret_cast<const u32x4_t*>(rs.flag);
+    const uint32_t any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+    if (any) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            if (__builtin_amdgcn_readfirstlane(fl[hb])) {
+                const float f = rs.fac[16 * hb + c];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    acc.o[d][hb] *= f;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+}
+
+// As pv_qk, reading E4M3 tiles: P.V of tile `tv` (record `rv`) and Q.K^T of tile `tq`.
+template <bool PV, bool QK>
+__device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, const uint8_t* tq, const TileAddr8& ad,
+                                       const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
+                                       int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const GatherPlan8& gp) {
+    const int g = lane >> 4;
+    bf16x8_t pbv[4];
+    if (PV) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
+        apply_rescale8(rv, lane & 15, acc);
+    }
+    if (QK) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+        if (PV) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int d = 2 * ch + i;  // value dims 128 wave + 16 d .. +15: chunk 8 wave + d
+                const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2_t*)(tv + ad.pv + 16 * ((8 * wave + d) ^ ad.fpv)));
+                const bf16x8_t a = e4m3x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+                if (i == 0) issue_gather(gp, nullptr, 2 * ch, lane);
+            }
+        }
+        if (QK) {
+            const int k0 = 2 * ch;
+            const int k1 = ch == 3 ? 9 : 2 * ch + 2;
+#pragma unroll
+            for (int kl = k0; kl < k1; ++kl) {
+                const int s = 18 * kk + 2 * kl + (g >> 1);  // chunk of dims 32(9kk + kl) + 8g .. +7
+                const uint2 r0 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * (s ^ ad.fq0));
+                const uint2 r1 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * kRow8 + 16 * (s ^ ad.fq1));
+                const bf16x8_t a0 = e4m3x8_to_bf16x8(r0.x, r0.y);
+                const bf16x8_t a1 = e4m3x8_to_bf16x8(r1.x, r1.y);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
+                    sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
+                }
+                if (kl == k0) issue_gather(gp, nullptr, 2 * ch + 1, lane);
+            }
+        } else if (!PV) {
+            issue_gather(gp, nullptr, 2 * ch, lane);
+            issue_gather(gp, nullptr, 2 * ch + 1, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool DIRECT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_mla_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, int64_t kv_bstride,
+    const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int grp = blockIdx.x / (kXcds * nsplit);
+    const int rem = blockIdx.x % (kXcds * nsplit);
+    const int split = rem / kXcds;
+    const int bt = grp * kXcds + rem % kXcds;
+    if (bt >= rows) return;
+    const int b = bt / T;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kk = wave & 1;
+    const int hh = wave >> 1;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int j0 = split * rows_per_split;
+    const int nrows = min(k, j0 + rows_per_split) - j0;
+    const int ntiles = (nrows + kRows - 1) / kRows;
+    const int nload = wave < 2 ? 5 : 4;
+
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[kStages8 * kTile8Bytes];
+    __shared__ __attribute__((aligned(16))) Rescale8 rescale[kStages8];
+    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];
+    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];
+    __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
+
+    bf16x8_t qb[2][9];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+    }
+    const int32_t* sel = idx + (int64_t)bt * k + j0;
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
+    __syncthreads();  // rows_lds ready
+
+    const uint8_t* kvb = kv + (int64_t)b * kv_bstride;  // kv_bstride counts bytes
+    const TileAddr8 ad = tile_addr8(lane);
+    auto buf = [&](int t) { return tiles + (t % kStages8) * kTile8Bytes; };
+    auto rec = [&](int t) -> Rescale8& { return rescale[t % kStages8]; };
+    for (int t = 0; t < kStages8 - 1 && t < ntiles; ++t) {
+        const GatherPlan8 gp = plan_gather8(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
+#pragma unroll
+        for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, nullptr, i, lane);
+    }
+
+    PvAcc acc;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st;
+    st.m_ref = -INFINITY;
+    st.lsum = 0.0f;
+    GatherPlan8 no_gather;
+    no_gather.active = false;
+    no_gather.nload = 0;
+
+    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
+        f32x4_t s[2];
+        own_scores(sp, sx, wave, kk, lane, s);
+        float factor;
+        bool moved;
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
+        pl[wave * kWave + lane] = pb;
+        if (g == 0) rec(t).fac[16 * wave + c] = factor;
+        if (lane == 0) rec(t).flag[wave] = moved ? 1u : 0u;
+    };
+
+    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
+    wait_tiles8(min(ntiles - 1, kStages8 - 2), nload);
+    lds_barrier();
+    {
+        f32x4_t sp[2][2];
+        pv_qk8<false, true>(buf(0), rec(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();
+        finish_scores(0, sp);
+    }
+    // Iteration t: P.V of tile t with Q.K^T of tile t+1 and the gather of tile
+    // t+6 into the buffer tile t-1 has left; then the exchange and softmax of t+1.
+    for (int t = 0; t + 1 < ntiles; ++t) {
+        wait_tiles8(min(ntiles - 1, t + kStages8 - 2) - (t + 1), nload);
+        lds_barrier();  // tile t+1 in LDS; P^T and record of tile t visible; buffer of tile t-1 free
+        const int u = t + kStages8 - 1;
+        GatherPlan8 gp = plan_gather8(kvb, rows_lds, min(u, ntiles - 1), nrows, L, buf(u), wave, lane);
+        gp.active = u < ntiles;
+        f32x4_t sp[2][2];
+        pv_qk8<true, true>(buf(t), rec(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp);
+        send_partial(sp, sx, wave, kk, lane);
+        lds_barrier();  // partials exchanged; every wave is done reading P^T and the record of tile t
+        finish_scores(t + 1, sp);
+    }
+    lds_barrier();
+    {
+        f32x4_t sp[2][2];
+        pv_qk8<true, false>(buf(ntiles - 1), rec(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp,
+                            no_gather);
+    }
+    store_output<DIRECT>(acc, st, sx, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
 }
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
@@ -794,38 +965,47 @@ size_t attn_ws_bytes(int rows, int k) {
     return align_up(n * kDv * sizeof(uint16_t), 256) + align_up(n * sizeof(float), 256);
 }
 
-template <bool FP8>
-static hipError_t launch_attn_t(const uint16_t* q, const void* kv, int64_t kv_bstride, const int32_t* idx, int B,
-                                int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                                hipStream_t stream) {
+hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
+                       int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
     const int rows = B * T;
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL((sparse_mla_kernel<true, FP8>), dim3(xcd_grid(rows, 1)), dim3(kThreads), 0, stream, q, kv,
+        hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(kThreads), 0, stream, q, kv,
                            kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL((sparse_mla_kernel<false, FP8>), dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q,
-                       kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q, kv,
+                       kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
                        nullptr, nullptr);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
                        part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
 }
 
-hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
-                       int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
-    return launch_attn_t<false>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, stream);
-}
-
 hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                            int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
                            hipStream_t stream) {
-    return launch_attn_t<true>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, stream);
+    const int rows = B * T;
+    const SplitPlan p = plan(rows, k);
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+    if (p.nsplit == 1) {
+        hipLaunchKernelGGL(sparse_mla_fp8_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(kThreads), 0, stream, q, kv,
+                           kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
+        return hipGetLastError();
+    }
+    const size_t n = (size_t)rows * p.nsplit * kHq;
+    uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
+    float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
+    hipLaunchKernelGGL(sparse_mla_fp8_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q, kv,
+                       kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
+                       nullptr, nullptr);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
+                       part_lse, rows, p.nsplit, out, lse);
+    return hipGetLastError();
 }
 
 }  // namespace dsa
