@@ -262,7 +262,8 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
     u32x4_t pw;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-        const uint32_t h2 = pack_bf16x2(exp2f(x[e] - mu), exp2f(x[e + 1] - mu));
+        // v_exp_f32 directly: arguments are <= 32 here and results below 2^-126 may flush to 0
+        const uint32_t h2 = pack_bf16x2(__builtin_amdgcn_exp2f(x[e] - mu), __builtin_amdgcn_exp2f(x[e + 1] - mu));
         st.lsum += __uint_as_float(h2 << 16) + __uint_as_float(h2 & 0xFFFF0000u);  // the bf16 values P uses
         pw[e / 2] = h2;
     }
@@ -270,14 +271,23 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
 }
 
 // Bits e of this lane's values (rows (e>>2)*16 + 4g + (e&3) of tile t) that are visible.
-__device__ __forceinline__ uint32_t valid_bits(const int* rows_lds, int t, int g, int L) {
+// rows_lds holds -1 for every masked or missing entry (canonicalised when the
+// list is loaded), so visibility is the sign bit.
+__device__ __forceinline__ uint32_t valid_bits(const int* rows_lds, int t, int g) {
     const int4 ra = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 4 * g);
     const int4 rb = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 16 + 4 * g);
     const int r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
     uint32_t v = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v |= (r8[e] >= 0 && r8[e] < L) ? (1u << e) : 0u;
+    for (int e = 0; e < 8; ++e) v |= ((uint32_t)~r8[e] >> 31) << e;
     return v;
+}
+
+// Entry j of a split's row list as kept in LDS: the row, or -1 when it is
+// missing (j >= nrows) or masked (outside [0, L)).
+__device__ __forceinline__ int list_entry(const int32_t* sel, int j, int nrows, int L) {
+    const int r = j < nrows ? sel[j] : -1;
+    return (r >= 0 && r < L) ? r : -1;
 }
 
 // Apply the rescale factors recorded with tile tv's softmax to the accumulators.
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
     }
     const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
     // Consume q here so the compiler's own wait for these loads (it cannot see the
     // gathers, which are issued from asm) stays ahead of the first gather.
 #pragma unroll
@@ -503,7 +513,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         own_scores(sp, sx, wave, kk, lane, s);
         float factor;
         bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
         pl[wave * kWave + lane] = pb;
         char* tail = reinterpret_cast<char*>(buf(t));
         if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * wave + c] = factor;
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
     }
     const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = j < nrows ? sel[j] : -1;
+    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -826,7 +836,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         own_scores(sp, sx, wave, kk, lane, s);
         float factor;
         bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g, L), scale_log2, st, factor, moved);
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
         pl[wave * kWave + lane] = pb;
         if (g == 0) rec(t).fac[16 * wave + c] = factor;
         if (lane == 0) rec(t).flag[wave] = moved ? 1u : 0u;
