@@ -92,10 +92,8 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // Wave w loads the main KiB of rows 8w .. 8w+7 (one load per row: the row index
 // is wave-uniform, so the address is a scalar base plus this lane's swizzled
 // offset) and the tails of the same 8 rows (one load).  Masked or missing rows
-// read row 0 (finite values) and get P = 0.  The plan is computed once; its nine
-// loads are then issued one at a time between matrix instructions, because a
-// wave stalls while the CU's address unit works through the loads ahead of
-// its own.
+// read row 0 (finite values) and get P = 0.  The plan is computed once and its
+// nine loads are issued together at the start of the tile's matrix work.
 struct GatherPlan {
     const uint16_t* row[8];  // wave-uniform row bases
     uint32_t lds[8];         // wave-uniform LDS byte addresses of the rows' main parts
@@ -314,7 +312,7 @@ __device__ __forceinline__ void apply_rescale(const uint16_t* tv, int c, PvAcc& 
 // Q.K^T partial of tile `tq` (this wave's half of the dims, both head blocks of
 // its pair) fused with P.V of tile `tv` (this wave's 128 value dims, all four
 // head blocks): two independent instruction streams, alternated in chunks.
-// When `gp` is active its nine loads are issued between matrix instructions.
+// When `gp` is active its loads are issued first.
 template <bool PV, bool QK>
 __device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad,
                                       const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
@@ -332,7 +330,10 @@ __device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, co
 #pragma unroll
             for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    issue_gather(gp, kvb, 8, lane);
+    // the next tile's gathers go out together before the matrix work (measured
+    // faster than spreading them between matrix instructions)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
         if (PV) {
@@ -345,7 +346,6 @@ __device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, co
                 const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
-                if (i == 0) issue_gather(gp, kvb, 2 * ch, lane);
             }
         }
         if (QK) {
@@ -367,11 +367,7 @@ __device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, co
                     sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
                     sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
                 }
-                if (kl == k0) issue_gather(gp, kvb, 2 * ch + 1, lane);
             }
-        } else if (!PV) {
-            issue_gather(gp, kvb, 2 * ch, lane);
-            issue_gather(gp, kvb, 2 * ch + 1, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -728,6 +724,8 @@ __device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, co
             for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
+    for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, nullptr, i, lane);
+#pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
         if (PV) {
 #pragma unroll
@@ -738,7 +736,6 @@ __device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, co
                 const bf16x8_t a = e4m3x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
-                if (i == 0) issue_gather(gp, nullptr, 2 * ch, lane);
             }
         }
         if (QK) {
@@ -756,11 +753,7 @@ __device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, co
                     sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
                     sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
                 }
-                if (kl == k0) issue_gather(gp, nullptr, 2 * ch + 1, lane);
             }
-        } else if (!PV) {
-            issue_gather(gp, nullptr, 2 * ch, lane);
-            issue_gather(gp, nullptr, 2 * ch + 1, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
