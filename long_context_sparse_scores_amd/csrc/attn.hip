@@ -390,11 +390,13 @@ __device__ __forceinline__ void own_scores(const f32x4_t (&sp)[2][2], const f32x
 // Epilogue of both kernels: denominators (and reference maxima) of all 64
 // heads from their owner waves, then the normalised output of this split (or
 // of the whole list) and its log-sum-exp.
+constexpr int kStageRow = 2 * kDv + 16;  // bytes per output row staged in LDS (64 rows: 65 KiB)
+
 template <bool DIRECT>
-__device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxState& st, f32x4_t* sx, int wave,
-                                             int lane, int bt, int split, int nsplit, uint16_t* __restrict__ part_o,
-                                             float* __restrict__ part_lse, uint16_t* __restrict__ out,
-                                             float* __restrict__ lse) {
+__device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxState& st, f32x4_t* sx, void* stage,
+                                             int wave, int lane, int bt, int split, int nsplit,
+                                             uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int c = lane & 15;
     const int g = lane >> 4;
     float lsum = st.lsum;
@@ -413,15 +415,26 @@ __device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxStat
         const float ls = stats[16 * hb + c];
         inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
     }
-    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+    // The 64 x 512 bf16 result goes through the (now free) tile LDS, rows padded
+    // to 1040 bytes so that these 8-byte writes hit every bank once, and then
+    // out as whole 1 KiB rows: one 16-byte store per lane per head.
+    char* st8 = reinterpret_cast<char*>(stage);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
             const f32x4_t& o = acc.o[d][hb];
-            *reinterpret_cast<uint2*>(dst + (16 * hb + c) * kDv + 128 * wave + 16 * d + 4 * g) =
+            *reinterpret_cast<uint2*>(st8 + (16 * hb + c) * kStageRow + 2 * (128 * wave + 16 * d + 4 * g)) =
                 make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
         }
+    lds_barrier();
+    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int h = 16 * wave + i;
+        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
+            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
+    }
     const int head = 16 * wave + c;
     if (DIRECT) {
         if (lse && g == 0)
@@ -460,6 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     constexpr int kStages = Cfg<DIRECT>::kStages;
     __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
+    static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile buffers");
     __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
     __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
     __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         pv_qk<true, false>(buf(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
     }
 
-    store_output<DIRECT>(acc, st, sx, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
+    store_output<DIRECT>(acc, st, sx, tiles, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
 }
 
 // ------------------------------------------------------------------ E4M3 latent rows
@@ -781,6 +795,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int nload = wave < 2 ? 5 : 4;
 
     __shared__ __attribute__((aligned(16))) uint8_t tiles[kStages8 * kTile8Bytes];
+    static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile ring");
     __shared__ __attribute__((aligned(16))) Rescale8 rescale[kStages8];
     __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];
     __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];
@@ -864,7 +879,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         pv_qk8<true, false>(buf(ntiles - 1), rec(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp,
                             no_gather);
     }
-    store_output<DIRECT>(acc, st, sx, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
+    store_output<DIRECT>(acc, st, sx, tiles, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
 }
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
