@@ -884,64 +884,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
 // split s, out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
-// summed in split order.  One 128-thread block per (query, head), 4 dims per
-// thread; blocks numbered like the split kernel so each reads partials from its
-// own XCD's L2.  The split weights go through LDS while the partial loads are
-// already in flight.
+// the numerator summed in split order.  One 128-thread block per (query, head),
+// 4 dims per thread; blocks numbered like the split kernel so each reads
+// partials from its own XCD's L2.
 constexpr int kCombineThreads = 128;
 constexpr int kCombineBatch = 16;  // splits loaded per round
 
+// Every wave derives the split weights itself: lane s holds split s's
+// log2-sum-exp (nsplit <= 64), the maximum and the denominator come from wave
+// reductions, and the weights reach the accumulation loop through readlane, so
+// the block needs no barrier.  The partial loads go out first.
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                        const float* __restrict__ part_lse, int rows,
                                                                        int nsplit, uint16_t* __restrict__ out,
                                                                        float* __restrict__ lse) {
+    static_assert(kMaxSplits <= kWave, "one lane per split");
     const int grp = blockIdx.x / (kXcds * kHq);
     const int rem = blockIdx.x % (kXcds * kHq);
     const int head = rem / kXcds;
     const int bt = grp * kXcds + rem % kXcds;
     if (bt >= rows) return;
-    __shared__ float wl[kMaxSplits];  // per split: log2-sum-exp, then weight
-    __shared__ float stat[2];
+    const int lane = lane_id();
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
     const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
-        uint2 v[kCombineBatch];
+    uint2 v[kCombineBatch];
+    auto load_batch = [&](int s0) {
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
             const int sp = min(s0 + u, nsplit - 1);  // past the end: a valid split, weight 0 below
             v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
         }
-        if (s0 == 0) {
-            for (int sp = threadIdx.x; sp < nsplit; sp += kCombineThreads) wl[sp] = pl[(int64_t)sp * kHq];
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                float M = -INFINITY;
-                for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, wl[sp]);
-                float den = 0.0f;
-                if (M != -INFINITY)
-                    for (int sp = 0; sp < nsplit; ++sp) {
-                        const float a = wl[sp] == -INFINITY ? 0.0f : exp2f(wl[sp] - M);
-                        wl[sp] = a;
-                        den += a;
-                    }
-                else
-                    for (int sp = 0; sp < nsplit; ++sp) wl[sp] = 0.0f;
-                stat[0] = M;
-                stat[1] = den;
-            }
-            __syncthreads();
-        }
+    };
+    load_batch(0);
+    const float ls = lane < nsplit ? pl[(int64_t)lane * kHq] : -INFINITY;
+    float M = ls;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    const float a = (ls == -INFINITY) ? 0.0f : exp2f(ls - M);  // M == -inf only when every split is empty
+    float den = a;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, kWave);
+    const uint32_t a_bits = __float_as_uint(a);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        if (s0 > 0) load_batch(s0);
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
-            const float a = s0 + u < nsplit ? wl[s0 + u] : 0.0f;
-            acc[0] += a * __uint_as_float(v[u].x << 16);
-            acc[1] += a * __uint_as_float(v[u].x & 0xFFFF0000u);
-            acc[2] += a * __uint_as_float(v[u].y << 16);
-            acc[3] += a * __uint_as_float(v[u].y & 0xFFFF0000u);
+            const float w = s0 + u < nsplit ? __uint_as_float(__builtin_amdgcn_readlane(a_bits, s0 + u)) : 0.0f;
+            acc[0] += w * __uint_as_float(v[u].x << 16);
+            acc[1] += w * __uint_as_float(v[u].x & 0xFFFF0000u);
+            acc[2] += w * __uint_as_float(v[u].y << 16);
+            acc[3] += w * __uint_as_float(v[u].y & 0xFFFF0000u);
         }
     }
-    const float M = stat[0], den = stat[1];
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) =
         make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
