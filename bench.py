@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak, published
 PREFILL_MIN_QUERIES = 8         # chunks of at least this many queries per sequence take the tile kernel
 METRIC = "query-tokens/sec per 4-layer DSA group at 128K ctx; % of HBM roofline"
 
@@ -255,13 +256,15 @@ def main():
     pos = cfg.q_pos().astype(np.int64)
     idx_flops = int(((np.minimum(pos, L - 1) + 1) * cfg.H * cfg.D * 2).sum())
     attn_flops = nl * qtok * cfg.Hq * k * (cfg.Dqk + cfg.Dv) * 2
-    if T >= PREFILL_MIN_QUERIES and not args.index_fp8:
+    if T >= PREFILL_MIN_QUERIES:
         # a chunk of queries runs the matrix-core tile kernel: one key scan for the
-        # whole chunk, bound by the bf16 matrix peak rather than by HBM
+        # whole chunk, bound by the matrix peak of its input type rather than by HBM
         idx_tflops = idx_flops / (idx_ms / 1e3) / 1e12
-        roofline = {"kernel": "indexer_prefill_kernel", "bound": "mfma", "achieved": round(idx_tflops, 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": None, "flops_per_launch": idx_flops, "avg_launch_ms": round(idx_ms, 4)}
+        peak = MFMA_FP8_PEAK_TFLOPS if args.index_fp8 else MFMA_BF16_PEAK_TFLOPS
+        roofline = {"kernel": "indexer_prefill_fp8_kernel" if args.index_fp8 else "indexer_prefill_kernel",
+                    "bound": "mfma", "achieved": round(idx_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(idx_tflops / peak, 4), "traffic": None, "flops_per_launch": idx_flops,
+                    "avg_launch_ms": round(idx_ms, 4)}
     else:
         roofline = {"kernel": "indexer_decode_fp8_kernel" if args.index_fp8 else "indexer_decode_kernel",
                     "bound": "hbm", "achieved": round(achieved, 1),

@@ -388,6 +388,131 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     (void)prow;
 }
 
+
+// ------------------------------------------------------------------ E4M3 multi-query (prefill) chunks
+// The prefill tile kernel for E4M3 index queries and keys.  gfx950's
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit scales) contracts a
+// whole 128-byte key in one instruction at twice the bf16 rate: lane (c, g)
+// supplies bytes 32g .. 32g+31 of A row c and of B column c (a probe on the box
+// confirmed that A and B bytes pair by position).  Work split as in the bf16
+// kernel: 16 queries per workgroup, 4 per wave held as A operands (2 head
+// blocks x 32 bytes each), 64-key tiles through a double-buffered LDS stage
+// (16-byte chunk s of key k at 8k + (s ^ ((k >> 1) & 7)): conflict-free), and
+// every B operand read feeds 8 instructions.
+constexpr int kPf8TileKeys = 64;
+constexpr int kPf8TileBytes = kPf8TileKeys * kD8;  // 8 KiB
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma16x16x128_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);  // E4M3, scales 2^0
+}
+
+__global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb, float* __restrict__ scores,
+    ZeroRange zero) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kPf8TileBytes];
+    const int kb_i = blockIdx.x % nkb;
+    const int qg = (blockIdx.x / nkb) % nqg;
+    const int b = blockIdx.x / (nkb * nqg);
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int t0 = qg * kPfQueries + kPfQPerWave * wave;
+
+    if (zero.base && kb_i == 0)
+        for (int i = threadIdx.x; i < kPfQueries * zero.count; i += 256) {
+            const int t = qg * kPfQueries + i / zero.count;
+            if (t < T) zero.base[((int64_t)b * T + t) * zero.stride + i % zero.count] = 0u;
+        }
+
+    // A operands: head 16*ht + c of the wave's 4 queries, bytes 32g .. 32g+31
+    i32x8_t qa[kPfQPerWave][2];
+    float wv[kPfQPerWave][2][4];
+#pragma unroll
+    for (int i = 0; i < kPfQPerWave; ++i) {
+        const int t = min(t0 + i, T - 1);  // past the end: the last query, never stored
+        const int64_t row = (int64_t)b * T + t;
+        const uint8_t* qrow = q_idx + row * kH * kD8;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) qa[i][ht] = *reinterpret_cast<const i32x8_t*>(qrow + (16 * ht + c) * kD8 + 32 * g);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[i][ht][r] = w[row * kH + 16 * ht + 4 * g + r];
+    }
+    const int my_t = t0 + g;
+    const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
+    const int64_t my_p = q_pos[my_row];
+    float* my_out = scores + my_row * L;
+
+    const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
+    const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
+    const int ntiles = (int)((min((int64_t)L, key0 + kPfKeysPerBlock) - key0 + kPf8TileKeys - 1) / kPf8TileKeys);
+    // tile loads: thread i brings 16-byte chunks i and i + 256 (key = chunk / 8, s = chunk % 8)
+    u32x4_t ld[2];
+    auto load_tile = [&](int j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int chunk = (int)threadIdx.x + 256 * h;
+            int64_t key = key0 + (int64_t)j * kPf8TileKeys + (chunk >> 3);
+            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
+            ld[h] = *reinterpret_cast<const u32x4_t*>(kb + key * kD8 + 16 * (chunk & 7));
+        }
+    };
+    auto store_tile = [&](int j) {
+        uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int chunk = (int)threadIdx.x + 256 * h;
+            const int k = chunk >> 3, sc = chunk & 7;
+            *reinterpret_cast<u32x4_t*>(tile + 16 * (8 * k + (sc ^ ((k >> 1) & 7)))) = ld[h];
+        }
+    };
+    load_tile(0);
+    store_tile(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int j = 0; j < ntiles; ++j) {
+        if (j + 1 < ntiles) load_tile(j + 1);  // in flight while tile j is computed
+        const uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
+#pragma unroll
+        for (int st = 0; st < kPf8TileKeys / 16; ++st) {
+            const int k = 16 * st + c;  // key of this lane's B column
+            const int f = (k >> 1) & 7;
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(tile + 16 * (8 * k + ((2 * g) ^ f)));
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(tile + 16 * (8 * k + ((2 * g + 1) ^ f)));
+            const i32x8_t kv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            float part[kPfQPerWave];
+#pragma unroll
+            for (int i = 0; i < kPfQPerWave; ++i) {
+                const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+                const f32x4_t a0 = mfma16x16x128_fp8(qa[i][0], kv, zero4);
+                const f32x4_t a1 = mfma16x16x128_fp8(qa[i][1], kv, zero4);
+                float v = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v = fmaf(wv[i][0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
+                    v = fmaf(wv[i][1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                }
+                part[i] = v;
+            }
+            // transpose-reduce over the 4 lane groups: group g ends with query g's total
+            const bool hi_g = (g & 2) != 0, lo_g = (g & 1) != 0;
+            const float r0 = __shfl_xor(hi_g ? part[0] : part[2], 32, kWave);
+            const float r1 = __shfl_xor(hi_g ? part[1] : part[3], 32, kWave);
+            const float k0 = (hi_g ? part[2] : part[0]) + r0;
+            const float k1 = (hi_g ? part[3] : part[1]) + r1;
+            const float rr = __shfl_xor(lo_g ? k0 : k1, 16, kWave);
+            const float score = (lo_g ? k1 : k0) + rr;
+            const int64_t key = key0 + (int64_t)j * kPf8TileKeys + 16 * st + c;
+            if (my_t < T && key < L) my_out[key] = key <= my_p ? score : -INFINITY;
+        }
+        if (j + 1 < ntiles) store_tile(j + 1);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+}
 }  // namespace
 
 template <int W, int N>
@@ -417,6 +542,13 @@ hipError_t launch_indexer_fp8_cfg(const uint8_t* q_idx, const float* w, const ui
 hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                               const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
                               ZeroRange zero) {
+    if (T >= kPrefillMinQueries) {
+        const int nqg = (T + kPfQueries - 1) / kPfQueries;
+        const int nkb = (L + kPfKeysPerBlock - 1) / kPfKeysPerBlock;
+        hipLaunchKernelGGL(indexer_prefill_fp8_kernel, dim3((unsigned)((int64_t)B * nqg * nkb)), dim3(256), 0, stream,
+                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
+        return hipGetLastError();
+    }
     return launch_indexer_fp8_cfg<INDEXER8_WAVES, INDEXER8_TILES, INDEXER8_AHEAD>(q_idx, w, k_idx, k_bstride, q_pos,
                                                                                   B, T, L, scores, stream, zero);
 }

@@ -302,3 +302,47 @@ def test_fullsize_decode_128k_fp8_group(dsa):
         err, scale = assert_attn_close(host(outs[l])[b, 0], ref[0, 0], "layer %d b %d" % (l, b))
         say("  attn layer %d b=%d: max err %.3g of scale %.3g" % (l, b, err, scale))
         np.testing.assert_allclose(host(lses[l])[b, 0], ref_lse[0, 0], atol=LSE_TOL, rtol=0)
+
+
+# ------------------------------------------------------------------ E4M3 multi-query (prefill) chunks
+def test_indexer_fp8_prefill_full_code_range(dsa):
+    # chunks of >= 8 queries take the tile kernel, whose K=128 instruction adds
+    # the 128 products of a key aligned to the largest of them, keeping about
+    # 13 bits below it: |err| <= 128 * 2^-13 * sum_h |w_h| max_d |q_hd k_d| (+ fp32)
+    rng = np.random.default_rng(24)
+    B, T, L, Lc = 1, 19, 2100, 2176
+    qi = _full_range_codes(rng, (B, T, 32, 128))
+    ki = _full_range_codes(rng, (B, Lc, 128))
+    w = synth.pow2_f32(24, 2, (B, T, 32))
+    pos = (np.arange(T, dtype=np.int32) * 97 + 300)[None]
+    say("fp8 prefill-path indexer, full code range")
+    got = host(dsa.indexer_scores_fp8(u8_dev(qi), f32_dev(w), u8_dev(ki), i32_dev(pos), L=L))
+    ref = oracle.indexer_scores(qi, w, ki, pos, L=L, fp8=True)
+    qa = np.abs(oracle.e4m3_decode(qi))
+    ka = np.abs(oracle.e4m3_decode(ki))[:, :L]
+    mag = np.einsum("bth,bthl->btl", np.abs(w).astype(np.float64), np.einsum("bthd,bld->bthl", qa, ka))
+    pmax = np.stack([np.max(qa[:, t][:, :, None, :] * ka[:, None, :, :], axis=-1) for t in range(T)], axis=1)
+    bound = 2.0 ** -6 * np.einsum("bth,bthl->btl", np.abs(w).astype(np.float64), pmax) + 2.0 ** -18 * mag
+    finite = np.isfinite(ref)
+    np.testing.assert_array_equal(np.isfinite(got), finite)
+    err = np.abs(got[finite].astype(np.float64) - ref[finite])
+    assert (err <= bound[finite]).all(), (err / bound[finite]).max()
+
+
+def test_fullsize_prefill_fp8_index_equals_bf16(dsa):
+    # the 4096-query chunk at 128K: E4M3 scores equal the bf16 scores bitwise on
+    # every row (the same integers), and sampled rows equal the oracle's
+    cfg = synth.PREFILL
+    say("fp8 prefill 4096 x 131072: scans")
+    qi8, w, pos = cfg.q_idx_fp8(), cfg.w(), cfg.q_pos()
+    d_w, d_pos = f32_dev(w), i32_dev(pos)
+    s8 = dsa.indexer_scores_fp8(u8_dev(qi8), d_w, u8_dev(cfg.k_idx_fp8()), d_pos)
+    s16 = dsa.indexer_scores(bf16_dev(cfg.q_idx()), d_w, bf16_dev(cfg.k_idx()), d_pos)
+    torch.cuda.synchronize()
+    assert torch.equal(s8.view(torch.int32), s16.view(torch.int32))
+    del s16
+    ki = cfg.k_idx_rows_fp8(0)[None]
+    for t in (0, 2047, 4095):
+        say("  oracle row t=%d" % t)
+        ref = oracle.indexer_scores(qi8[:, t:t + 1], w[:, t:t + 1], ki, pos[:, t:t + 1], fp8=True)
+        _bits_equal(s8[0, t].cpu().numpy(), ref[0, 0])
