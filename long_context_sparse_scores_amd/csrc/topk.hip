@@ -9,59 +9,61 @@
 // k-th largest key K* is found digit by digit (11 + 11 + 10 bits, most
 // significant first).  Each row is cut into slices (a few hundred workgroups
 // over all rows, so a few long rows still fill the chip); a slice is cut
-// into one contiguous range per wave.  Five launches:
-//   init    zero the row's global histogram and counters;
+// into one contiguous range per wave.  The passes:
+//   init    zero the row's global histogram and counters (the layer group
+//           lets the indexer do this instead);
 //   hist    histogram of the top digit (LDS per slice, non-zero bins added
 //           to the row's histogram);
-//   filter  every slice finds the threshold digit T from that histogram,
-//           counts per wave the keys whose top digit is above T, and appends
-//           the keys whose top digit equals T to the row's candidate list;
-//   resolve one workgroup per row: the middle and low digits of K* and the
-//           number of keys equal to K* still to take, from the candidates
-//           (LDS histograms); per wave, the
-//           number of selected keys and of keys equal to K* before it;
-//   write   each wave writes its selected positions in order (ballot ranks)
-//           from its output offset: every key above K*, and keys equal to K*
-//           while their rank in position order is below the number to take.
-// Each pass issues its score loads before it reads the row's histograms and
-// counters, and synchronises through LDS only, so the two latencies overlap.
-// The score rows are re-read from L2 / the last-level cache by each pass.
+//   filter  every slice finds the threshold digit T from that histogram and
+//           appends every key whose top digit is T or above to the row's
+//           candidate list (fewer than k lie above T, so the list is the
+//           top-k plus the keys that share T's bin);
+//   select  one workgroup per row, from the candidates alone: the middle and
+//           low digits of K*, the number of keys equal to K* to take and,
+//           when ties straddle the cut, the lowest positions among them (a
+//           second radix select, on the complemented position, or a direct
+//           ranking when there are at most 64 of them); the k kept positions
+//           are compacted into LDS and written out in ascending order from a
+//           bitmap of the row's positions (one chunk of 2^17 at a time).
+// The scores are thus read twice (hist, filter), and select never touches
+// them.  (Running select in the last filter workgroup of each row would save
+// a launch, but publishing the candidates across XCDs then takes an L2
+// write-back per workgroup, which costs far more on this part.)
 // When a row's candidate list overflows its capacity (heavily tied scores),
-// resolve reads the whole row instead; the result is the same.
+// select scans the whole row instead; the result is the same.
 #include "common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSelectThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kResolveThreads = 1024;
 constexpr int kBins = 2048;
 constexpr int kTargetBlocks = 512;   // slices over all rows
 constexpr int kMinSlice = 4096;
-constexpr int kMaxUnits = 2048;      // waves (slice x 4) per row
+constexpr int kMaxSlices = 512;      // per row
 constexpr int kStage = 256;          // per-wave LDS staging of candidates
 constexpr int kBatch = 32;           // loads in flight per lane in the streaming passes
-constexpr int kCandRegs = 8;         // candidates per resolve thread kept in registers
+constexpr int kSelMax = 2048;        // the kept positions (k <= 2048) are compacted in LDS
+constexpr int kBitWords = 4096;      // position bitmap: 2^17 positions per chunk
+constexpr int kCandLds = 12288;      // candidates the selection holds in LDS
+constexpr int kSelBatch = kCandLds / kSelectThreads;  // loads in flight per thread in its passes
 
 // Per-row workspace (32-bit words).
-enum : int { kCtrCand = 0, kStKey = 2, kStTakeEq = 3, kCtrWords = 8 };
+// kStT, kStAbove: the threshold digit T and the count of keys whose top digit is above it.
+enum : int { kCtrCand = 0, kStT = 1, kStAbove = 2, kCtrWords = 8 };
 
 struct Layout {
     int slice;    // elements per slice (multiple of 256)
     int nslice;   // slices per row
     int cap;      // candidate capacity per row
-    __host__ __device__ int units() const { return nslice * kWaves; }
-    __host__ __device__ int wave_len() const { return slice / kWaves; }
-    __host__ __device__ size_t row_words() const { return kBins + kCtrWords + 3 * (size_t)units() + 2 * (size_t)cap; }
+    __host__ __device__ size_t row_words() const { return kBins + kCtrWords + 2 * (size_t)cap; }
 };
 
 struct RowWs {
     uint32_t* hist1;   // [kBins] top digit
     uint32_t* ctr;     // [kCtrWords]
-    uint32_t* gt_hi;   // [units] keys with top digit > T, per wave
-    uint32_t* sel_b;   // [units] selected keys in the waves before (written by resolve)
-    uint32_t* eq_b;    // [units] keys == K* in the waves before (written by resolve)
     uint32_t* cpos;    // [cap] candidate positions
     uint32_t* ckey;    // [cap] candidate keys
 };
@@ -71,10 +73,7 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int row, const Layout& lo) {
     RowWs r;
     r.hist1 = b;
     r.ctr = b + kBins;
-    r.gt_hi = r.ctr + kCtrWords;
-    r.sel_b = r.gt_hi + lo.units();
-    r.eq_b = r.sel_b + lo.units();
-    r.cpos = r.eq_b + lo.units();
+    r.cpos = r.ctr + kCtrWords;
     r.ckey = r.cpos + lo.cap;
     return r;
 }
@@ -93,6 +92,8 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
 // Workgroup barrier for LDS hand-offs that leaves outstanding global loads in
 // flight (__syncthreads would wait for them as well).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The same between the lanes of one wave (LDS executes a wave's accesses in order).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Exclusive prefix sum over a workgroup of NT threads; `scratch` holds NT/64 words of LDS.
 template <int NT>
@@ -133,19 +134,19 @@ __device__ __forceinline__ HistPart<NT> load_hist(const uint32_t* hist, int nbin
     return hp;
 }
 
-// The bin holding the `need`-th largest element (1 <= need <= total) and the
-// count of elements in higher bins.  All NT threads call it.
+// The bin holding the `need`-th largest element (1 <= need <= total), the
+// count of elements in higher bins and the count in that bin.  All NT threads call it.
 struct BinPick {
-    uint32_t bin, above;
+    uint32_t bin, above, count;
 };
 
 template <int NT>
-__device__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, uint32_t* scratch, BinPick* result) {
+__device__ __forceinline__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, uint32_t* scratch, BinPick* result) {
     constexpr int per = kBins / NT;
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) s += hp.h[i];
-    if (threadIdx.x == 0) *result = BinPick{0u, 0u};
+    if (threadIdx.x == 0) *result = BinPick{0u, 0u, 0u};
     uint32_t total;
     const uint32_t above = excl_scan<NT>(s, scratch, &total);  // count in higher bins (also orders the reset)
     if (above < need && need <= above + s) {
@@ -153,8 +154,7 @@ __device__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, ui
 #pragma unroll
         for (int i = 0; i < per; ++i) {
             if (acc + hp.h[i] >= need) {
-                result->bin = (uint32_t)(nbins - 1 - (per * (int)threadIdx.x + i));
-                result->above = acc;
+                *result = BinPick{(uint32_t)(nbins - 1 - (per * (int)threadIdx.x + i)), acc, hp.h[i]};
                 break;
             }
             acc += hp.h[i];
@@ -164,6 +164,240 @@ __device__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, ui
     const BinPick r = *result;
     lds_sync();
     return r;
+}
+
+// LDS of the selection.
+template <int NT>
+struct SelectLds {
+    struct {
+        uint32_t pos[kCandLds], key[kCandLds];
+    } cand;  // copy of the candidate list
+    uint32_t h[kBins];
+    uint32_t sel[kSelMax];
+    uint32_t bits[kBitWords];
+    uint32_t wpre[kBitWords];  // kept positions in the bitmap words before each word
+    uint32_t scratch[NT / kWave];
+    BinPick pick;
+    uint32_t nsel, cut;
+};
+
+// Clear h[0, nbins), let fill(h) add to it, then pick the bin of the need-th largest.
+template <int NT, typename Fill>
+__device__ __forceinline__ BinPick hist_pick(SelectLds<NT>& s, int nbins, uint32_t need, Fill&& fill) {
+    for (int i = threadIdx.x; i < nbins; i += NT) s.h[i] = 0u;
+    lds_sync();
+    fill(s.h);
+    lds_sync();
+    const HistPart<NT> hp = load_hist<NT>(s.h, nbins);
+    return pick_bin<NT>(hp, nbins, need, s.scratch, &s.pick);
+}
+
+// The k kept positions of one row with n > k visible keys, ascending, into
+// out[0, k): NT threads, the candidate list (keys with top digit >= T) of the
+// filter pass, or the row's scores after an overflow.
+template <int NT>
+__device__ __forceinline__ void select_row(const float* __restrict__ row_scores, int64_t n, int k, const RowWs& rw,
+                                           int cap, int32_t* __restrict__ out, SelectLds<NT>& s) {
+    const uint32_t ncand = rw.ctr[kCtrCand];
+    const uint32_t T = rw.ctr[kStT];
+    const uint32_t need = (uint32_t)k - rw.ctr[kStAbove];
+    const bool from_list = ncand <= (uint32_t)cap;                  // else the list overflowed
+    const bool in_lds = from_list && ncand <= (uint32_t)kCandLds;
+    const int lane = lane_id();
+    constexpr uint32_t kStep = kSelBatch * NT;
+    if (in_lds) {  // one batch of loads per thread
+        static_assert(kCandLds <= kSelBatch * NT, "the LDS copy is one batch");
+        uint32_t cp[kSelBatch], ck[kSelBatch];
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const uint32_t i = j * NT + threadIdx.x;
+            cp[j] = i < ncand ? rw.cpos[i] : 0u;
+            ck[j] = i < ncand ? rw.ckey[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const uint32_t i = j * NT + threadIdx.x;
+            if (i < ncand) {
+                s.cand.pos[i] = cp[j];
+                s.cand.key[i] = ck[j];
+            }
+        }
+        lds_sync();
+    }
+    // Visit every key of the row whose top digit is T or above in batches of
+    // kSelBatch per thread, all loads of a batch issued before any is used:
+    // g(key[], pos[], ok[]) with ok[j] set for the batch's candidates.  Every
+    // lane of a wave takes part in every call.
+    auto visit = [&](auto&& g) {
+        uint32_t ck[kSelBatch], cp[kSelBatch];
+        bool ok[kSelBatch];
+        if (in_lds) {
+#pragma unroll
+            for (int j = 0; j < kSelBatch; ++j) {
+                const uint32_t i = j * NT + threadIdx.x;
+                ok[j] = i < ncand;
+                ck[j] = ok[j] ? s.cand.key[i] : 0u;
+                cp[j] = ok[j] ? s.cand.pos[i] : 0u;
+            }
+            g(ck, cp, ok);
+        } else if (from_list) {
+            for (uint32_t i0 = 0; i0 < ncand; i0 += kStep) {
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j) {
+                    const uint32_t i = i0 + j * NT + threadIdx.x;
+                    ok[j] = i < ncand;
+                    ck[j] = ok[j] ? rw.ckey[i] : 0u;
+                    cp[j] = ok[j] ? rw.cpos[i] : 0u;
+                }
+                g(ck, cp, ok);
+            }
+        } else {
+            for (int64_t i0 = 0; i0 < n; i0 += kStep) {
+                float sv[kSelBatch];
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j) {
+                    const int64_t i = i0 + j * NT + threadIdx.x;
+                    sv[j] = i < n ? row_scores[i] : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j) {
+                    const int64_t i = i0 + j * NT + threadIdx.x;
+                    ck[j] = score_key(sv[j]);
+                    cp[j] = (uint32_t)i;
+                    ok[j] = i < n && (ck[j] >> 21) >= T;
+                }
+                g(ck, cp, ok);
+            }
+        }
+    };
+    // f(key, position) for every candidate
+    auto for_candidates = [&](auto&& f) {
+        visit([&](const uint32_t (&ck)[kSelBatch], const uint32_t (&cp)[kSelBatch], const bool (&ok)[kSelBatch]) {
+#pragma unroll
+            for (int j = 0; j < kSelBatch; ++j)
+                if (ok[j]) f(ck[j], cp[j]);
+        });
+    };
+    // K*: its middle and low digits among the keys whose top digit is T
+    const BinPick b1 = hist_pick<NT>(s, kBins, need, [&](uint32_t* h) {
+        for_candidates([&](uint32_t key, uint32_t) {
+            if ((key >> 21) == T) atomicAdd(&h[(key >> 10) & 0x7FFu], 1u);
+        });
+    });
+    const uint32_t need1 = need - b1.above;
+    const uint32_t prefix = (T << 11) | b1.bin;  // top 22 bits of K*
+    const BinPick b2 = hist_pick<NT>(s, 1024, need1, [&](uint32_t* h) {
+        for_candidates([&](uint32_t key, uint32_t) {
+            if ((key >> 10) == prefix) atomicAdd(&h[key & 0x3FFu], 1u);
+        });
+    });
+    const uint32_t kstar = (prefix << 10) | b2.bin;
+    const uint32_t take_eq = need1 - b2.above;  // of the b2.count keys equal to K*
+    // ties kept: position <= pos_cut.  When only some are taken, the take_eq
+    // lowest positions are the take_eq largest values of ~position (distinct).
+    uint32_t pos_cut = 0xFFFFFFFFu;
+    if (take_eq < b2.count && b2.count <= (uint32_t)kWave) {
+        // few ties: gather them, and one wave ranks each by position
+        if (threadIdx.x == 0) s.nsel = 0u;
+        lds_sync();
+        for_candidates([&](uint32_t key, uint32_t pos) {
+            if (key == kstar) s.sel[atomicAdd(&s.nsel, 1u)] = pos;
+        });
+        lds_sync();
+        if (threadIdx.x < kWave) {
+            const uint32_t my = (uint32_t)lane < b2.count ? s.sel[lane] : 0xFFFFFFFFu;
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < b2.count; ++j) rank += s.sel[j] < my ? 1u : 0u;
+            if ((uint32_t)lane < b2.count && rank == take_eq - 1u) s.cut = my;
+        }
+        lds_sync();
+        pos_cut = s.cut;
+    } else if (take_eq < b2.count) {
+        auto ties = [&](auto&& g) {
+            for_candidates([&](uint32_t key, uint32_t pos) {
+                if (key == kstar) g(~pos);
+            });
+        };
+        const BinPick t0 = hist_pick<NT>(s, kBins, take_eq, [&](uint32_t* h) {
+            ties([&](uint32_t v) { atomicAdd(&h[v >> 21], 1u); });
+        });
+        const uint32_t tneed1 = take_eq - t0.above;
+        const BinPick t1 = hist_pick<NT>(s, kBins, tneed1, [&](uint32_t* h) {
+            ties([&](uint32_t v) {
+                if ((v >> 21) == t0.bin) atomicAdd(&h[(v >> 10) & 0x7FFu], 1u);
+            });
+        });
+        const uint32_t tneed2 = tneed1 - t1.above;
+        const uint32_t tprefix = (t0.bin << 11) | t1.bin;
+        const BinPick t2 = hist_pick<NT>(s, 1024, tneed2, [&](uint32_t* h) {
+            ties([&](uint32_t v) {
+                if ((v >> 10) == tprefix) atomicAdd(&h[v & 0x3FFu], 1u);
+            });
+        });
+        pos_cut = ~((tprefix << 10) | t2.bin);
+    }
+    // compact the k kept positions: per batch, one LDS atomic per wave
+    if (threadIdx.x == 0) s.nsel = 0u;
+    lds_sync();
+    visit([&](const uint32_t (&ck)[kSelBatch], const uint32_t (&cp)[kSelBatch], const bool (&ok)[kSelBatch]) {
+        uint64_t m[kSelBatch];
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            m[j] = __ballot(ok[j] && (ck[j] > kstar || (ck[j] == kstar && cp[j] <= pos_cut)));
+            tot += (uint32_t)__popcll(m[j]);
+        }
+        uint32_t base = 0;
+        if (lane == 0 && tot) base = atomicAdd(&s.nsel, tot);
+        base = __shfl(base, 0, kWave);
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            if ((m[j] >> lane) & 1u) {
+                const uint32_t slot = base + lane_rank(m[j]);
+                if (slot < (uint32_t)kSelMax) s.sel[slot] = cp[j];
+            }
+            base += (uint32_t)__popcll(m[j]);
+        }
+    });
+    lds_sync();
+    // ascending order, per chunk of 2^17 positions: a bitmap of the kept ones
+    // and the prefix count of its words give every kept position its rank
+    constexpr int kPer = kBitWords / NT;
+    uint32_t base = 0;
+    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kBitWords * 32) {
+        const int nw = (int)min((int64_t)kBitWords, (n - c0 + 31) / 32);
+        for (int i = threadIdx.x; i < nw; i += NT) s.bits[i] = 0u;
+        lds_sync();
+        for (int j = threadIdx.x; j < k; j += NT) {
+            const int64_t p = (int64_t)s.sel[j] - c0;
+            if (p >= 0 && p < (int64_t)nw * 32) atomicOr(&s.bits[p >> 5], 1u << (p & 31));
+        }
+        lds_sync();
+        uint32_t wc[kPer], cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int wi = (int)threadIdx.x * kPer + i;
+            wc[i] = wi < nw ? (uint32_t)__popc(s.bits[wi]) : 0u;
+            cnt += wc[i];
+        }
+        uint32_t total;
+        uint32_t o = excl_scan<NT>(cnt, s.scratch, &total);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            s.wpre[threadIdx.x * kPer + i] = o;
+            o += wc[i];
+        }
+        lds_sync();
+        for (int j = threadIdx.x; j < k; j += NT) {
+            const int64_t p = (int64_t)s.sel[j] - c0;
+            if (p >= 0 && p < (int64_t)nw * 32) {
+                const uint32_t below = s.bits[p >> 5] & ((1u << (p & 31)) - 1u);
+                out[base + s.wpre[p >> 5] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
+            }
+        }
+        base += total;
+        lds_sync();  // before the next chunk clears the bitmap
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_init_kernel(void* ws, Layout lo) {
@@ -219,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 
     // the row's top-digit histogram, then this wave's first batch of scores
     const HistPart<kThreads> hp = load_hist<kThreads>(rw.hist1, kBins);
-    const int64_t w0 = start + (int64_t)wave * lo.wave_len();
-    const int64_t w1 = min(w0 + lo.wave_len(), n);
+    const int64_t w0 = start + (int64_t)wave * (lo.slice / kWaves);
+    const int64_t w1 = min(w0 + lo.slice / kWaves, n);
     const float* row_scores = scores + (int64_t)row * L;
     float v[kBatch];
     auto load_batch = [&](int64_t i0) {
@@ -233,8 +467,11 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     load_batch(w0);
     const BinPick b0 = pick_bin<kThreads>(hp, kBins, (uint32_t)k, scratch, &pick);
     const uint32_t T = b0.bin;
+    if (slice == 0 && threadIdx.x == 0) {  // for the selection
+        rw.ctr[kStT] = T;
+        rw.ctr[kStAbove] = b0.above;
+    }
 
-    uint32_t gt = 0;
     // Candidates are staged per wave in LDS and appended to the row's list in
     // batches: one global atomic per batch rather than per 64 keys.
     uint32_t staged = 0;  // wave-uniform
@@ -260,11 +497,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int64_t i = i0 + j * kWave + lane;
-            const bool valid = i < w1;
             const uint32_t key = score_key(v[j]);
-            const uint32_t top = key >> 21;
-            gt += (valid && top > T) ? 1u : 0u;
-            const bool cand = valid && top == T;
+            const bool cand = i < w1 && (key >> 21) >= T;
             const uint64_t m = __ballot(cand);
             if (m) {
                 const uint32_t c = (uint32_t)__popcll(m);
@@ -279,200 +513,30 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         }
     }
     if (staged) flush();
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) gt += __shfl_xor(gt, off, kWave);
-    if (lane == 0) rw.gt_hi[slice * kWaves + wave] = gt;
 }
 
-// One 1024-thread workgroup per row: K* from the candidates (or, after an
-// overflow, from the whole row), then per wave of the filter/write passes the
-// number of selected keys and of keys equal to K* in the waves before it.
-__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(const float* __restrict__ scores,
-                                                                       const int32_t* __restrict__ q_pos, int L,
-                                                                       int k, Layout lo, void* ws) {
-    constexpr int NT = kResolveThreads;
+// One workgroup per row: the k kept positions in ascending order (rows with
+// at most k visible positions: all of them, then -1).
+__global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float* __restrict__ scores,
+                                                                     const int32_t* __restrict__ q_pos, int L,
+                                                                     int k, Layout lo, void* ws,
+                                                                     int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
     const int64_t n = n_visible(q_pos, row, L);
-    if (n <= k) return;
-    const int units_used = (int)((n + lo.slice - 1) / lo.slice) * kWaves;
-    RowWs rw = row_ws(ws, row, lo);
-    const float* row_scores = scores + (int64_t)row * L;
-    __shared__ uint32_t h2[kBins];
-    __shared__ uint32_t h3[1024];
-    __shared__ uint32_t gtc[kMaxUnits], eqc[kMaxUnits];
-    __shared__ uint32_t scratch[NT / kWave];
-    __shared__ BinPick pick;
-
-    // everything this kernel reads, issued together
-    const HistPart<NT> hp1 = load_hist<NT>(rw.hist1, kBins);
-    const uint32_t ncand = rw.ctr[kCtrCand];
-    uint32_t kk[kCandRegs], pp[kCandRegs];
-    const uint32_t reg_cap = (uint32_t)min(lo.cap, kCandRegs * NT);
-#pragma unroll
-    for (int j = 0; j < kCandRegs; ++j) {
-        const uint32_t i = j * NT + threadIdx.x;
-        kk[j] = i < reg_cap ? rw.ckey[i] : 0u;
-        pp[j] = i < reg_cap ? rw.cpos[i] : 0u;
-    }
-    uint32_t gh[kMaxUnits / NT];
-#pragma unroll
-    for (int j = 0; j < kMaxUnits / NT; ++j) {
-        const int u = (kMaxUnits / NT) * threadIdx.x + j;
-        gh[j] = u < units_used ? rw.gt_hi[u] : 0u;
-    }
-    for (int i = threadIdx.x; i < kBins; i += NT) h2[i] = 0u;
-    for (int i = threadIdx.x; i < 1024; i += NT) h3[i] = 0u;
-    for (int i = threadIdx.x; i < kMaxUnits; i += NT) gtc[i] = eqc[i] = 0u;
-
-    const BinPick b0 = pick_bin<NT>(hp1, kBins, (uint32_t)k, scratch, &pick);  // also orders the resets
-    const uint32_t T = b0.bin;
-    const uint32_t need = (uint32_t)k - b0.above;
-    const bool in_regs = ncand <= reg_cap;
-    const bool from_list = ncand <= (uint32_t)lo.cap;
-    // visit every key of the row whose top digit is T: f(key, position)
-    auto for_candidates = [&](auto&& f) {
-        if (in_regs) {
-#pragma unroll
-            for (int j = 0; j < kCandRegs; ++j)
-                if (j * NT + threadIdx.x < ncand) f(kk[j], pp[j]);
-        } else if (from_list) {
-            for (uint32_t i0 = 0; i0 < ncand; i0 += kCandRegs * NT) {
-                uint32_t ck[kCandRegs], cp[kCandRegs];
-#pragma unroll
-                for (int j = 0; j < kCandRegs; ++j) {
-                    const uint32_t i = i0 + j * NT + threadIdx.x;
-                    ck[j] = i < ncand ? rw.ckey[i] : 0u;
-                    cp[j] = i < ncand ? rw.cpos[i] : 0u;
-                }
-#pragma unroll
-                for (int j = 0; j < kCandRegs; ++j)
-                    if (i0 + j * NT + threadIdx.x < ncand) f(ck[j], cp[j]);
-            }
-        } else {
-            for (int64_t i0 = 0; i0 < n; i0 += kCandRegs * NT) {
-                float sv[kCandRegs];
-#pragma unroll
-                for (int j = 0; j < kCandRegs; ++j) {
-                    const int64_t i = i0 + j * NT + threadIdx.x;
-                    sv[j] = i < n ? row_scores[i] : 0.0f;
-                }
-#pragma unroll
-                for (int j = 0; j < kCandRegs; ++j) {
-                    const int64_t i = i0 + j * NT + threadIdx.x;
-                    const uint32_t key = score_key(sv[j]);
-                    if (i < n && (key >> 21) == T) f(key, (uint32_t)i);
-                }
-            }
-        }
-    };
-    for_candidates([&](uint32_t key, uint32_t) { atomicAdd(&h2[(key >> 10) & 0x7FFu], 1u); });
-    lds_sync();
-    const HistPart<NT> hp2 = load_hist<NT>(h2, kBins);
-    const BinPick b1 = pick_bin<NT>(hp2, kBins, need, scratch, &pick);
-    const uint32_t need1 = need - b1.above;
-    const uint32_t prefix = (T << 11) | b1.bin;  // top 22 bits of K*
-    for_candidates([&](uint32_t key, uint32_t) {
-        if ((key >> 10) == prefix) atomicAdd(&h3[key & 0x3FFu], 1u);
-    });
-    lds_sync();
-    const HistPart<NT> hp3 = load_hist<NT>(h3, 1024);
-    const BinPick b2 = pick_bin<NT>(hp3, 1024, need1, scratch, &pick);
-    const uint32_t kstar = (prefix << 10) | b2.bin;
-    const uint32_t take_eq = need1 - b2.above;
-    const uint32_t wl = (uint32_t)lo.wave_len();
-    for_candidates([&](uint32_t key, uint32_t pos) {
-        if (key > kstar) atomicAdd(&gtc[pos / wl], 1u);
-        else if (key == kstar) atomicAdd(&eqc[pos / wl], 1u);
-    });
-    lds_sync();
-    // per wave (unit): selected keys and keys equal to K* in the units before it
-    constexpr int kPer = kMaxUnits / NT;
-    uint32_t sel[kPer], eq[kPer], ssum = 0, esum = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int u = kPer * threadIdx.x + j;
-        sel[j] = u < units_used ? gh[j] + gtc[u] : 0u;
-        eq[j] = u < units_used ? eqc[u] : 0u;
-        ssum += sel[j];
-        esum += eq[j];
-    }
-    uint32_t tot;
-    uint32_t sb = excl_scan<NT>(ssum, scratch, &tot);
-    uint32_t eb = excl_scan<NT>(esum, scratch, &tot);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int u = kPer * threadIdx.x + j;
-        if (u < units_used) {
-            rw.sel_b[u] = sb;
-            rw.eq_b[u] = eb;
-        }
-        sb += sel[j];
-        eb += eq[j];
-    }
-    if (threadIdx.x == 0) {
-        rw.ctr[kStKey] = kstar;
-        rw.ctr[kStTakeEq] = take_eq;
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void topk_write_kernel(const float* __restrict__ scores,
-                                                              const int32_t* __restrict__ q_pos, int L, int k,
-                                                              Layout lo, void* ws, int32_t* __restrict__ idx) {
-    const int row = blockIdx.x / lo.nslice;
-    const int slice = blockIdx.x % lo.nslice;
-    const int64_t n = n_visible(q_pos, row, L);
     int32_t* out = idx + (int64_t)row * k;
-    if (n <= k) {  // every visible position, in order, then -1
-        if (slice == 0)
-            for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
+    if (n <= k) {
+        for (int j = threadIdx.x; j < k; j += kSelectThreads) out[j] = j < n ? j : -1;
         return;
     }
-    const int64_t start = (int64_t)slice * lo.slice;
-    if (start >= n) return;
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    RowWs rw = row_ws(ws, row, lo);
-    const int u = slice * kWaves + wave;
-    const uint32_t kstar = rw.ctr[kStKey];
-    const uint32_t take_eq = rw.ctr[kStTakeEq];
-    const uint32_t sel_b = rw.sel_b[u];
-    const uint32_t eq_b = rw.eq_b[u];
-    const int64_t w0 = start + (int64_t)wave * lo.wave_len();
-    const int64_t w1 = min(w0 + lo.wave_len(), n);
-    const float* row_scores = scores + (int64_t)row * L;
-    uint32_t pos = sel_b + (eq_b < take_eq ? eq_b : take_eq);
-    uint32_t eq_seen = eq_b;
-    for (int64_t i0 = w0; i0 < w1; i0 += kBatch * kWave) {
-        float v[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int64_t i = i0 + j * kWave + lane;
-            v[j] = i < w1 ? row_scores[i] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int64_t i = i0 + j * kWave + lane;
-            const bool valid = i < w1;
-            const uint32_t key = score_key(v[j]);
-            const bool eq = valid && key == kstar;
-            const uint64_t meq = __ballot(eq);
-            const bool sel = valid && (key > kstar || (eq && eq_seen + lane_rank(meq) < take_eq));
-            const uint64_t msel = __ballot(sel);
-            if (sel) {
-                const uint32_t o = pos + lane_rank(msel);
-                if (o < (uint32_t)k) out[o] = (int32_t)i;
-            }
-            pos += (uint32_t)__popcll(msel);
-            eq_seen += (uint32_t)__popcll(meq);
-        }
-    }
+    __shared__ SelectLds<kSelectThreads> sl;
+    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, row_ws(ws, row, lo), lo.cap, out, sl);
 }
 
 Layout make_layout(int rows, int L) {
     const int max_slices = (L + kMinSlice - 1) / kMinSlice;
     int ns = (kTargetBlocks + rows - 1) / rows;
     if (ns > max_slices) ns = max_slices;
-    if (ns > kMaxUnits / kWaves) ns = kMaxUnits / kWaves;
+    if (ns > kMaxSlices) ns = kMaxSlices;
     if (ns < 1) ns = 1;
     int64_t slice = ((int64_t)L + ns - 1) / ns;
     slice = (slice + 255) / 256 * 256;
@@ -509,9 +573,8 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     if (!state_zeroed) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
-    hipLaunchKernelGGL(topk_resolve_kernel, dim3(rows), dim3(kResolveThreads), 0, stream, scores, q_pos, L, k, lo,
-                       ws);
-    hipLaunchKernelGGL(topk_write_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws, idx);
+    hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
+                       idx);
     return hipGetLastError();
 }
 

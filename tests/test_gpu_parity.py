@@ -116,9 +116,9 @@ def test_topk_short_rows(dsa):
 
 
 def test_topk_candidate_overflow(dsa):
-    # a row's candidate list (keys sharing the threshold's top digit) holds
-    # max(4096, L/8) entries; fully tied rows overflow it and are resolved
-    # from the whole row instead
+    # a row's candidate list (keys whose top digit is the threshold's or
+    # above) holds max(4096, L/8) entries; fully tied rows overflow it and are
+    # selected from the whole row instead
     rng = np.random.default_rng(13)
     B, T, L = 1, 4, 40000
     say("topk candidate overflow")
@@ -127,6 +127,38 @@ def test_topk_candidate_overflow(dsa):
     s[0, 1] = np.where(rng.random(L) < 0.5, 1.0, 1.25).astype(np.float32)  # two values
     s[0, 2, ::2] = -0.0
     pos = np.array([[L - 1, L - 1, 30000, 20000]], np.int32)
+    _topk_case(dsa, s, pos, 2048)
+
+
+@pytest.mark.parametrize("n_tied", [11, 100])
+def test_topk_ties_straddling_cut(dsa, n_tied):
+    # distinct scores, except n_tied keys equal to the one ranked 2045th: only
+    # the lowest positions among them are kept (a wave ranks up to 64 ties;
+    # more go through the radix passes over positions)
+    rng = np.random.default_rng(16 + n_tied)
+    B, T, L, k = 1, 2, 30000, 2048
+    say("topk %d ties straddling the cut" % n_tied)
+    s = rng.permutation(L).astype(np.float32)[None, None].repeat(T, 1) / 7.0
+    for t in range(T):
+        order = np.argsort(-s[0, t], kind="stable")
+        v = s[0, t, order[k - 4]]
+        s[0, t, rng.choice(order[k + 500:], n_tied - 1, replace=False)] = v
+    pos = np.array([[L - 1, 25000]], np.int32)
+    _topk_case(dsa, s, pos, k)
+
+
+def test_topk_candidates_beyond_lds(dsa):
+    # 14000 keys share the threshold's top digit: more candidates than the
+    # selection holds in LDS (12288), fewer than the list's capacity (L/8 = 16384)
+    rng = np.random.default_rng(15)
+    B, T, L, n_hot = 1, 3, 131072, 14000
+    say("topk candidate list read from memory")
+    s = (rng.standard_normal((B, T, L)) * 0.1).astype(np.float32)
+    hot = rng.choice(L, n_hot, replace=False)
+    s[0, 0, hot] = (1.0 + 0.2 * rng.random(n_hot)).astype(np.float32)                   # distinct
+    s[0, 1, hot] = (1.0 + rng.integers(0, 16, n_hot) / 128).astype(np.float32)          # ties straddle K*
+    s[0, 2, hot] = 1.125                                                                 # all tied
+    pos = np.array([[L - 1, L - 1, 120000]], np.int32)
     _topk_case(dsa, s, pos, 2048)
 
 
