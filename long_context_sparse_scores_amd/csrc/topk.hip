@@ -24,7 +24,8 @@
 //           second radix select, on the complemented position, or a direct
 //           ranking when there are at most 64 of them); the k kept positions
 //           are compacted into LDS and written out in ascending order from a
-//           bitmap of the row's positions (one chunk of 2^17 at a time).
+//           bitmap of the row's positions (393216 per chunk, in the space the
+//           candidate copy used).
 // The scores are thus read twice (hist, filter), and select never touches
 // them.  (Running select in the last filter workgroup of each row would save
 // a launch, but publishing the candidates across XCDs then takes an L2
@@ -46,7 +47,6 @@ constexpr int kMaxSlices = 512;      // per row
 constexpr int kStage = 256;          // per-wave LDS staging of candidates
 constexpr int kBatch = 32;           // loads in flight per lane in the streaming passes
 constexpr int kSelMax = 2048;        // the kept positions (k <= 2048) are compacted in LDS
-constexpr int kBitWords = 4096;      // position bitmap: 2^17 positions per chunk
 constexpr int kCandLds = 12288;      // candidates the selection holds in LDS
 constexpr int kSelBatch = kCandLds / kSelectThreads;  // loads in flight per thread in its passes
 
@@ -166,16 +166,21 @@ __device__ __forceinline__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, u
     return r;
 }
 
-// LDS of the selection.
+// LDS of the selection.  Once the kept positions are compacted, the candidate
+// copy's space holds the position bitmap and its per-word prefix counts.
 template <int NT>
 struct SelectLds {
-    struct {
-        uint32_t pos[kCandLds], key[kCandLds];
-    } cand;  // copy of the candidate list
+    union {
+        struct {
+            uint32_t pos[kCandLds], key[kCandLds];
+        } cand;  // copy of the candidate list
+        struct {
+            uint32_t bits[kCandLds];  // kCandLds * 32 positions per chunk
+            uint32_t wpre[kCandLds];  // kept positions in the bitmap words before each word
+        } order;
+    };
     uint32_t h[kBins];
     uint32_t sel[kSelMax];
-    uint32_t bits[kBitWords];
-    uint32_t wpre[kBitWords];  // kept positions in the bitmap words before each word
     uint32_t scratch[NT / kWave];
     BinPick pick;
     uint32_t nsel, cut;
@@ -360,39 +365,41 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
         }
     });
     lds_sync();
-    // ascending order, per chunk of 2^17 positions: a bitmap of the kept ones
-    // and the prefix count of its words give every kept position its rank
-    constexpr int kPer = kBitWords / NT;
+    // ascending order, per chunk of kCandLds * 32 positions (the candidate copy
+    // is no longer needed): a bitmap of the kept positions and the prefix count
+    // of its words give every kept position its rank
+    static_assert(kCandLds % NT == 0, "whole bitmap words per thread");
+    constexpr int kPer = kCandLds / NT;
     uint32_t base = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kBitWords * 32) {
-        const int nw = (int)min((int64_t)kBitWords, (n - c0 + 31) / 32);
-        for (int i = threadIdx.x; i < nw; i += NT) s.bits[i] = 0u;
+    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kCandLds * 32) {
+        const int nw = (int)min((int64_t)kCandLds, (n - c0 + 31) / 32);
+        for (int i = threadIdx.x; i < nw; i += NT) s.order.bits[i] = 0u;
         lds_sync();
         for (int j = threadIdx.x; j < k; j += NT) {
             const int64_t p = (int64_t)s.sel[j] - c0;
-            if (p >= 0 && p < (int64_t)nw * 32) atomicOr(&s.bits[p >> 5], 1u << (p & 31));
+            if (p >= 0 && p < (int64_t)nw * 32) atomicOr(&s.order.bits[p >> 5], 1u << (p & 31));
         }
         lds_sync();
         uint32_t wc[kPer], cnt = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int wi = (int)threadIdx.x * kPer + i;
-            wc[i] = wi < nw ? (uint32_t)__popc(s.bits[wi]) : 0u;
+            wc[i] = wi < nw ? (uint32_t)__popc(s.order.bits[wi]) : 0u;
             cnt += wc[i];
         }
         uint32_t total;
         uint32_t o = excl_scan<NT>(cnt, s.scratch, &total);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            s.wpre[threadIdx.x * kPer + i] = o;
+            s.order.wpre[threadIdx.x * kPer + i] = o;
             o += wc[i];
         }
         lds_sync();
         for (int j = threadIdx.x; j < k; j += NT) {
             const int64_t p = (int64_t)s.sel[j] - c0;
             if (p >= 0 && p < (int64_t)nw * 32) {
-                const uint32_t below = s.bits[p >> 5] & ((1u << (p & 31)) - 1u);
-                out[base + s.wpre[p >> 5] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
+                const uint32_t below = s.order.bits[p >> 5] & ((1u << (p & 31)) - 1u);
+                out[base + s.order.wpre[p >> 5] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
             }
         }
         base += total;
