@@ -7,15 +7,17 @@
 // In absorbed form each head's query already lives in that latent space, so
 //   z_j = sm_scale * <q_h, c_j>   (576 dims),   o_h = softmax(z) . c[:, 0:512].
 //
-// Work unit: one query (b,t) and a split of its index list; one 256-thread
-// workgroup per CU.  Selected rows are gathered 32 at a time (36 KiB tiles)
-// straight from HBM into LDS with direct-to-LDS loads (no registers), four
-// tile buffers deep so three tiles are in flight while one is computed.  The
-// tile layout XOR-swizzles 16-byte chunks per row to spread operand reads
-// over the LDS banks.  Wave w owns heads 16w..16w+15:
-//   S^T (32 rows x 16 heads) = K_rows . Q^T   v_mfma_f32_16x16x32_bf16, q in registers
-//   O^T (512 dims x 16 heads) += V^T . P^T    V^T read with ds_read_b64_tr_b16,
-//                                             P^T stays in the S^T registers
+// Work unit: one query (b,t) and a split of its index list; one workgroup per
+// CU.  Selected rows are gathered 32 at a time (36 KiB tiles) straight from
+// HBM into LDS with direct-to-LDS loads (no registers), four tile buffers
+// deep so three tiles are in flight while one is computed.  The tile layout
+// XOR-swizzles 16-byte chunks per row to spread operand reads over the LDS
+// banks.  Per tile, with v_mfma_f32_16x16x32_bf16:
+//   S^T (32 rows x 64 heads) = K_rows . Q^T   q in registers
+//   O^T (512 dims x 64 heads) += V^T . P^T    V^T read with ds_read_b64_tr_b16,
+//                                             P^T (bf16) through LDS
+// The bf16 kernel splits this over eight waves in two roles, two waves per
+// SIMD, so that one wave's softmax runs beside another's P.V (see below).
 // Softmax is online in base 2 with a lazily moved reference maximum: the
 // accumulators are rescaled only when a tile's maximum exceeds the reference
 // by more than 32 (so P < 2^32 and the fp32 sums stay far from overflow);
@@ -164,7 +166,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Work split inside the workgroup (wave w = 2*hh + kk):
+// Work split over four waves w = 2*hh + kk (in the bf16 kernel the score
+// waves take the first two jobs and the value waves the third; in the E4M3
+// kernel each wave does all three):
 //   Q.K^T  wave w computes partial S^T for the 32 heads of head blocks 2hh and
 //          2hh+1 over k-steps 9kk .. 9kk+8 (latent dims 288kk .. +287), q in
 //          registers; partner waves w and w^1 swap the halves of the block the
@@ -309,66 +313,28 @@ __device__ __forceinline__ void apply_rescale(const uint16_t* tv, int c, PvAcc& 
     }
 }
 
-// Q.K^T partial of tile `tq` (this wave's half of the dims, both head blocks of
-// its pair) fused with P.V of tile `tv` (this wave's 128 value dims, all four
-// head blocks): two independent instruction streams, written as four chunks
-// that the compiler is free to interleave (fencing the chunks measured 10 %
-// slower).  When `gp` is active its loads are issued first.
-template <bool PV, bool QK>
-__device__ __forceinline__ void pv_qk(const uint16_t* tv, const uint16_t* tq, const TileAddr& ad,
-                                      const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
-                                      int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const GatherPlan& gp,
-                                      const uint16_t* kvb) {
-    bf16x8_t pbv[4];
-    if (PV) {
+// Q.K^T partial of tile `tq`: this wave's half of the dims, both head blocks of
+// its pair, accumulated into sp[row block][head block of the pair].
+__device__ __forceinline__ void qk_partial(const uint16_t* tq, const TileAddr& ad, const bf16x8_t (&qb)[2][9], int kk,
+                                           f32x4_t (&sp)[2][2]) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
-        apply_rescale(tv, lane & 15, acc);
-    }
-    if (QK) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    // the next tile's gathers go out together before the matrix work (measured
-    // faster than spreading them between matrix instructions)
+    for (int kl = 0; kl < 9; ++kl) {
+        // k-step 9kk + kl: both candidates index the offset table at compile time
+        const int off_lo = ad.qk[kl & 3] + 256 * (kl >> 2);  // kk = 0: always in the main part
+        const int off_hi = kl < 7 ? ad.qk[(kl + 1) & 3] + 256 * ((9 + kl) >> 2) : ad.qt[kl - 7];
+        const int off = kk ? off_hi : off_lo;
+        const int rb1 = (kk && kl >= 7) ? 16 * 128 : 16 * 1024;  // next row block: tail rows are 128 B
+        const char* p = reinterpret_cast<const char*>(tq) + off;
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + rb1);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-        if (PV) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int d = 2 * ch + i;
-                const char* p = reinterpret_cast<const char*>(tv) + ad.tr[d] + 256 * wave;
-                const bf16x4_t lo = lds_read_tr16(p);
-                const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
-                const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
-            }
-        }
-        if (QK) {
-            // local k-steps [k0, k1): 2, 2, 2, 3
-            const int k0 = 2 * ch;
-            const int k1 = ch == 3 ? 9 : 2 * ch + 2;
-#pragma unroll
-            for (int kl = k0; kl < k1; ++kl) {
-                // k-step 9kk + kl: both candidates index the offset table at compile time
-                const int off_lo = ad.qk[kl & 3] + 256 * (kl >> 2);  // kk = 0: always in the main part
-                const int off_hi = kl < 7 ? ad.qk[(kl + 1) & 3] + 256 * ((9 + kl) >> 2) : ad.qt[kl - 7];
-                const int off = kk ? off_hi : off_lo;
-                const int rb1 = (kk && kl >= 7) ? 16 * 128 : 16 * 1024;  // next row block: tail rows are 128 B
-                const char* p = reinterpret_cast<const char*>(tq) + off;
-                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
-                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + rb1);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
-                    sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
-                }
-            }
+        for (int h = 0; h < 2; ++h) {
+            sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
+            sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
         }
     }
 }
@@ -445,16 +411,51 @@ __device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxStat
     if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
 }
 
-// One workgroup (one wave per SIMD) fills a CU's LDS, so the scheduler may use
-// every register to run operand loads ahead.
+// ------------------------------------------------------------------ the bf16 kernel: two roles per SIMD
+// Eight waves, two per SIMD.  Waves 0-3 ("score waves", w = 2hh + kk) do
+// Q.K^T, the partner exchange and the softmax of the work split described
+// above; waves 4-7 ("value waves") issue the gathers and do P.V for value
+// dims 128(w-4) .. +127 of all 64 heads.  Each tile step has two phases
+// between workgroup barriers:
+//   phase 1  score waves: Q.K^T of tile t+1, partials sent to the partner;
+//            value waves: gathers of tile t+kStages-1, tile t's rescale
+//            record applied, its four P^T blocks loaded into registers;
+//   phase 2  score waves: scores and softmax of tile t+1 (P^T and rescale
+//            record to LDS); value waves: P.V of tile t, then the wait for
+//            their loads of tile t+1.
+// So every SIMD runs one wave's softmax (VALU) beside the other's P.V (matrix
+// cores) instead of one after the other (with one wave per SIMD doing all
+// four jobs in turn, the matrix cores sat idle through every softmax; this
+// measured 1.56x faster per prefill layer).  The two roles run separate loops
+// with the same sequence of barriers, so the registers of one (q for the
+// score waves, the accumulators for the value waves) are not held by the
+// other.  The LDS budget is the single-role kernel's: P^T needs one buffer,
+// since the value waves read it before the phase barrier that precedes its
+// next write.
+__device__ __forceinline__ void load_p(const bf16x8_t* __restrict__ pl, int lane, bf16x8_t (&pbv)[4]) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
+}
+
+// P.V of tile tv for value dims 128 vw .. +127 of all four head blocks.
+__device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, const bf16x8_t (&pbv)[4], int vw,
+                                        PvAcc& acc) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const char* p = reinterpret_cast<const char*>(tv) + ad.tr[d] + 256 * vw;
+        const bf16x4_t lo = lds_read_tr16(p);
+        const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
+        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+    }
+}
+
 template <bool DIRECT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_mla_kernel(
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    // Blocks are numbered so that every split of query bt lands on XCD bt % 8
-    // (consecutive block ids go to consecutive XCDs): the splits' partials and
-    // the combine that reads them share one L2.
     const int grp = blockIdx.x / (kXcds * nsplit);
     const int rem = blockIdx.x % (kXcds * nsplit);
     const int split = rem / kXcds;
@@ -462,9 +463,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (bt >= rows) return;
     const int b = bt / T;
     const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: keeps role selects scalar
-    const int kk = wave & 1;   // contraction half for Q.K^T
-    const int hh = wave >> 1;  // head pair for Q.K^T
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool score = wave < kWaves;
     const int c = lane & 15;
     const int g = lane >> 4;
     const int j0 = split * rows_per_split;
@@ -477,100 +477,140 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
     __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
     __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
-
-    // B operands of S^T: q[head 16*(2hh+h) + c][32*(9kk+kl) + 8g .. +7], loaded
-    // while the row list is fetched so that the two latencies overlap.
-    bf16x8_t qb[2][9];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
-    }
-    const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
-    // Consume q here so the compiler's own wait for these loads (it cannot see the
-    // gathers, which are issued from asm) stays ahead of the first gather.
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
-    __syncthreads();  // rows_lds ready
-
-    const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
-    const TileAddr ad = tile_addr(lane);
     auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
-        const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
+    const TileAddr ad = tile_addr(lane);
+    float* stats = reinterpret_cast<float*>(sx);  // epilogue: [0, 64) sums, [64, 128) maxima
+    char* st8 = reinterpret_cast<char*>(tiles);   // epilogue: output rows staged, kStageRow bytes apart
+
+    const int32_t* sel = idx + (int64_t)bt * k + j0;
+    if (score) {
+        // ---------------- score waves: w = 2hh + kk as in the single-role kernel
+        const int sw = wave, kk = sw & 1, hh = sw >> 1;
+        bf16x8_t qb[2][9];
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
-    }
-
-    PvAcc acc;
+        for (int h = 0; h < 2; ++h) {
+            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+            for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+        }
+        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
+        __syncthreads();  // rows_lds ready
+        SoftmaxState st;
+        st.m_ref = -INFINITY;
+        st.lsum = 0.0f;
+        auto scores_of = [&](int t) {  // Q.K^T of tile t, exchange, softmax; P^T and rescale record to LDS
+            f32x4_t sp[2][2];
+            qk_partial(buf(t), ad, qb, kk, sp);
+            send_partial(sp, sx, sw, kk, lane);
+            lds_barrier();  // partials exchanged (phase 1 -> 2)
+            f32x4_t s[2];
+            own_scores(sp, sx, sw, kk, lane, s);
+            float factor;
+            bool moved;
+            const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
+            pl[sw * kWave + lane] = pb;
+            char* tail = reinterpret_cast<char*>(buf(t));
+            if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * sw + c] = factor;
+            if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[sw] = moved ? 1u : 0u;
+        };
+        lds_barrier();  // tile 0 in LDS
+        scores_of(0);
+        for (int t = 0; t + 1 < ntiles; ++t) {
+            lds_barrier();  // tile t+1 in LDS; the value waves hold P^T of tile t
+            scores_of(t + 1);
+        }
+        lds_barrier();  // P^T and rescale record of the last tile visible
+        // epilogue: denominators and maxima of head block sw
+        float lsum = st.lsum;
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        if (g == 0) {
+            stats[16 * sw + c] = lsum;
+            stats[64 + 16 * sw + c] = st.m_ref;
+        }
+        lds_barrier();  // stats visible
+        lds_barrier();  // output rows staged
+        const int head = 16 * sw + c;
+        if (g == 0) {
+            if (DIRECT) {
+                if (lse) lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (st.m_ref + log2f(lsum)) * 0.69314718055994531f
+                                                                      : -INFINITY;
+            } else {
+                part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY;
+            }
+        }
+    } else {
+        // ---------------- value waves
+        const int vw = wave - kWaves;
+        const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
+        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
+        __syncthreads();  // rows_lds ready
+        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
+            const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), vw, lane);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState st;
-    st.m_ref = -INFINITY;
-    st.lsum = 0.0f;
-    GatherPlan no_gather;
-    no_gather.active = false;
-
-    // softmax of tile t from the exchanged partials, P^T and rescale record to LDS
-    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
-        f32x4_t s[2];
-        own_scores(sp, sx, wave, kk, lane, s);
-        float factor;
-        bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
-        pl[wave * kWave + lane] = pb;
-        char* tail = reinterpret_cast<char*>(buf(t));
-        if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * wave + c] = factor;
-        if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[wave] = moved ? 1u : 0u;
-    };
-
-    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
-    {
-        const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
-        if (later >= 2) wait_vmem<2 * kLoads>();
-        else if (later == 1) wait_vmem<kLoads>();
-        else wait_vmem<0>();
-        static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
+            for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
+        }
+        PvAcc acc;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
+            if (later >= 2) wait_vmem<2 * kLoads>();
+            else if (later == 1) wait_vmem<kLoads>();
+            else wait_vmem<0>();
+            static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
+        }
+        lds_barrier();  // tile 0 in LDS
+        lds_barrier();  // (score waves: partials of tile 0 exchanged)
+        bf16x8_t pbv[4];
+        for (int t = 0; t + 1 < ntiles; ++t) {
+            // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
+            const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
+            if (later >= 1) wait_vmem<kLoads>();
+            else wait_vmem<0>();
+            lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
+            if (t + kStages - 1 < ntiles) {
+                const GatherPlan gp = plan_gather(kvb, rows_lds, t + kStages - 1, nrows, L, buf(t + kStages - 1), vw,
+                                                  lane);
+#pragma unroll
+                for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
+            }
+            apply_rescale(buf(t), c, acc);
+            load_p(pl, lane, pbv);
+            lds_barrier();  // (phase 1 -> 2) P^T of tile t is in registers; the score waves may overwrite it
+            pv_tile(buf(t), ad, pbv, vw, acc);
+        }
+        lds_barrier();  // P^T and rescale record of the last tile visible
+        apply_rescale(buf(ntiles - 1), c, acc);
+        load_p(pl, lane, pbv);
+        pv_tile(buf(ntiles - 1), ad, pbv, vw, acc);
+        lds_barrier();  // stats visible; every value wave is done reading the tiles
+        float inv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const float ls = stats[16 * hb + c];
+            inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
+        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const f32x4_t& o = acc.o[d][hb];
+                *reinterpret_cast<uint2*>(st8 + (16 * hb + c) * kStageRow + 2 * (128 * vw + 16 * d + 4 * g)) =
+                    make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
+            }
+        lds_barrier();  // output rows staged
     }
-    lds_barrier();
-    {
-        f32x4_t sp[2][2];
-        pv_qk<false, true>(buf(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();
-        finish_scores(0, sp);
+    // every wave stores 8 of the 64 head rows, one 16-byte store per lane per row
+    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int h = 8 * wave + i;
+        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
+            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
     }
-    // Iteration t: P.V of tile t alongside Q.K^T of tile t+1 (and the gather of
-    // tile t+3), then the exchange and softmax of tile t+1.
-    // Buffers: t and t+1 are being read, t+2 is in flight, t+3 is issued during the compute.
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
-        const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
-        if (later >= 1) wait_vmem<kLoads>();
-        else wait_vmem<0>();
-        lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer (t+3) % 4 free
-        GatherPlan gp = plan_gather(kvb, rows_lds, min(t + kStages - 1, ntiles - 1), nrows, L, buf(t + kStages - 1),
-                                    wave, lane);
-        gp.active = t + kStages - 1 < ntiles;
-        f32x4_t sp[2][2];
-        pv_qk<true, true>(buf(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp, kvb);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();  // partials exchanged; every wave is done reading P^T of tile t
-        finish_scores(t + 1, sp);
-    }
-    lds_barrier();  // P^T and rescale record of the last tile visible
-    {
-        f32x4_t sp[2][2];
-        pv_qk<true, false>(buf(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp, no_gather, kvb);
-    }
-
-    store_output<DIRECT>(acc, st, sx, tiles, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
 }
 
 // ------------------------------------------------------------------ E4M3 latent rows
@@ -719,7 +759,8 @@ __device__ __forceinline__ void apply_rescale8(const Rescale8& rs, int c, PvAcc&
     }
 }
 
-// As pv_qk, reading E4M3 tiles: P.V of tile `tv` (record `rv`) and Q.K^T of tile `tq`.
+// One wave per SIMD, reading E4M3 tiles: P.V of tile `tv` (record `rv`, this wave's 128 value dims,
+// all four head blocks) fused with the Q.K^T partial of tile `tq` (this wave's half of the dims).
 template <bool PV, bool QK>
 __device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, const uint8_t* tq, const TileAddr8& ad,
                                        const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
@@ -983,15 +1024,15 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(kThreads), 0, stream, q, kv,
+        hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q, kv,
                            kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q, kv,
-                       kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q,
+                       kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
                        nullptr, nullptr);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
                        part_lse, rows, p.nsplit, out, lse);
