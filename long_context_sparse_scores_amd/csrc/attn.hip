@@ -91,22 +91,24 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 
 // Gather of tile t (rows t*32 .. t*32+31 of this split) into LDS at `tile`.
-// Wave w loads the main KiB of rows 8w .. 8w+7 (one load per row: the row index
-// is wave-uniform, so the address is a scalar base plus this lane's swizzled
-// offset) and the tails of the same 8 rows (one load).  Masked or missing rows
-// read row 0 (finite values) and get P = 0.  The plan is computed once and its
-// nine loads are issued together at the start of the tile's matrix work.
+// Wave w loads the main KiB of rows 8w .. 8w+7 (one load per row: lane l
+// brings the row's 16-byte chunk l ^ (r & 15), which lands at tile byte
+// 1024 r + 16 l) and the tails of the same 8 rows (one load).  Every lane
+// holds its own source addresses, so making the plan is vector arithmetic on
+// the row indices with no scalar dependency chain; only the LDS destinations
+// are wave-uniform, and they do not depend on the row list.  rows_lds holds -1
+// for every masked or missing entry (canonicalised when the list is loaded), so
+// such rows read row 0 (finite values) and get P = 0.
 struct GatherPlan {
-    const uint16_t* row[8];  // wave-uniform row bases
+    const uint16_t* src[8];  // this lane's chunk of the main part of row 8w+i
     uint32_t lds[8];         // wave-uniform LDS byte addresses of the rows' main parts
-    uint32_t tail_off;       // this lane's 16-byte tail chunk: element offset from kvb
+    const uint16_t* tail;    // this lane's 16-byte tail chunk
     uint32_t lds_tail;
-    int xr;                  // (8w) & 15: row r = 8w + i has r & 15 == xr + i
     bool active;             // wave-uniform: false when there is no tile left to gather
 };
 
 __device__ __forceinline__ GatherPlan plan_gather(const uint16_t* __restrict__ kvb, const int* __restrict__ rows_lds,
-                                                  int t, int nrows, int L, const uint16_t* tile, int wave, int lane) {
+                                                  int t, const uint16_t* tile, int wave, int lane) {
     GatherPlan gp;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
     const int r0 = 8 * wave;
@@ -116,33 +118,25 @@ __device__ __forceinline__ GatherPlan plan_gather(const uint16_t* __restrict__ k
     const int rows8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int j = t * kRows + r0 + i;
-        int rid = j < nrows ? rows8[i] : 0;
-        rid = __builtin_amdgcn_readfirstlane((rid >= 0 && rid < L) ? rid : 0);
-        gp.row[i] = kvb + (int64_t)rid * kDqk;
-        gp.lds[i] = __builtin_amdgcn_readfirstlane(base + 1024u * (r0 + i));
+        const uint32_t rid = (uint32_t)max(rows8[i], 0);
+        gp.src[i] = kvb + rid * kDqk + 8 * (lane ^ ((r0 + i) & 15));  // fits: L <= 2^22 rows
+        gp.lds[i] = base + 1024u * (r0 + i);
     }
     {
         const int r = r0 + (lane >> 3);
-        const int j = t * kRows + r;
-        int rid = j < nrows ? rows_lds[j] : 0;
-        rid = (rid >= 0 && rid < L) ? rid : 0;
+        const uint32_t rid = (uint32_t)max(rows_lds[t * kRows + r], 0);
         const int c = 64 + ((lane & 7) ^ (r & 7));
-        gp.tail_off = (uint32_t)rid * kDqk + 8 * c;  // fits: L <= 2^22 rows is checked at the boundary
-        gp.lds_tail = __builtin_amdgcn_readfirstlane(base + kMainBytes + 1024u * wave);
+        gp.tail = kvb + rid * kDqk + 8 * c;
+        gp.lds_tail = base + kMainBytes + 1024u * wave;
     }
-    gp.xr = r0 & 15;
     gp.active = true;
     return gp;
 }
 
 // Load i of the plan: i < 8 the main part of row 8w+i, i == 8 the tails.
-__device__ __forceinline__ void issue_gather(const GatherPlan& gp, const uint16_t* kvb, int i, int lane) {
+__device__ __forceinline__ void issue_gather(const GatherPlan& gp, int i) {
     if (!gp.active) return;
-    if (i < 8)
-        lds_dma16_sbase(gp.row[i], (uint32_t)((lane ^ (gp.xr + i)) << 4), gp.lds[i]);
-    else
-        lds_dma16(kvb + gp.tail_off, gp.lds_tail);
+    lds_dma16(i < 8 ? gp.src[i] : gp.tail, i < 8 ? gp.lds[i] : gp.lds_tail);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -229,24 +223,22 @@ constexpr int kFlagOffset = kMainBytes + 4 * 16 * 4;
 // maximum and denominator share; when the reference moves, records the factor
 // the P.V accumulators of these heads must be scaled by.  Returns P^T (k-slot
 // 8g+e holds row e<4 ? 4g+e : 16+4g+e-4) in bf16.
-__device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, float scale_log2,
+__device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, bool full, float scale_log2,
                                                  SoftmaxState& st, float& factor, bool& moved) {
     float x[8];
-    bool over = false;
+    if (full) {  // wave-uniform: every row of the tile is visible
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float v = ((valid >> e) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
-        x[e] = v;
-        over |= v > st.m_ref + kRescaleSlack;
+        for (int e = 0; e < 8; ++e) x[e] = s[e >> 2][e & 3] * scale_log2;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ((valid >> e) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
     }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     factor = 1.0f;
     moved = false;
-    // The exact tile maximum is only needed when the reference has to move
-    // (the first tile with a visible row, or a jump beyond the slack).
-    if (__ballot(over)) {
-        float mx = x[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    // The tile maximum over all lanes is only needed when the reference has to
+    // move (the first tile with a visible row, or a jump beyond the slack).
+    if (__ballot(mx > st.m_ref + kRescaleSlack)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         const float m_new = fmaxf(st.m_ref, mx);
@@ -262,11 +254,13 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
     }
     const float mu = (st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
     u32x4_t pw;
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         // v_exp_f32 directly: arguments are <= 32 here and results below 2^-126 may flush to 0
         const uint32_t h2 = pack_bf16x2(__builtin_amdgcn_exp2f(x[e] - mu), __builtin_amdgcn_exp2f(x[e + 1] - mu));
-        st.lsum += __uint_as_float(h2 << 16) + __uint_as_float(h2 & 0xFFFF0000u);  // the bf16 values P uses
+        // the denominator sums the bf16 values P uses: one v_dot2 with (1, 1) per pair
+        st.lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h2), ones, st.lsum, false);
         pw[e / 2] = h2;
     }
     return __builtin_bit_cast(bf16x8_t, pw);
@@ -484,12 +478,14 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     const int32_t* sel = idx + (int64_t)bt * k + j0;
     if (score) {
-        // ---------------- score waves: w = 2hh + kk as in the single-role kernel
-        const int sw = wave, kk = sw & 1, hh = sw >> 1;
+        // ---------------- score waves, w = 2hh + kk.  qb[0] holds the wave's own
+        // head block w, qb[1] the partner's block w ^ 1, so the partial to keep
+        // and the partial to send need no selects.
+        const int sw = wave, kk = sw & 1;
         bf16x8_t qb[2][9];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
+            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (sw ^ h) + c) * kDqk + 8 * g + 32 * 9 * kk;
 #pragma unroll
             for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
         }
@@ -501,13 +497,19 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         auto scores_of = [&](int t) {  // Q.K^T of tile t, exchange, softmax; P^T and rescale record to LDS
             f32x4_t sp[2][2];
             qk_partial(buf(t), ad, qb, kk, sp);
-            send_partial(sp, sx, sw, kk, lane);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) sx[((sw ^ 1) * 2 + rb) * kWave + lane] = sp[rb][1];
+            // the tile's visible rows: one LDS read and a ballot give a wave-uniform mask
+            const uint32_t tmask = (uint32_t)__ballot(rows_lds[t * kRows + (lane & 31)] >= 0);
             lds_barrier();  // partials exchanged (phase 1 -> 2)
             f32x4_t s[2];
-            own_scores(sp, sx, sw, kk, lane, s);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) s[rb] = sp[rb][0] + sx[(sw * 2 + rb) * kWave + lane];
+            // value e of this lane is row e < 4 ? 4g + e : 16 + 4g + e - 4
+            const uint32_t valid = ((tmask >> (4 * g)) & 0xFu) | (((tmask >> (16 + 4 * g)) & 0xFu) << 4);
             float factor;
             bool moved;
-            const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
+            const bf16x8_t pb = softmax_tile(s, valid, tmask == 0xFFFFFFFFu, scale_log2, st, factor, moved);
             pl[sw * kWave + lane] = pb;
             char* tail = reinterpret_cast<char*>(buf(t));
             if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * sw + c] = factor;
@@ -546,9 +548,9 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
         __syncthreads();  // rows_lds ready
         for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
-            const GatherPlan gp = plan_gather(kvb, rows_lds, t, nrows, L, buf(t), vw, lane);
+            const GatherPlan gp = plan_gather(kvb, rows_lds, t, buf(t), vw, lane);
 #pragma unroll
-            for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
+            for (int i = 0; i < kLoads; ++i) issue_gather(gp, i);
         }
         PvAcc acc;
 #pragma unroll
@@ -562,6 +564,10 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
             else wait_vmem<0>();
             static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
         }
+        // The plan of each in-loop gather (row addresses from rows_lds) is made one
+        // iteration ahead, beside the P.V work, so phase 1 only issues the loads.
+        GatherPlan next = plan_gather(kvb, rows_lds, min(kStages - 1, ntiles - 1), buf(kStages - 1), vw, lane);
+        next.active = kStages - 1 < ntiles;
         lds_barrier();  // tile 0 in LDS
         lds_barrier();  // (score waves: partials of tile 0 exchanged)
         bf16x8_t pbv[4];
@@ -571,16 +577,16 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (later >= 1) wait_vmem<kLoads>();
             else wait_vmem<0>();
             lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
-            if (t + kStages - 1 < ntiles) {
-                const GatherPlan gp = plan_gather(kvb, rows_lds, t + kStages - 1, nrows, L, buf(t + kStages - 1), vw,
-                                                  lane);
 #pragma unroll
-                for (int i = 0; i < kLoads; ++i) issue_gather(gp, kvb, i, lane);
-            }
+            for (int i = 0; i < kLoads; ++i) issue_gather(next, i);  // tile t + kStages - 1
             apply_rescale(buf(t), c, acc);
             load_p(pl, lane, pbv);
             lds_barrier();  // (phase 1 -> 2) P^T of tile t is in registers; the score waves may overwrite it
+            // tile t + kStages goes to this tile's buffer, next iteration, after this P.V and a barrier
+            GatherPlan nx = plan_gather(kvb, rows_lds, min(t + kStages, ntiles - 1), buf(t), vw, lane);
+            nx.active = t + kStages < ntiles;
             pv_tile(buf(t), ad, pbv, vw, acc);
+            next = nx;
         }
         lds_barrier();  // P^T and rescale record of the last tile visible
         apply_rescale(buf(ntiles - 1), c, acc);
@@ -884,7 +890,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         own_scores(sp, sx, wave, kk, lane, s);
         float factor;
         bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), scale_log2, st, factor, moved);
+        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), false, scale_log2, st, factor, moved);
         pl[wave * kWave + lane] = pb;
         if (g == 0) rec(t).fac[16 * wave + c] = factor;
         if (lane == 0) rec(t).flag[wave] = moved ? 1u : 0u;
