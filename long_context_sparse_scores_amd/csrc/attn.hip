@@ -27,10 +27,13 @@
 // list fits one split is normalised and written directly.
 //
 // E4M3 latent rows ([CTXFR, "Entraînement par renforcement de l'agent
-// intelligent"] names an FP8 KV cache) take a kernel of their own below: with
-// 576-byte rows the LDS holds a ring of seven 18 KiB tiles, twice the rows in
-// flight, and every operand is widened exactly to bf16 in registers as it is
-// read, so the matrix cores compute as in the bf16 kernel.
+// intelligent"] names an FP8 KV cache) run through the same kernel
+// (template parameter FP8): with 576-byte rows the LDS holds a ring of seven
+// 18 KiB tiles, twice the rows in flight, and every operand is widened
+// exactly to bf16 in registers as it is read, so the matrix cores compute as
+// for bf16 rows.
+#include <type_traits>
+
 #include "common.h"
 
 namespace dsa {
@@ -208,10 +211,6 @@ __device__ __forceinline__ TileAddr tile_addr(int lane) {
     return a;
 }
 
-__device__ __forceinline__ int qk_offset(const TileAddr& ad, int ks) {
-    return ks < 16 ? ad.qk[ks & 3] + 256 * (ks >> 2) : ad.qt[ks - 16];
-}
-
 // Rescale factors of a tile's softmax live in that tile's K-tail region once
 // Q.K^T has read it: float fac[4][16] (per head block, per head), then uint32
 // flag[4] (block hb moved its reference).  P.V of the same tile reads them.
@@ -266,19 +265,6 @@ __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t
     return __builtin_bit_cast(bf16x8_t, pw);
 }
 
-// Bits e of this lane's values (rows (e>>2)*16 + 4g + (e&3) of tile t) that are visible.
-// rows_lds holds -1 for every masked or missing entry (canonicalised when the
-// list is loaded), so visibility is the sign bit.
-__device__ __forceinline__ uint32_t valid_bits(const int* rows_lds, int t, int g) {
-    const int4 ra = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 4 * g);
-    const int4 rb = *reinterpret_cast<const int4*>(rows_lds + t * kRows + 16 + 4 * g);
-    const int r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-    uint32_t v = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v |= ((uint32_t)~r8[e] >> 31) << e;
-    return v;
-}
-
 // Entry j of a split's row list as kept in LDS: the row, or -1 when it is
 // missing (j >= nrows) or masked (outside [0, L)).
 __device__ __forceinline__ int list_entry(const int32_t* sel, int j, int nrows, int L) {
@@ -331,20 +317,6 @@ __device__ __forceinline__ void qk_partial(const uint16_t* tq, const TileAddr& a
             sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
         }
     }
-}
-
-// Partner exchange of the Q.K^T partials: this wave keeps the half of head block
-// w and sends the half of head block w^1; afterwards s holds S^T of head block w.
-__device__ __forceinline__ void send_partial(const f32x4_t (&sp)[2][2], f32x4_t* sx, int wave, int kk, int lane) {
-    // sp[.][h] covers head block 2hh + h; the partner owns block 2hh + (1 - kk)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) sx[((wave ^ 1) * 2 + rb) * kWave + lane] = kk ? sp[rb][0] : sp[rb][1];
-}
-
-__device__ __forceinline__ void own_scores(const f32x4_t (&sp)[2][2], const f32x4_t* sx, int wave, int kk, int lane,
-                                           f32x4_t (&s)[2]) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) s[rb] = (kk ? sp[rb][1] : sp[rb][0]) + sx[(wave * 2 + rb) * kWave + lane];
 }
 
 // Epilogue of both kernels: denominators (and reference maxima) of all 64
@@ -405,27 +377,7 @@ __device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxStat
     if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
 }
 
-// ------------------------------------------------------------------ the bf16 kernel: two roles per SIMD
-// Eight waves, two per SIMD.  Waves 0-3 ("score waves", w = 2hh + kk) do
-// Q.K^T, the partner exchange and the softmax of the work split described
-// above; waves 4-7 ("value waves") issue the gathers and do P.V for value
-// dims 128(w-4) .. +127 of all 64 heads.  Each tile step has two phases
-// between workgroup barriers:
-//   phase 1  score waves: Q.K^T of tile t+1, partials sent to the partner;
-//            value waves: gathers of tile t+kStages-1, tile t's rescale
-//            record applied, its four P^T blocks loaded into registers;
-//   phase 2  score waves: scores and softmax of tile t+1 (P^T and rescale
-//            record to LDS); value waves: P.V of tile t, then the wait for
-//            their loads of tile t+1.
-// So every SIMD runs one wave's softmax (VALU) beside the other's P.V (matrix
-// cores) instead of one after the other (with one wave per SIMD doing all
-// four jobs in turn, the matrix cores sat idle through every softmax; this
-// measured 1.56x faster per prefill layer).  The two roles run separate loops
-// with the same sequence of barriers, so the registers of one (q for the
-// score waves, the accumulators for the value waves) are not held by the
-// other.  The LDS budget is the single-role kernel's: P^T needs one buffer,
-// since the value waves read it before the phase barrier that precedes its
-// next write.
+// ------------------------------------------------------------------ P.V helpers of the bf16 tiles
 __device__ __forceinline__ void load_p(const bf16x8_t* __restrict__ pl, int lane, bf16x8_t (&pbv)[4]) {
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
@@ -445,187 +397,13 @@ __device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, 
     }
 }
 
-template <bool DIRECT>
-__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t kv_bstride,
-    const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int grp = blockIdx.x / (kXcds * nsplit);
-    const int rem = blockIdx.x % (kXcds * nsplit);
-    const int split = rem / kXcds;
-    const int bt = grp * kXcds + rem % kXcds;
-    if (bt >= rows) return;
-    const int b = bt / T;
-    const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const bool score = wave < kWaves;
-    const int c = lane & 15;
-    const int g = lane >> 4;
-    const int j0 = split * rows_per_split;
-    const int nrows = min(k, j0 + rows_per_split) - j0;
-    const int ntiles = (nrows + kRows - 1) / kRows;
-
-    constexpr int kStages = Cfg<DIRECT>::kStages;
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[kStages * kTileChunks * 8];
-    static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile buffers");
-    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
-    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
-    __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
-    auto buf = [&](int t) { return tiles + (t % kStages) * (kTileChunks * 8); };
-    const TileAddr ad = tile_addr(lane);
-    float* stats = reinterpret_cast<float*>(sx);  // epilogue: [0, 64) sums, [64, 128) maxima
-    char* st8 = reinterpret_cast<char*>(tiles);   // epilogue: output rows staged, kStageRow bytes apart
-
-    const int32_t* sel = idx + (int64_t)bt * k + j0;
-    if (score) {
-        // ---------------- score waves, w = 2hh + kk.  qb[0] holds the wave's own
-        // head block w, qb[1] the partner's block w ^ 1, so the partial to keep
-        // and the partial to send need no selects.
-        const int sw = wave, kk = sw & 1;
-        bf16x8_t qb[2][9];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (sw ^ h) + c) * kDqk + 8 * g + 32 * 9 * kk;
-#pragma unroll
-            for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
-        }
-        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
-        __syncthreads();  // rows_lds ready
-        SoftmaxState st;
-        st.m_ref = -INFINITY;
-        st.lsum = 0.0f;
-        auto scores_of = [&](int t) {  // Q.K^T of tile t, exchange, softmax; P^T and rescale record to LDS
-            f32x4_t sp[2][2];
-            qk_partial(buf(t), ad, qb, kk, sp);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sx[((sw ^ 1) * 2 + rb) * kWave + lane] = sp[rb][1];
-            // the tile's visible rows: one LDS read and a ballot give a wave-uniform mask
-            const uint32_t tmask = (uint32_t)__ballot(rows_lds[t * kRows + (lane & 31)] >= 0);
-            lds_barrier();  // partials exchanged (phase 1 -> 2)
-            f32x4_t s[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) s[rb] = sp[rb][0] + sx[(sw * 2 + rb) * kWave + lane];
-            // value e of this lane is row e < 4 ? 4g + e : 16 + 4g + e - 4
-            const uint32_t valid = ((tmask >> (4 * g)) & 0xFu) | (((tmask >> (16 + 4 * g)) & 0xFu) << 4);
-            float factor;
-            bool moved;
-            const bf16x8_t pb = softmax_tile(s, valid, tmask == 0xFFFFFFFFu, scale_log2, st, factor, moved);
-            pl[sw * kWave + lane] = pb;
-            char* tail = reinterpret_cast<char*>(buf(t));
-            if (g == 0) reinterpret_cast<float*>(tail + kFacOffset)[16 * sw + c] = factor;
-            if (lane == 0) reinterpret_cast<uint32_t*>(tail + kFlagOffset)[sw] = moved ? 1u : 0u;
-        };
-        lds_barrier();  // tile 0 in LDS
-        scores_of(0);
-        for (int t = 0; t + 1 < ntiles; ++t) {
-            lds_barrier();  // tile t+1 in LDS; the value waves hold P^T of tile t
-            scores_of(t + 1);
-        }
-        lds_barrier();  // P^T and rescale record of the last tile visible
-        // epilogue: denominators and maxima of head block sw
-        float lsum = st.lsum;
-        lsum += __shfl_xor(lsum, 16, kWave);
-        lsum += __shfl_xor(lsum, 32, kWave);
-        if (g == 0) {
-            stats[16 * sw + c] = lsum;
-            stats[64 + 16 * sw + c] = st.m_ref;
-        }
-        lds_barrier();  // stats visible
-        lds_barrier();  // output rows staged
-        const int head = 16 * sw + c;
-        if (g == 0) {
-            if (DIRECT) {
-                if (lse) lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (st.m_ref + log2f(lsum)) * 0.69314718055994531f
-                                                                      : -INFINITY;
-            } else {
-                part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY;
-            }
-        }
-    } else {
-        // ---------------- value waves
-        const int vw = wave - kWaves;
-        const uint16_t* kvb = kv + (int64_t)b * kv_bstride;
-        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
-        __syncthreads();  // rows_lds ready
-        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
-            const GatherPlan gp = plan_gather(kvb, rows_lds, t, buf(t), vw, lane);
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) issue_gather(gp, i);
-        }
-        PvAcc acc;
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        {
-            const int later = min(ntiles - 1, kStages - 2);  // tiles issued after tile 0
-            if (later >= 2) wait_vmem<2 * kLoads>();
-            else if (later == 1) wait_vmem<kLoads>();
-            else wait_vmem<0>();
-            static_assert(kStages <= 4, "wait counts cover at most two tiles issued after tile 0");
-        }
-        // The plan of each in-loop gather (row addresses from rows_lds) is made one
-        // iteration ahead, beside the P.V work, so phase 1 only issues the loads.
-        GatherPlan next = plan_gather(kvb, rows_lds, min(kStages - 1, ntiles - 1), buf(kStages - 1), vw, lane);
-        next.active = kStages - 1 < ntiles;
-        lds_barrier();  // tile 0 in LDS
-        lds_barrier();  // (score waves: partials of tile 0 exchanged)
-        bf16x8_t pbv[4];
-        for (int t = 0; t + 1 < ntiles; ++t) {
-            // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
-            const int later = min(ntiles - 1, t + kStages - 2) - (t + 1);
-            if (later >= 1) wait_vmem<kLoads>();
-            else wait_vmem<0>();
-            lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) issue_gather(next, i);  // tile t + kStages - 1
-            apply_rescale(buf(t), c, acc);
-            load_p(pl, lane, pbv);
-            lds_barrier();  // (phase 1 -> 2) P^T of tile t is in registers; the score waves may overwrite it
-            // tile t + kStages goes to this tile's buffer, next iteration, after this P.V and a barrier
-            GatherPlan nx = plan_gather(kvb, rows_lds, min(t + kStages, ntiles - 1), buf(t), vw, lane);
-            nx.active = t + kStages < ntiles;
-            pv_tile(buf(t), ad, pbv, vw, acc);
-            next = nx;
-        }
-        lds_barrier();  // P^T and rescale record of the last tile visible
-        apply_rescale(buf(ntiles - 1), c, acc);
-        load_p(pl, lane, pbv);
-        pv_tile(buf(ntiles - 1), ad, pbv, vw, acc);
-        lds_barrier();  // stats visible; every value wave is done reading the tiles
-        float inv[4];
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-            const float ls = stats[16 * hb + c];
-            inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
-        }
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const f32x4_t& o = acc.o[d][hb];
-                *reinterpret_cast<uint2*>(st8 + (16 * hb + c) * kStageRow + 2 * (128 * vw + 16 * d + 4 * g)) =
-                    make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
-            }
-        lds_barrier();  // output rows staged
-    }
-    // every wave stores 8 of the 64 head rows, one 16-byte store per lane per row
-    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int h = 8 * wave + i;
-        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
-            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
-    }
-}
-
 // ------------------------------------------------------------------ E4M3 latent rows
 // A 32-row tile of 576-byte E4M3 rows is 18 KiB, so the LDS holds a ring of
 // seven: six tiles in flight while one is read, twice the rows in flight of
-// the bf16 kernel (whose gathers are limited by rows in flight, not bytes).
-// The work split, softmax and combine are the bf16 kernel's; only the operand
-// reads differ, each widened exactly to bf16 in registers (v_cvt_pk_f32_fp8;
-// the upper halves of the fp32 results are the bf16 values):
+// the bf16 tiles.  The work split, softmax and combine are the same; only the
+// gathers and the operand reads differ, each operand widened exactly to bf16
+// in registers (v_cvt_pk_f32_fp8; the upper halves of the fp32 results are the
+// bf16 values):
 //   Q.K^T  A operand, 8 dims of a row: one ds_read_b64;
 //   P.V    A operand, 8 rows of one dim: one ds_read_b64_tr_b8 (in each
 //          16-lane group, lane 8q + r receives byte r of the 8-byte chunks
@@ -654,8 +432,7 @@ struct GatherPlan8 {
 };
 
 __device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ kvb, const int* __restrict__ rows_lds,
-                                                    int t, int nrows, int L, const uint8_t* tile, int wave,
-                                                    int lane) {
+                                                    int t, const uint8_t* tile, int wave, int lane) {
     GatherPlan8 gp;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(tile));
     gp.base = kvb;
@@ -665,18 +442,17 @@ __device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ 
         const int n = wave + 4 * i;                 // < 18 for the loads this wave issues
         const int slot = 64 * n + lane;
         const int r = min(slot / kChunks8, kRows - 1);
-        const int j = t * kRows + r;
-        int rid = j < nrows ? rows_lds[j] : 0;
-        rid = (rid >= 0 && rid < L) ? rid : 0;      // masked or missing rows read row 0 (finite values, P = 0)
+        // rows_lds holds -1 for masked or missing rows: they read row 0 (finite values, P = 0)
+        const uint32_t rid = (uint32_t)max(rows_lds[t * kRows + r], 0);
         const int s = (slot - kChunks8 * r) ^ swz8(r);
-        gp.off[i] = slot < kRows * kChunks8 ? (uint32_t)rid * kRow8 + 16u * (uint32_t)s : 0u;  // L <= 2^22 rows
+        gp.off[i] = slot < kRows * kChunks8 ? rid * kRow8 + 16u * (uint32_t)s : 0u;  // L <= 2^22 rows
         gp.lds[i] = __builtin_amdgcn_readfirstlane(base + 1024u * n);
     }
     gp.active = true;
     return gp;
 }
 
-__device__ __forceinline__ void issue_gather(const GatherPlan8& gp, const void*, int i, int) {
+__device__ __forceinline__ void issue_gather(const GatherPlan8& gp, int i) {
     if (!gp.active || i >= gp.nload) return;
     lds_dma16_sbase(gp.base, gp.off[i], gp.lds[i]);
 }
@@ -765,63 +541,91 @@ __device__ __forceinline__ void apply_rescale8(const Rescale8& rs, int c, PvAcc&
     }
 }
 
-// One wave per SIMD, reading E4M3 tiles: P.V of tile `tv` (record `rv`, this wave's 128 value dims,
-// all four head blocks) fused with the Q.K^T partial of tile `tq` (this wave's half of the dims).
-template <bool PV, bool QK>
-__device__ __forceinline__ void pv_qk8(const uint8_t* tv, const Rescale8& rv, const uint8_t* tq, const TileAddr8& ad,
-                                       const bf16x8_t* __restrict__ pl, const bf16x8_t (&qb)[2][9], int kk, int wave,
-                                       int lane, PvAcc& acc, f32x4_t (&sp)[2][2], const GatherPlan8& gp) {
-    const int g = lane >> 4;
-    bf16x8_t pbv[4];
-    if (PV) {
+// Q.K^T partial of E4M3 tile `tq`: this wave's half of the dims, both head
+// blocks of its pair (the rows widened exactly to bf16 as they are read).
+__device__ __forceinline__ void qk_partial8(const uint8_t* tq, const TileAddr8& ad, const bf16x8_t (&qb)[2][9],
+                                            int kk, int g, f32x4_t (&sp)[2][2]) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
-        apply_rescale8(rv, lane & 15, acc);
-    }
-    if (QK) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kl = 0; kl < 9; ++kl) {
+        const int s = 18 * kk + 2 * kl + (g >> 1);  // chunk of dims 32(9kk + kl) + 8g .. +7
+        const uint2 r0 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * (s ^ ad.fq0));
+        const uint2 r1 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * kRow8 + 16 * (s ^ ad.fq1));
+        const bf16x8_t a0 = e4m3x8_to_bf16x8(r0.x, r0.y);
+        const bf16x8_t a1 = e4m3x8_to_bf16x8(r1.x, r1.y);
 #pragma unroll
-    for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, nullptr, i, lane);
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-        if (PV) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int d = 2 * ch + i;  // value dims 128 wave + 16 d .. +15: chunk 8 wave + d
-                const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) i32x2_t*)(tv + ad.pv + 16 * ((8 * wave + d) ^ ad.fpv)));
-                const bf16x8_t a = e4m3x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
-            }
-        }
-        if (QK) {
-            const int k0 = 2 * ch;
-            const int k1 = ch == 3 ? 9 : 2 * ch + 2;
-#pragma unroll
-            for (int kl = k0; kl < k1; ++kl) {
-                const int s = 18 * kk + 2 * kl + (g >> 1);  // chunk of dims 32(9kk + kl) + 8g .. +7
-                const uint2 r0 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * (s ^ ad.fq0));
-                const uint2 r1 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * kRow8 + 16 * (s ^ ad.fq1));
-                const bf16x8_t a0 = e4m3x8_to_bf16x8(r0.x, r0.y);
-                const bf16x8_t a1 = e4m3x8_to_bf16x8(r1.x, r1.y);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
-                    sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
-                }
-            }
+        for (int h = 0; h < 2; ++h) {
+            sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
+            sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
         }
     }
 }
 
-template <bool DIRECT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_mla_fp8_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, int64_t kv_bstride,
+// P.V of E4M3 tile tv for value dims 128 vw .. +127 of all four head blocks.
+__device__ __forceinline__ void pv_tile8(const uint8_t* tv, const TileAddr8& ad, const bf16x8_t (&pbv)[4], int vw,
+                                         PvAcc& acc) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {  // value dims 128 vw + 16 d .. +15: chunk 8 vw + d
+        const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(tv + ad.pv + 16 * ((8 * vw + d) ^ ad.fpv)));
+        const bf16x8_t a = e4m3x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+    }
+}
+
+// The gather plan of tile t into LDS buffer `tile` for value wave vw (bf16 or E4M3 rows).
+template <bool FP8>
+__device__ __forceinline__ auto plan_tile(const void* kvb, const int* rows_lds, int t, uint8_t* tile, int vw,
+                                          int lane) {
+    if constexpr (FP8) return plan_gather8(reinterpret_cast<const uint8_t*>(kvb), rows_lds, t, tile, vw, lane);
+    else return plan_gather(reinterpret_cast<const uint16_t*>(kvb), rows_lds, t, reinterpret_cast<uint16_t*>(tile),
+                            vw, lane);
+}
+
+// Wait until at most `tiles_left` of this value wave's tile gathers are in flight.
+template <bool FP8>
+__device__ __forceinline__ void wait_gathers(int tiles_left, int nload) {
+    if constexpr (FP8) {
+        wait_tiles8(tiles_left, nload);
+    } else {
+        (void)nload;
+        if (tiles_left >= 2) wait_vmem<2 * kLoads>();
+        else if (tiles_left == 1) wait_vmem<kLoads>();
+        else wait_vmem<0>();
+    }
+}
+
+// ------------------------------------------------------------------ the attention kernel: two roles per SIMD
+// Eight waves, two per SIMD.  Waves 0-3 ("score waves", w = 2hh + kk) do
+// Q.K^T, the partner exchange and the softmax of the work split described
+// above; waves 4-7 ("value waves") issue the gathers and do P.V for value
+// dims 128(w-4) .. +127 of all 64 heads.  Each tile step has two phases
+// between workgroup barriers:
+//   phase 1  score waves: Q.K^T of tile t+1, partials sent to the partner;
+//            value waves: the gathers of tile t+kStages-1 (planned one
+//            iteration earlier), tile t's rescale record applied, its four
+//            P^T blocks loaded into registers;
+//   phase 2  score waves: scores and softmax of tile t+1 (P^T and rescale
+//            record to LDS); value waves: the next gather plan beside P.V of
+//            tile t, then the wait for their loads of tile t+1.
+// So every SIMD runs one wave's softmax (VALU) beside the other's P.V (matrix
+// cores) instead of one after the other (with one wave per SIMD doing all
+// four jobs in turn, the matrix cores sat idle through every softmax; this
+// measured 1.56x faster per bf16 prefill layer).  The two roles run separate
+// loops with the same sequence of barriers, so the registers of one (q for the
+// score waves, the accumulators for the value waves) are not held by the
+// other.  P^T needs one buffer: the value waves read it before the phase
+// barrier that precedes its next write.
+// FP8: the latent rows are E4M3 codes in a ring of seven 18 KiB tiles with the
+// rescale records beside it; otherwise bf16 tiles with the records in the
+// freed K-tail of each tile (the bf16 decode configuration uses all 160 KiB).
+template <bool DIRECT, bool FP8>
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
+    const uint16_t* __restrict__ q, const void* __restrict__ kv_any, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int grp = blockIdx.x / (kXcds * nsplit);
@@ -832,101 +636,193 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int b = bt / T;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int kk = wave & 1;
-    const int hh = wave >> 1;
+    const bool score = wave < kWaves;
     const int c = lane & 15;
     const int g = lane >> 4;
     const int j0 = split * rows_per_split;
     const int nrows = min(k, j0 + rows_per_split) - j0;
     const int ntiles = (nrows + kRows - 1) / kRows;
-    const int nload = wave < 2 ? 5 : 4;
 
-    __shared__ __attribute__((aligned(16))) uint8_t tiles[kStages8 * kTile8Bytes];
-    static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile ring");
-    __shared__ __attribute__((aligned(16))) Rescale8 rescale[kStages8];
-    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];
-    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];
+    constexpr int kStages = FP8 ? kStages8 : Cfg<DIRECT>::kStages;
+    constexpr int kTileBytes = FP8 ? kTile8Bytes : kTileChunks * 16;
+    using TileT = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+    __shared__ __attribute__((aligned(16))) TileT tiles[kStages * kTileBytes / sizeof(TileT)];
+    static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile buffers");
+    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
+    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
     __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
-
-    bf16x8_t qb[2][9];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (2 * hh + h) + c) * kDqk + 8 * g + 32 * 9 * kk;
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+    Rescale8* records = nullptr;  // FP8: rescale record of tile t at records[t % kStages]
+    if constexpr (FP8) {
+        __shared__ __attribute__((aligned(16))) Rescale8 rescale8[kStages8];
+        records = rescale8;
     }
-    const int32_t* sel = idx + (int64_t)bt * k + j0;
-    for (int j = threadIdx.x; j < ntiles * kRows; j += kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int kl = 0; kl < 9; ++kl) asm volatile("" ::"v"(qb[h][kl]));
-    __syncthreads();  // rows_lds ready
-
-    const uint8_t* kvb = kv + (int64_t)b * kv_bstride;  // kv_bstride counts bytes
-    const TileAddr8 ad = tile_addr8(lane);
-    auto buf = [&](int t) { return tiles + (t % kStages8) * kTile8Bytes; };
-    auto rec = [&](int t) -> Rescale8& { return rescale[t % kStages8]; };
-    for (int t = 0; t < kStages8 - 1 && t < ntiles; ++t) {
-        const GatherPlan8 gp = plan_gather8(kvb, rows_lds, t, nrows, L, buf(t), wave, lane);
-#pragma unroll
-        for (int i = 0; i < kLoads8Max; ++i) issue_gather(gp, nullptr, i, lane);
-    }
-
-    PvAcc acc;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    SoftmaxState st;
-    st.m_ref = -INFINITY;
-    st.lsum = 0.0f;
-    GatherPlan8 no_gather;
-    no_gather.active = false;
-    no_gather.nload = 0;
-
-    auto finish_scores = [&](int t, const f32x4_t (&sp)[2][2]) {
-        f32x4_t s[2];
-        own_scores(sp, sx, wave, kk, lane, s);
-        float factor;
-        bool moved;
-        const bf16x8_t pb = softmax_tile(s, valid_bits(rows_lds, t, g), false, scale_log2, st, factor, moved);
-        pl[wave * kWave + lane] = pb;
-        if (g == 0) rec(t).fac[16 * wave + c] = factor;
-        if (lane == 0) rec(t).flag[wave] = moved ? 1u : 0u;
+    auto buf = [&](int t) __attribute__((always_inline)) {
+        return reinterpret_cast<uint8_t*>(tiles) + (t % kStages) * kTileBytes;
     };
+    auto buf16 = [&](int t) __attribute__((always_inline)) {
+        return reinterpret_cast<const uint16_t*>(tiles) + (t % kStages) * (kTileBytes / 2);
+    };
+    const TileAddr ad = tile_addr(lane);     // bf16 operand addresses
+    const TileAddr8 ad8 = tile_addr8(lane);  // E4M3 operand addresses
+    float* stats = reinterpret_cast<float*>(sx);  // epilogue: [0, 64) sums, [64, 128) maxima
+    char* st8 = reinterpret_cast<char*>(tiles);   // epilogue: output rows staged, kStageRow bytes apart
 
-    // Tile 0: wait for it alone, Q.K^T, exchange, softmax.
-    wait_tiles8(min(ntiles - 1, kStages8 - 2), nload);
-    lds_barrier();
-    {
-        f32x4_t sp[2][2];
-        pv_qk8<false, true>(buf(0), rec(0), buf(0), ad, pl, qb, kk, wave, lane, acc, sp, no_gather);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();
-        finish_scores(0, sp);
+    const int32_t* sel = idx + (int64_t)bt * k + j0;
+    if (score) {
+        // ---------------- score waves, w = 2hh + kk.  qb[0] holds the wave's own
+        // head block w, qb[1] the partner's block w ^ 1, so the partial to keep
+        // and the partial to send need no selects.
+        const int sw = wave, kk = sw & 1;
+        bf16x8_t qb[2][9];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (sw ^ h) + c) * kDqk + 8 * g + 32 * 9 * kk;
+#pragma unroll
+            for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+        }
+        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
+        __syncthreads();  // rows_lds ready
+        SoftmaxState st;
+        st.m_ref = -INFINITY;
+        st.lsum = 0.0f;
+        // Q.K^T of tile t, the exchange and the softmax; P^T and the rescale record to LDS
+        auto scores_of = [&](int t) __attribute__((always_inline)) {
+            f32x4_t sp[2][2];
+            if constexpr (FP8) qk_partial8(buf(t), ad8, qb, kk, g, sp);
+            else qk_partial(buf16(t), ad, qb, kk, sp);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) sx[((sw ^ 1) * 2 + rb) * kWave + lane] = sp[rb][1];
+            // the tile's visible rows: one LDS read and a ballot give a wave-uniform mask
+            const uint32_t tmask = (uint32_t)__ballot(rows_lds[t * kRows + (lane & 31)] >= 0);
+            lds_barrier();  // partials exchanged (phase 1 -> 2)
+            f32x4_t s[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) s[rb] = sp[rb][0] + sx[(sw * 2 + rb) * kWave + lane];
+            // value e of this lane is row e < 4 ? 4g + e : 16 + 4g + e - 4
+            const uint32_t valid = ((tmask >> (4 * g)) & 0xFu) | (((tmask >> (16 + 4 * g)) & 0xFu) << 4);
+            float factor;
+            bool moved;
+            const bf16x8_t pb = softmax_tile(s, valid, tmask == 0xFFFFFFFFu, scale_log2, st, factor, moved);
+            pl[sw * kWave + lane] = pb;
+            float* fac;
+            uint32_t* flag;
+            if constexpr (FP8) {
+                fac = records[t % kStages].fac;
+                flag = records[t % kStages].flag;
+            } else {
+                fac = reinterpret_cast<float*>(buf(t) + kFacOffset);
+                flag = reinterpret_cast<uint32_t*>(buf(t) + kFlagOffset);
+            }
+            if (g == 0) fac[16 * sw + c] = factor;
+            if (lane == 0) flag[sw] = moved ? 1u : 0u;
+        };
+        lds_barrier();  // tile 0 in LDS
+        scores_of(0);
+        for (int t = 0; t + 1 < ntiles; ++t) {
+            lds_barrier();  // tile t+1 in LDS; the value waves hold P^T of tile t
+            scores_of(t + 1);
+        }
+        lds_barrier();  // P^T and rescale record of the last tile visible
+        // epilogue: denominators and maxima of head block sw
+        float lsum = st.lsum;
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        if (g == 0) {
+            stats[16 * sw + c] = lsum;
+            stats[64 + 16 * sw + c] = st.m_ref;
+        }
+        lds_barrier();  // stats visible
+        lds_barrier();  // output rows staged
+        const int head = 16 * sw + c;
+        if (g == 0) {
+            if (DIRECT) {
+                if (lse) lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (st.m_ref + log2f(lsum)) * 0.69314718055994531f
+                                                                      : -INFINITY;
+            } else {
+                part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY;
+            }
+        }
+    } else {
+        // ---------------- value waves
+        const int vw = wave - kWaves;
+        // the sequence's rows (bf16 strides count elements, E4M3 strides bytes)
+        const void* kvb = FP8 ? (const void*)(reinterpret_cast<const uint8_t*>(kv_any) + b * kv_bstride)
+                              : (const void*)(reinterpret_cast<const uint16_t*>(kv_any) + b * kv_bstride);
+        const int nload = FP8 ? (vw < 2 ? 5 : 4) : kLoads;  // loads per tile of this wave
+        constexpr int kMaxLoads = FP8 ? kLoads8Max : kLoads;
+        static_assert(FP8 || Cfg<DIRECT>::kStages <= 4, "bf16 wait counts cover at most two tiles in flight");
+        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
+        __syncthreads();  // rows_lds ready
+        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
+            const auto gp = plan_tile<FP8>(kvb, rows_lds, t, buf(t), vw, lane);
+#pragma unroll
+            for (int i = 0; i < kMaxLoads; ++i) issue_gather(gp, i);
+        }
+        PvAcc acc;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        wait_gathers<FP8>(min(ntiles - 1, kStages - 2), nload);  // tile 0 landed
+        // The plan of each in-loop gather (addresses from rows_lds) is made one
+        // iteration ahead, beside the P.V work, so phase 1 only issues the loads.
+        auto next = plan_tile<FP8>(kvb, rows_lds, min(kStages - 1, ntiles - 1), buf(kStages - 1), vw, lane);
+        next.active = kStages - 1 < ntiles;
+        lds_barrier();  // tile 0 in LDS
+        lds_barrier();  // (score waves: partials of tile 0 exchanged)
+        bf16x8_t pbv[4];
+        for (int t = 0; t + 1 < ntiles; ++t) {
+            // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
+            wait_gathers<FP8>(min(ntiles - 1, t + kStages - 2) - (t + 1), nload);
+            lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
+#pragma unroll
+            for (int i = 0; i < kMaxLoads; ++i) issue_gather(next, i);  // tile t + kStages - 1
+            if constexpr (FP8) apply_rescale8(records[t % kStages], c, acc);
+            else apply_rescale(buf16(t), c, acc);
+            load_p(pl, lane, pbv);
+            lds_barrier();  // (phase 1 -> 2) P^T of tile t is in registers; the score waves may overwrite it
+            // tile t + kStages goes to this tile's buffer, next iteration, after this P.V and a barrier
+            auto nx = plan_tile<FP8>(kvb, rows_lds, min(t + kStages, ntiles - 1), buf(t), vw, lane);
+            nx.active = t + kStages < ntiles;
+            if constexpr (FP8) pv_tile8(buf(t), ad8, pbv, vw, acc);
+            else pv_tile(buf16(t), ad, pbv, vw, acc);
+            next = nx;
+        }
+        lds_barrier();  // P^T and rescale record of the last tile visible
+        if constexpr (FP8) {
+            apply_rescale8(records[(ntiles - 1) % kStages], c, acc);
+            load_p(pl, lane, pbv);
+            pv_tile8(buf(ntiles - 1), ad8, pbv, vw, acc);
+        } else {
+            apply_rescale(buf16(ntiles - 1), c, acc);
+            load_p(pl, lane, pbv);
+            pv_tile(buf16(ntiles - 1), ad, pbv, vw, acc);
+        }
+        lds_barrier();  // stats visible; every value wave is done reading the tiles
+        float inv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const float ls = stats[16 * hb + c];
+            inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
+        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const f32x4_t& o = acc.o[d][hb];
+                *reinterpret_cast<uint2*>(st8 + (16 * hb + c) * kStageRow + 2 * (128 * vw + 16 * d + 4 * g)) =
+                    make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
+            }
+        lds_barrier();  // output rows staged
     }
-    // Iteration t: P.V of tile t with Q.K^T of tile t+1 and the gather of tile
-    // t+6 into the buffer tile t-1 has left; then the exchange and softmax of t+1.
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        wait_tiles8(min(ntiles - 1, t + kStages8 - 2) - (t + 1), nload);
-        lds_barrier();  // tile t+1 in LDS; P^T and record of tile t visible; buffer of tile t-1 free
-        const int u = t + kStages8 - 1;
-        GatherPlan8 gp = plan_gather8(kvb, rows_lds, min(u, ntiles - 1), nrows, L, buf(u), wave, lane);
-        gp.active = u < ntiles;
-        f32x4_t sp[2][2];
-        pv_qk8<true, true>(buf(t), rec(t), buf(t + 1), ad, pl, qb, kk, wave, lane, acc, sp, gp);
-        send_partial(sp, sx, wave, kk, lane);
-        lds_barrier();  // partials exchanged; every wave is done reading P^T and the record of tile t
-        finish_scores(t + 1, sp);
+    // every wave stores 8 of the 64 head rows, one 16-byte store per lane per row
+    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int h = 8 * wave + i;
+        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
+            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
     }
-    lds_barrier();
-    {
-        f32x4_t sp[2][2];
-        pv_qk8<true, false>(buf(ntiles - 1), rec(ntiles - 1), buf(ntiles - 1), ad, pl, qb, kk, wave, lane, acc, sp,
-                            no_gather);
-    }
-    store_output<DIRECT>(acc, st, sx, tiles, wave, lane, bt, split, nsplit, part_o, part_lse, out, lse);
 }
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
@@ -1030,16 +926,17 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q, kv,
-                           kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
+        hipLaunchKernelGGL((sparse_mla_kernel<true, false>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q,
+                           kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out,
+                           lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q,
-                       kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
-                       nullptr, nullptr);
+    hipLaunchKernelGGL((sparse_mla_kernel<false, false>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
+                       stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
+                       part_lse, nullptr, nullptr);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
                        part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
@@ -1052,16 +949,17 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstr
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL(sparse_mla_fp8_kernel<true>, dim3(xcd_grid(rows, 1)), dim3(kThreads), 0, stream, q, kv,
-                           kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
+        hipLaunchKernelGGL((sparse_mla_kernel<true, true>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q,
+                           kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out,
+                           lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL(sparse_mla_fp8_kernel<false>, dim3(xcd_grid(rows, p.nsplit)), dim3(kThreads), 0, stream, q, kv,
-                       kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse,
-                       nullptr, nullptr);
+    hipLaunchKernelGGL((sparse_mla_kernel<false, true>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
+                       stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
+                       part_lse, nullptr, nullptr);
     hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
                        part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
