@@ -60,9 +60,6 @@ constexpr int kMaxSplitRows = Cfg<false>::kMaxRows;
 constexpr int kMaxSplits = 2048 / kRows;          // k <= 2048
 constexpr int kTargetBlocks = 256;                // one resident block per CU
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs, block ids dealt round-robin
-#ifndef QK_AHEAD
-#define QK_AHEAD 2
-#endif
 constexpr float kRescaleSlack = 32.0f;            // log2 units: P < 2^32, |O| < 2^46 in fp32
 
 static_assert(kTileChunks % kThreads == 0, "tile load must split evenly");
