@@ -205,6 +205,8 @@ int dsa_sparse_mla_attn_fp8kv(const uint16_t* q, const uint8_t* kv, int64_t kv_b
  *   if all S are accepted: next_token[b] = InvCDF(p_S, u_resample[b]);
  *   n_accepted[b] = number of accepted drafts (acceptance length n_accepted + 1)
  * where InvCDF(r, u) is the smallest v with sum_{v'<=v} r[v'] > u * sum_v r[v].
+ * A draft token outside [0, V) has p_i(x) = 0 and is rejected; a residual
+ * without mass (p_i == q_i) is replaced by p_i.
  * fp32 exponentials, fp64 sums.  Decisions whose margin is below the fp32
  * resolution of p/q, or a CDF step closer to u*sum r than that resolution,
  * may go either way.

@@ -331,7 +331,9 @@ void oracle_mtp_verify(const float* target, const float* draft, const int32_t* d
             for (int v = 0; v < V; ++v) ms += p[v] < qd[v] ? p[v] : qd[v];
             min_sum[(int64_t)b * S + i] = ms;
             int32_t x = draft_tokens[(int64_t)b * S + i];
-            double rt = p[x] / qd[x];
+            /* the target distribution has no mass outside the vocabulary: such a token has
+               p(x) = 0, ratio 0, and is rejected */
+            double rt = (x >= 0 && x < V) ? p[x] / qd[x] : 0.0;
             if (ratio) ratio[(int64_t)b * S + i] = rt;
             if (rejected_at < 0 && !((double)u_acc[(int64_t)b * S + i] < rt)) {
                 rejected_at = i;

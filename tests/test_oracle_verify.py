@@ -116,6 +116,24 @@ def test_resample_is_inverse_cdf_of_residual():
     assert r["n_acc"][0] == 1 and r["next_tok"][0] == 1
 
 
+def test_out_of_vocabulary_token_is_rejected():
+    # A token outside [0, V) has target probability 0: ratio 0, rejected for any u.
+    # Hand-built p = [.5,.3,.2], q = [.2,.3,.5]: the residual [.3,0,0] gives token 0.
+    p = np.array([0.5, 0.3, 0.2])
+    q = np.array([0.2, 0.3, 0.5])
+    t = np.log(np.stack([p, p]))[None].astype(np.float32)
+    d = np.log(q)[None, None].astype(np.float32)
+    for x in (-1, 3, 1 << 20):
+        r = oracle.mtp_verify(t, d, np.array([[x]], np.int32), np.array([[1e-6]], np.float32),
+                              np.array([0.5], np.float32))
+        assert r["ratio"][0, 0] == 0.0 and r["n_acc"][0] == 0 and r["next_tok"][0] == 0, x
+    # q == p: the residual has no mass, so the sample comes from p itself;
+    # cumsum [.5,.8,1.0] > 0.75 first at index 1
+    r = oracle.mtp_verify(t, np.log(p)[None, None].astype(np.float32), np.array([[7]], np.int32),
+                          np.array([[0.5]], np.float32), np.array([0.75], np.float32))
+    assert r["n_acc"][0] == 0 and r["next_tok"][0] == 1
+
+
 def test_inverse_cdf_boundary_is_strict():
     # InvCDF takes the smallest v whose cumulative mass is strictly above u*total:
     # p = [.5, .5] and u = .5 lands exactly on the first step, so the answer is 1.
