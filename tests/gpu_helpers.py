@@ -65,7 +65,7 @@ def check_topk_properties(idx: np.ndarray, scores: np.ndarray, pos: np.ndarray, 
             assert tied_in.max() < tied_out.min()
 
 
-def _inv_cdf_valid(r: np.ndarray, u: float, v: int) -> bool:
+def inv_cdf_valid(r: np.ndarray, u: float, v: int) -> bool:
     c = np.cumsum(r)
     thr = u * c[-1]
     if v < 0 or v >= r.size or r[v] <= 0:
@@ -99,4 +99,4 @@ def check_verify(min_sum, n_acc, nxt, target, draft, tokens, u_acc, u_res):
             r = np.maximum(p - q, 0.0)
         else:
             r = oracle.softmax_row(target[b, S])
-        assert _inv_cdf_valid(r, float(u_res[b]), int(nxt[b])), (b, na, int(nxt[b]), int(ref["next_tok"][b]))
+        assert inv_cdf_valid(r, float(u_res[b]), int(nxt[b])), (b, na, int(nxt[b]), int(ref["next_tok"][b]))

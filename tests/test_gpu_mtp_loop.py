@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import (ATTN_TOL, DEV, RATIO_BAND, assert_attn_close, bf16_dev, f32_dev, host, i32_dev, say,
-                         _inv_cdf_valid)
+                         inv_cdf_valid)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,7 +164,7 @@ def test_rounds_chained_on_device_match_oracle(dsa, rule, entry):
                 na = int(ref[r]["n_acc"][b])
                 p = oracle.softmax_row(rd.target[r][b, na])
                 rr = np.maximum(p - oracle.softmax_row(rd.draft[r][b, na]), 0.0) if na < S else p
-                assert _inv_cdf_valid(rr, float(rd.ur[r][b]), int(got_nt[b]))
+                assert inv_cdf_valid(rr, float(rd.ur[r][b]), int(got_nt[b]))
         for i in (0, S - 1):
             assert_attn_close(host(outs[i]), ref[r]["outs"][i], "round %d step %d" % (r, i))
     np.testing.assert_array_equal(host(qp[R % 2]), q_final)

@@ -9,7 +9,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import (DEV, LSE_TOL, assert_attn_close, bf16_dev, check_topk_properties, check_verify, f32_dev,
-                         host, i32_dev, say)
+                         host, i32_dev, inv_cdf_valid, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -345,7 +345,7 @@ def test_verify_small(dsa, rho):
     check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
 
 
-@pytest.mark.parametrize("S", [1, 20])
+@pytest.mark.parametrize("S", [1, 20, 64])
 def test_verify_draft_lengths(dsa, S):
     rng = np.random.default_rng(60 + S)
     B, V = 5, 3000
@@ -367,6 +367,38 @@ def test_verify_mtp_vocab(dsa):
     tok = cfg.draft_tokens(d)
     u, ur = cfg.u_accept(), cfg.u_resample()
     ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
+def test_verify_ragged_vocab(dsa):
+    # V not a multiple of 4 (element-wise loads) and a ragged last chunk
+    rng = np.random.default_rng(71)
+    B, S, V = 4, 5, 8195
+    say("verify V=%d" % V)
+    t = (rng.standard_normal((B, S + 1, V)) * 2).astype(np.float32)
+    d = (0.8 * t[:, :S] + 0.6 * rng.standard_normal((B, S, V)) * 2).astype(np.float32)
+    tok = np.argmax(d + rng.gumbel(size=d.shape), axis=-1).astype(np.int32)
+    u = rng.random((B, S)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
+def test_verify_residual_without_mass_samples_p(dsa):
+    # draft == target and a rejected out-of-vocabulary token: max(p - q, 0) has no
+    # mass, so the resample draws from p of the rejected step
+    rng = np.random.default_rng(72)
+    B, S, V = 3, 2, 20000
+    t = rng.standard_normal((B, S + 1, V)).astype(np.float32)
+    d = t[:, :S].copy()
+    tok = np.full((B, S), V + 1, np.int32)
+    u = np.full((B, S), 0.5, np.float32)
+    ur = np.array([0.1, 0.5, 0.97], np.float32)
+    say("verify residual without mass")
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    assert np.all(host(na) == 0)
+    for b in range(B):
+        assert inv_cdf_valid(oracle.softmax_row(t[b, 0]), float(ur[b]), int(host(nx)[b])), b
     check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
 
 
