@@ -76,6 +76,10 @@ constexpr int kMainBytes = kRows * 1024;
 // load fills, does not drain every in-flight load before each LDS read; the
 // kernel orders these writes itself with wait_vmem() and lds_barrier().  The
 // instruction has no register result and reads its address when issued.
+// The statement sets m0 (the LDS destination) itself and lists it as clobbered.
+// The compiler warns that it may not preserve a reserved register across asm;
+// that is harmless here, because nothing else in these kernels keeps a value
+// in m0: in their assembly every write of m0 is one of these statements.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_byte_addr) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte_addr) : "memory", "m0");
 }
@@ -828,12 +832,13 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 // 4 dims per thread; blocks numbered like the split kernel so each reads
 // partials from its own XCD's L2.
 constexpr int kCombineThreads = 128;
-constexpr int kCombineBatch = 16;  // splits loaded per round
 
 // Every wave derives the split weights itself: lane s holds split s's
 // log2-sum-exp (nsplit <= 64), the maximum and the denominator come from wave
 // reductions, and the weights reach the accumulation loop through readlane, so
-// the block needs no barrier.  The partial loads go out first.
+// the block needs no barrier.  The partial loads go out first, NB splits per
+// round (8 when there are at most 8 splits, else 16).
+template <int NB>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                        const float* __restrict__ part_lse, int rows,
                                                                        int nsplit, uint16_t* __restrict__ out,
@@ -847,10 +852,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     const int lane = lane_id();
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
     const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
-    uint2 v[kCombineBatch];
+    uint2 v[NB];
     auto load_batch = [&](int s0) {
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int sp = min(s0 + u, nsplit - 1);  // past the end: a valid split, weight 0 below
             v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
         }
@@ -866,10 +871,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, kWave);
     const uint32_t a_bits = __float_as_uint(a);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+    for (int s0 = 0; s0 < nsplit; s0 += NB) {
         if (s0 > 0) load_batch(s0);
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const float w = s0 + u < nsplit ? __uint_as_float(__builtin_amdgcn_readlane(a_bits, s0 + u)) : 0.0f;
             acc[0] += w * __uint_as_float(v[u].x << 16);
             acc[1] += w * __uint_as_float(v[u].x & 0xFFFF0000u);
@@ -934,8 +939,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     hipLaunchKernelGGL((sparse_mla_kernel<false, false>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
                        stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
                        part_lse, nullptr, nullptr);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
-                       part_lse, rows, p.nsplit, out, lse);
+    hipLaunchKernelGGL(p.nsplit <= 8 ? attn_combine_kernel<8> : attn_combine_kernel<16>, dim3(xcd_grid(rows, kHq)),
+                       dim3(kCombineThreads), 0, stream, part_o, part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
 }
 
@@ -957,8 +962,8 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstr
     hipLaunchKernelGGL((sparse_mla_kernel<false, true>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
                        stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
                        part_lse, nullptr, nullptr);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, part_o,
-                       part_lse, rows, p.nsplit, out, lse);
+    hipLaunchKernelGGL(p.nsplit <= 8 ? attn_combine_kernel<8> : attn_combine_kernel<16>, dim3(xcd_grid(rows, kHq)),
+                       dim3(kCombineThreads), 0, stream, part_o, part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
 }
 
