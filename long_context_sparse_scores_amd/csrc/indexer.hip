@@ -30,16 +30,10 @@ constexpr int kD = 128;
 constexpr int kTile = 16;                      // keys per MFMA tile
 constexpr int kTileBytes = kTile * kD * 2;     // 4 KiB
 constexpr int kLoads = kTileBytes / (kWave * 16);  // 4 loads of 1 KiB per tile
-#ifndef INDEXER_AHEAD
-#define INDEXER_AHEAD 4
-#endif
-constexpr int kAhead = INDEXER_AHEAD;          // tiles loaded ahead of the one computed
-
 // Measured best on MI355X for 128K and 1M rows: 4 waves x 16 tiles, 4 tiles ahead.
-#ifndef INDEXER_WAVES
-#define INDEXER_WAVES 4
-#define INDEXER_TILES 16
-#endif
+constexpr int kAhead = 4;                      // tiles loaded ahead of the one computed
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeTiles = 16;               // tiles per wave
 
 template <int kWaves, int kTilesPerWave>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
@@ -152,11 +146,9 @@ constexpr int kTile8Bytes = kTile8 * kD8;       // 4 KiB
 constexpr int kLoads8 = kTile8Bytes / (kWave * 16);  // 4 loads of 1 KiB per tile
 
 // Measured best on MI355X for 128K x 32 and 1M x 4: 4 waves x 16 tiles of 32 keys, 6 tiles ahead.
-#ifndef INDEXER8_WAVES
-#define INDEXER8_WAVES 4
-#define INDEXER8_TILES 16
-#define INDEXER8_AHEAD 6
-#endif
+constexpr int kDecode8Waves = 4;
+constexpr int kDecode8Tiles = 16;
+constexpr int kDecode8Ahead = 6;
 
 __device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
@@ -549,8 +541,8 @@ hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_
                            q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
         return hipGetLastError();
     }
-    return launch_indexer_fp8_cfg<INDEXER8_WAVES, INDEXER8_TILES, INDEXER8_AHEAD>(q_idx, w, k_idx, k_bstride, q_pos,
-                                                                                  B, T, L, scores, stream, zero);
+    return launch_indexer_fp8_cfg<kDecode8Waves, kDecode8Tiles, kDecode8Ahead>(q_idx, w, k_idx, k_bstride, q_pos, B,
+                                                                               T, L, scores, stream, zero);
 }
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
@@ -563,8 +555,8 @@ hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t*
                            q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
         return hipGetLastError();
     }
-    return launch_indexer_cfg<INDEXER_WAVES, INDEXER_TILES>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores,
-                                                            stream, zero);
+    return launch_indexer_cfg<kDecodeWaves, kDecodeTiles>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, stream,
+                                                          zero);
 }
 
 }  // namespace dsa
