@@ -48,14 +48,20 @@ constexpr int kTileChunks = kRows * kChunks;      // 2304 chunks = 36 KiB per ti
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLoads = 9;                         // direct-to-LDS loads per wave per tile: 8 row mains + 1 tail block
-// Splits of a query's list (decode): 4 tile buffers (3 tiles in flight) and
-// row lists of up to 1024 entries.  Whole lists (a query per workgroup, prefill
-// sized batches): 3 buffers and up to 2048 entries; that path is bound by the
-// matrix work, not by how many gathers are in flight.
+// Splits of a query's list (decode): row lists of up to 1024 entries, and 4
+// bf16 tile buffers (3 tiles in flight) for splits of more than 4 tiles, else
+// 3.  At the start every workgroup asks for its first tiles at once and that
+// burst is bound by HBM, so a shorter burst lands tile 0 sooner, which pays
+// when the split has few tiles to hide it behind (measured: 4-tile splits at
+// B = 16, 21.4 -> 20.6 us per launch pair; 8-tile splits at B = 32, 31.4 us
+// with 4 buffers against 31.9 with 3).  Whole lists (a query per workgroup,
+// prefill sized batches): 3 buffers and up to 2048 entries; that path is bound
+// by the matrix work, not by how many gathers are in flight.
 template <bool DIRECT> struct Cfg {
-    static constexpr int kStages = DIRECT ? 3 : 4;
     static constexpr int kMaxRows = DIRECT ? 2048 : 1024;
 };
+constexpr int kDirectStages = 3;
+constexpr int kFewTiles = 4;  // splits of at most this many tiles take 3 buffers
 constexpr int kMaxSplitRows = Cfg<false>::kMaxRows;
 constexpr int kMaxSplits = 2048 / kRows;          // k <= 2048
 constexpr int kTargetBlocks = 256;                // one resident block per CU
@@ -624,7 +630,7 @@ __device__ __forceinline__ void wait_gathers(int tiles_left, int nload) {
 // FP8: the latent rows are E4M3 codes in a ring of seven 18 KiB tiles with the
 // rescale records beside it; otherwise bf16 tiles with the records in the
 // freed K-tail of each tile (the bf16 decode configuration uses all 160 KiB).
-template <bool DIRECT, bool FP8>
+template <bool DIRECT, bool FP8, int STAGES>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_any, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int nrows = min(k, j0 + rows_per_split) - j0;
     const int ntiles = (nrows + kRows - 1) / kRows;
 
-    constexpr int kStages = FP8 ? kStages8 : Cfg<DIRECT>::kStages;
+    constexpr int kStages = FP8 ? kStages8 : STAGES;  // tile buffers
     constexpr int kTileBytes = FP8 ? kTile8Bytes : kTileChunks * 16;
     using TileT = typename std::conditional<FP8, uint8_t, uint16_t>::type;
     __shared__ __attribute__((aligned(16))) TileT tiles[kStages * kTileBytes / sizeof(TileT)];
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
                               : (const void*)(reinterpret_cast<const uint16_t*>(kv_any) + b * kv_bstride);
         const int nload = FP8 ? (vw < 2 ? 5 : 4) : kLoads;  // loads per tile of this wave
         constexpr int kMaxLoads = FP8 ? kLoads8Max : kLoads;
-        static_assert(FP8 || Cfg<DIRECT>::kStages <= 4, "bf16 wait counts cover at most two tiles in flight");
+        static_assert(FP8 || (STAGES >= 3 && STAGES <= 4), "bf16 wait counts cover one or two later tiles in flight");
         for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
         __syncthreads();  // rows_lds ready
         for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
@@ -928,17 +934,18 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL((sparse_mla_kernel<true, false>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q,
-                           kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out,
-                           lse);
+        hipLaunchKernelGGL((sparse_mla_kernel<true, false, kDirectStages>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads),
+                           0, stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr,
+                           nullptr, out, lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL((sparse_mla_kernel<false, false>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
-                       stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
-                       part_lse, nullptr, nullptr);
+    auto* split_kernel = p.rows_per_split <= kFewTiles * kRows ? sparse_mla_kernel<false, false, 3>
+                                                               : sparse_mla_kernel<false, false, 4>;
+    hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q, kv, kv_bstride,
+                       idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o, part_lse, nullptr, nullptr);
     hipLaunchKernelGGL(p.nsplit <= 8 ? attn_combine_kernel<8> : attn_combine_kernel<16>, dim3(xcd_grid(rows, kHq)),
                        dim3(kCombineThreads), 0, stream, part_o, part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
@@ -951,17 +958,17 @@ hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstr
     const SplitPlan p = plan(rows, k);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL((sparse_mla_kernel<true, true>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0, stream, q,
-                           kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out,
-                           lse);
+        hipLaunchKernelGGL((sparse_mla_kernel<true, true, kStages8>), dim3(xcd_grid(rows, 1)), dim3(2 * kThreads), 0,
+                           stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1, scale_log2, nullptr,
+                           nullptr, out, lse);
         return hipGetLastError();
     }
     const size_t n = (size_t)rows * p.nsplit * kHq;
     uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
     float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(n * kDv * sizeof(uint16_t), 256));
-    hipLaunchKernelGGL((sparse_mla_kernel<false, true>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0,
-                       stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, part_o,
-                       part_lse, nullptr, nullptr);
+    hipLaunchKernelGGL((sparse_mla_kernel<false, true, kStages8>), dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads),
+                       0, stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2,
+                       part_o, part_lse, nullptr, nullptr);
     hipLaunchKernelGGL(p.nsplit <= 8 ? attn_combine_kernel<8> : attn_combine_kernel<16>, dim3(xcd_grid(rows, kHq)),
                        dim3(kCombineThreads), 0, stream, part_o, part_lse, rows, p.nsplit, out, lse);
     return hipGetLastError();
