@@ -63,8 +63,12 @@ template <bool DIRECT> struct Cfg {
 constexpr int kDirectStages = 3;
 constexpr int kFewTiles = 4;  // splits of at most this many tiles take 3 buffers
 constexpr int kMaxSplitRows = Cfg<false>::kMaxRows;
-constexpr int kMaxSplits = 2048 / kRows;          // k <= 2048
 constexpr int kTargetBlocks = 256;                // one resident block per CU
+// At most 16 splits per query: every split writes a 64 KiB partial that the
+// combine reads back, and more, shorter splits cost more partials and combine
+// rounds than they save (measured at 1M, B = 4: 64 splits of one tile 29 us per
+// layer, 32 splits 19.8, 16 splits 18.4, 8 splits 20.6).
+constexpr int kMaxQuerySplits = 16;
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs, block ids dealt round-robin
 constexpr float kRescaleSlack = 32.0f;            // log2 units: P < 2^32, |O| < 2^46 in fp32
 
@@ -840,16 +844,16 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 constexpr int kCombineThreads = 128;
 
 // Every wave derives the split weights itself: lane s holds split s's
-// log2-sum-exp (nsplit <= 64), the maximum and the denominator come from wave
-// reductions, and the weights reach the accumulation loop through readlane, so
-// the block needs no barrier.  The partial loads go out first, NB splits per
-// round (8 when there are at most 8 splits, else 16).
+// log2-sum-exp, the maximum and the denominator come from wave reductions, and
+// the weights reach the accumulation through readlane, so the block needs no
+// barrier.  The loads of all NB >= nsplit partials go out first (NB = 8 when
+// there are at most 8 splits, else 16).
 template <int NB>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                        const float* __restrict__ part_lse, int rows,
                                                                        int nsplit, uint16_t* __restrict__ out,
                                                                        float* __restrict__ lse) {
-    static_assert(kMaxSplits <= kWave, "one lane per split");
+    static_assert(kMaxQuerySplits <= 16 && kMaxQuerySplits <= kWave, "one load round, one lane per split");
     const int grp = blockIdx.x / (kXcds * kHq);
     const int rem = blockIdx.x % (kXcds * kHq);
     const int head = rem / kXcds;
@@ -859,14 +863,11 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
     const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
     uint2 v[NB];
-    auto load_batch = [&](int s0) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int sp = min(s0 + u, nsplit - 1);  // past the end: a valid split, weight 0 below
-            v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
-        }
-    };
-    load_batch(0);
+    for (int u = 0; u < NB; ++u) {
+        const int sp = min(u, nsplit - 1);  // past the end: a valid split, weight 0 below
+        v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
+    }
     const float ls = lane < nsplit ? pl[(int64_t)lane * kHq] : -INFINITY;
     float M = ls;
 #pragma unroll
@@ -877,16 +878,13 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, kWave);
     const uint32_t a_bits = __float_as_uint(a);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += NB) {
-        if (s0 > 0) load_batch(s0);
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const float w = s0 + u < nsplit ? __uint_as_float(__builtin_amdgcn_readlane(a_bits, s0 + u)) : 0.0f;
-            acc[0] += w * __uint_as_float(v[u].x << 16);
-            acc[1] += w * __uint_as_float(v[u].x & 0xFFFF0000u);
-            acc[2] += w * __uint_as_float(v[u].y << 16);
-            acc[3] += w * __uint_as_float(v[u].y & 0xFFFF0000u);
-        }
+    for (int u = 0; u < NB; ++u) {
+        const float w = u < nsplit ? __uint_as_float(__builtin_amdgcn_readlane(a_bits, u)) : 0.0f;
+        acc[0] += w * __uint_as_float(v[u].x << 16);
+        acc[1] += w * __uint_as_float(v[u].x & 0xFFFF0000u);
+        acc[2] += w * __uint_as_float(v[u].y << 16);
+        acc[3] += w * __uint_as_float(v[u].y & 0xFFFF0000u);
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) =
@@ -902,6 +900,7 @@ struct SplitPlan {
 SplitPlan plan(int rows, int k) {
     const int tiles = (k + kRows - 1) / kRows;
     int ns = (kTargetBlocks + rows - 1) / rows;
+    if (ns > kMaxQuerySplits) ns = kMaxQuerySplits;
     if (ns > 1) {  // split lists: each split's row list fits the split kernel's LDS
         const int min_ns = (tiles * kRows + kMaxSplitRows - 1) / kMaxSplitRows;
         if (ns < min_ns) ns = min_ns;
