@@ -92,8 +92,6 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
 // Workgroup barrier for LDS hand-offs that leaves outstanding global loads in
 // flight (__syncthreads would wait for them as well).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// The same between the lanes of one wave (LDS executes a wave's accesses in order).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Exclusive prefix sum over a workgroup of NT threads; `scratch` holds NT/64 words of LDS.
 template <int NT>
@@ -175,8 +173,8 @@ struct SelectLds {
             uint32_t pos[kCandLds], key[kCandLds];
         } cand;  // copy of the candidate list
         struct {
-            uint32_t bits[kCandLds];  // kCandLds * 32 positions per chunk
-            uint32_t wpre[kCandLds];  // kept positions in the bitmap words before each word
+            uint32_t bits[kCandLds + NT];  // kCandLds * 32 positions per chunk, word w at w + w / (kCandLds / NT)
+            uint32_t wpre[kCandLds + NT];  // kept positions in the bitmap words before each word (same layout)
         } order;
     };
     uint32_t h[kBins];
@@ -370,36 +368,43 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
     // of its words give every kept position its rank
     static_assert(kCandLds % NT == 0, "whole bitmap words per thread");
     constexpr int kPer = kCandLds / NT;
+    // Thread t counts and prefixes words kPer t .. kPer t + kPer - 1.  Word w is
+    // stored at pw(w) = w + w / kPer, so thread t's words start at (kPer + 1) t:
+    // with an odd stride those loops are free of LDS bank conflicts (a stride of
+    // 12 words put 8 lanes on every bank they touched).
+    static_assert(kPer % 2 == 0, "odd padded stride");
+    auto pw = [](int w) { return w + w / kPer; };
     uint32_t base = 0;
     for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kCandLds * 32) {
         const int nw = (int)min((int64_t)kCandLds, (n - c0 + 31) / 32);
-        for (int i = threadIdx.x; i < nw; i += NT) s.order.bits[i] = 0u;
+        for (int i = threadIdx.x; i < pw(nw - 1) + 1; i += NT) s.order.bits[i] = 0u;
         lds_sync();
         for (int j = threadIdx.x; j < k; j += NT) {
             const int64_t p = (int64_t)s.sel[j] - c0;
-            if (p >= 0 && p < (int64_t)nw * 32) atomicOr(&s.order.bits[p >> 5], 1u << (p & 31));
+            if (p >= 0 && p < (int64_t)nw * 32) atomicOr(&s.order.bits[pw((int)(p >> 5))], 1u << (p & 31));
         }
         lds_sync();
         uint32_t wc[kPer], cnt = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int wi = (int)threadIdx.x * kPer + i;
-            wc[i] = wi < nw ? (uint32_t)__popc(s.order.bits[wi]) : 0u;
+            wc[i] = wi < nw ? (uint32_t)__popc(s.order.bits[pw(wi)]) : 0u;
             cnt += wc[i];
         }
         uint32_t total;
         uint32_t o = excl_scan<NT>(cnt, s.scratch, &total);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            s.order.wpre[threadIdx.x * kPer + i] = o;
+            s.order.wpre[pw((int)threadIdx.x * kPer + i)] = o;
             o += wc[i];
         }
         lds_sync();
         for (int j = threadIdx.x; j < k; j += NT) {
             const int64_t p = (int64_t)s.sel[j] - c0;
             if (p >= 0 && p < (int64_t)nw * 32) {
-                const uint32_t below = s.order.bits[p >> 5] & ((1u << (p & 31)) - 1u);
-                out[base + s.order.wpre[p >> 5] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
+                const int w = pw((int)(p >> 5));
+                const uint32_t below = s.order.bits[w] & ((1u << (p & 31)) - 1u);
+                out[base + s.order.wpre[w] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
             }
         }
         base += total;
