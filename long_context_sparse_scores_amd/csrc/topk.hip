@@ -46,6 +46,7 @@ constexpr int kMinSlice = 4096;
 constexpr int kMaxSlices = 512;      // per row
 constexpr int kStage = 256;          // per-wave LDS staging of candidates
 constexpr int kBatch = 32;           // loads in flight per lane in the streaming passes
+constexpr int kFineSlice = 65536;    // slices at least this long take the 8192-bin LDS histogram
 constexpr int kSelMax = 2048;        // the kept positions (k <= 2048) are compacted in LDS
 constexpr int kCandLds = 12288;      // candidates the selection holds in LDS
 constexpr int kSelBatch = kCandLds / kSelectThreads;  // loads in flight per thread in its passes
@@ -417,16 +418,25 @@ __global__ __launch_bounds__(kThreads) void topk_init_kernel(void* ws, Layout lo
     for (int i = threadIdx.x; i < kBins + kCtrWords; i += kThreads) rw.hist1[i] = 0u;  // hist1, ctr
 }
 
+// The top digit's histogram of one slice.  FINE > 11 counts 2^FINE bins in
+// LDS and folds them to the 2048 top-digit bins on the way out: scores cluster
+// in few top-digit bins, so the LDS atomics of one instruction collide, and
+// finer bins spread them; that pays on long slices (one per row at prefill),
+// where the atomics bound the pass.
+template <int FINE>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ q_pos, int L, int k,
                                                              Layout lo, void* ws) {
+    constexpr int kFine = 1 << FINE;
+    constexpr int kFold = kFine / kBins;
+    static_assert(FINE >= 11, "at least the top digit");
     const int row = blockIdx.x / lo.nslice;
     const int slice = blockIdx.x % lo.nslice;
     const int64_t n = n_visible(q_pos, row, L);
     const int64_t start = (int64_t)slice * lo.slice;
     if (n <= k || start >= n) return;
-    __shared__ uint32_t h[kBins];
-    for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
+    __shared__ uint32_t h[kFine];
+    for (int i = threadIdx.x; i < kFine; i += kThreads) h[i] = 0u;
     const float* src = scores + (int64_t)row * L + start;
     const int m = (int)((n - start) < lo.slice ? (n - start) : lo.slice);
     lds_sync();
@@ -439,12 +449,16 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
-            if (i0 + j * kThreads + (int)threadIdx.x < m) atomicAdd(&h[score_key(v[j]) >> 21], 1u);
+            if (i0 + j * kThreads + (int)threadIdx.x < m) atomicAdd(&h[score_key(v[j]) >> (32 - FINE)], 1u);
     }
     lds_sync();
     uint32_t* g = row_ws(ws, row, lo).hist1;
-    for (int i = threadIdx.x; i < kBins; i += kThreads)
-        if (h[i]) atomicAdd(&g[i], h[i]);
+    for (int i = threadIdx.x; i < kBins; i += kThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int f = 0; f < kFold; ++f) c += h[i * kFold + f];
+        if (c) atomicAdd(&g[i], c);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
@@ -583,7 +597,9 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
     if (!state_zeroed) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
+    // finer LDS bins for long slices (measured: prefill 4096 x 128K rows, one slice per row)
+    hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
+                       dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        idx);

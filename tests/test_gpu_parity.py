@@ -171,6 +171,23 @@ def test_topk_long_rows(dsa, L):
     _topk_case(dsa, s, pos, 2048)
 
 
+def test_topk_long_slices(dsa):
+    # 512 rows of 66000 keys: one slice per row, long enough for the fine-bin
+    # histogram; clustered values (few top-digit bins), ties and ragged rows.
+    # The oracle checks a sample of the rows.
+    rng = np.random.default_rng(16)
+    B, T, L = 1, 512, 66000
+    say("topk %d rows x %d (fine-bin histogram)" % (T, L))
+    s = (1.0 + rng.integers(0, 4096, size=(B, T, L)) / 1024).astype(np.float32)
+    s[0, 1::5] = (2.0 + rng.integers(0, 3, size=(T // 5 + 1, L))[: len(range(1, T, 5))]).astype(np.float32)
+    pos = np.full((B, T), L - 1, np.int32)
+    pos[0, ::7] = rng.integers(1000, L, size=len(range(0, T, 7)))
+    got = host(dsa.topk(f32_dev(s), i32_dev(pos), 2048))
+    rows = np.array([0, 1, 2, 6, 7, 11, 100, 255, 256, 301, 510, 511])
+    ref = oracle.topk(s[:, rows], pos[:, rows], 2048)
+    np.testing.assert_array_equal(got[:, rows], ref)
+
+
 def test_topk_many_rows(dsa):
     # 600 rows of ragged visible lengths, tied rows overflowing the candidate list
     rng = np.random.default_rng(14)
