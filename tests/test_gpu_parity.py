@@ -401,6 +401,21 @@ def test_verify_ragged_vocab(dsa):
     check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
 
 
+def test_verify_vocab_beyond_64_chunks(dsa):
+    # V = 600001: 74 chunks of 8192, so the accept block's chunk scan runs over
+    # two 64-chunk groups; V odd takes the element-wise loads
+    rng = np.random.default_rng(73)
+    B, S, V = 3, 2, 600001
+    say("verify V=%d" % V)
+    t = (rng.standard_normal((B, S + 1, V)) * 2).astype(np.float32)
+    d = (0.5 * t[:, :S] + 0.9 * rng.standard_normal((B, S, V)) * 2).astype(np.float32)
+    tok = np.argmax(d + rng.gumbel(size=d.shape), axis=-1).astype(np.int32)
+    u = rng.random((B, S)).astype(np.float32)
+    ur = np.array([0.02, 0.6, 0.995], np.float32)
+    ms, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
+    check_verify(host(ms), host(na), host(nx), t, d, tok, u, ur)
+
+
 def test_verify_residual_without_mass_samples_p(dsa):
     # draft == target and a rejected out-of-vocabulary token: max(p - q, 0) has no
     # mass, so the resample draws from p of the rejected step
