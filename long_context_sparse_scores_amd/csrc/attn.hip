@@ -838,15 +838,15 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 
 // Merge the split partials of one (query, head): with lse_s the log2-sum-exp of
 // split s, out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
-// the numerator summed in split order.  One 128-thread block per (query, head),
-// 4 dims per thread; blocks numbered like the split kernel so each reads
-// partials from its own XCD's L2.
-constexpr int kCombineThreads = 128;
+// the numerator summed in split order.  One wave per (query, head), 8 dims
+// per lane (16-byte loads and stores); blocks numbered like the split kernel
+// so each reads partials from its own XCD's L2.
+constexpr int kCombineThreads = kWave;
+static_assert(kCombineThreads * 8 == kDv, "8 value dims per lane");
 
-// Every wave derives the split weights itself: lane s holds split s's
-// log2-sum-exp, the maximum and the denominator come from wave reductions, and
-// the weights reach the accumulation through readlane, so the block needs no
-// barrier.  The loads of all NB >= nsplit partials go out first (NB = 8 when
+// Lane s holds split s's log2-sum-exp, the maximum and the denominator come
+// from wave reductions, and the weights reach the accumulation through
+// readlane.  The loads of all NB >= nsplit partials go out first (NB = 8 when
 // there are at most 8 splits, else 16).
 template <int NB>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uint16_t* __restrict__ part_o,
@@ -861,12 +861,12 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     if (bt >= rows) return;
     const int lane = lane_id();
     const float* pl = part_lse + (int64_t)bt * nsplit * kHq + head;  // split s at pl[s * kHq]
-    const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 4 * threadIdx.x;
-    uint2 v[NB];
+    const uint16_t* po = part_o + ((int64_t)bt * nsplit * kHq + head) * kDv + 8 * lane;
+    u32x4_t v[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
         const int sp = min(u, nsplit - 1);  // past the end: a valid split, weight 0 below
-        v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)sp * kHq * kDv);
+        v[u] = *reinterpret_cast<const u32x4_t*>(po + (int64_t)sp * kHq * kDv);
     }
     const float ls = lane < nsplit ? pl[(int64_t)lane * kHq] : -INFINITY;
     float M = ls;
@@ -877,19 +877,22 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, kWave);
     const uint32_t a_bits = __float_as_uint(a);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
         const float w = u < nsplit ? __uint_as_float(__builtin_amdgcn_readlane(a_bits, u)) : 0.0f;
-        acc[0] += w * __uint_as_float(v[u].x << 16);
-        acc[1] += w * __uint_as_float(v[u].x & 0xFFFF0000u);
-        acc[2] += w * __uint_as_float(v[u].y << 16);
-        acc[3] += w * __uint_as_float(v[u].y & 0xFFFF0000u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * __uint_as_float(v[u][e] << 16);
+            acc[2 * e + 1] += w * __uint_as_float(v[u][e] & 0xFFFF0000u);
+        }
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    *reinterpret_cast<uint2*>(out + ((int64_t)bt * kHq + head) * kDv + 4 * threadIdx.x) =
-        make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
-    if (lse && threadIdx.x == 0)
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *reinterpret_cast<u32x4_t*>(out + ((int64_t)bt * kHq + head) * kDv + 8 * lane) = o;
+    if (lse && lane == 0)
         lse[(int64_t)bt * kHq + head] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
