@@ -346,6 +346,49 @@ def test_group_eight_layers(dsa):
         assert_attn_close(host(outs[l]), ref_outs[l], "layer %d" % l)
 
 
+def test_group_on_side_stream_and_in_graph(dsa):
+    # The entry points only enqueue work on the caller's stream: on a side
+    # stream, and captured in a graph replayed several times with eager work
+    # between the replays, the group gives the eager result bit for bit.
+    cfg = synth.TINY
+    say("group on a side stream and in a graph")
+    qi, w, ki, pos = bf16_dev(cfg.q_idx()), f32_dev(cfg.w()), bf16_dev(cfg.k_idx()), i32_dev(cfg.q_pos())
+    dq = [bf16_dev(cfg.q_attn(l)) for l in range(cfg.n_layers)]
+    dkv = [bf16_dev(cfg.kv(l)) for l in range(cfg.n_layers)]
+    idx0, outs0, _ = dsa.layer_group(qi, w, ki, pos, cfg.k, dq, dkv, cfg.sm_scale)
+    torch.cuda.synchronize()
+
+    def same(idx, outs):
+        return torch.equal(idx, idx0) and all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+                                              for a, b in zip(outs, outs0))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        idx1, outs1, _ = dsa.layer_group(qi, w, ki, pos, cfg.k, dq, dkv, cfg.sm_scale)
+    side.synchronize()
+    assert same(idx1, outs1)
+
+    idx2 = torch.full_like(idx0, -7)
+    outs2 = [torch.zeros_like(o) for o in outs0]
+    ws = torch.empty(dsa.layer_group_workspace_size(
+        dsa.make_group_args(qi, w, ki, pos, cfg.k, dq, dkv, cfg.sm_scale, idx2, outs2, None)),
+        dtype=torch.uint8, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dsa.layer_group(qi, w, ki, pos, cfg.k, dq, dkv, cfg.sm_scale, ws=ws, idx_out=idx2, outs=outs2)
+    for r in range(3):
+        idx2.fill_(-7)
+        for o in outs2:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(idx2, outs2), r
+        dsa.layer_group(qi, w, ki, pos, cfg.k, dq, dkv, cfg.sm_scale)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ verification
 @pytest.mark.parametrize("rho", [0.0, 0.9, 1.0])
 def test_verify_small(dsa, rho):
