@@ -112,7 +112,8 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // the row indices with no scalar dependency chain; only the LDS destinations
 // are wave-uniform, and they do not depend on the row list.  rows_lds holds -1
 // for every masked or missing entry (canonicalised when the list is loaded), so
-// such rows read row 0 (finite values) and get P = 0.
+// such rows read row 0; their scores are discarded and their value dims are
+// cleared in LDS before P.V.
 struct GatherPlan {
     const uint16_t* src[8];  // this lane's chunk of the main part of row 8w+i
     uint32_t lds[8];         // wave-uniform LDS byte addresses of the rows' main parts
@@ -330,63 +331,9 @@ __device__ __forceinline__ void qk_partial(const uint16_t* tq, const TileAddr& a
     }
 }
 
-// Epilogue of both kernels: denominators (and reference maxima) of all 64
-// heads from their owner waves, then the normalised output of this split (or
-// of the whole list) and its log-sum-exp.
-constexpr int kStageRow = 2 * kDv + 16;  // bytes per output row staged in LDS (64 rows: 65 KiB)
-
-template <bool DIRECT>
-__device__ __forceinline__ void store_output(const PvAcc& acc, const SoftmaxState& st, f32x4_t* sx, void* stage,
-                                             int wave, int lane, int bt, int split, int nsplit,
-                                             uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int c = lane & 15;
-    const int g = lane >> 4;
-    float lsum = st.lsum;
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
-    const float m_ref = st.m_ref;
-    float* stats = reinterpret_cast<float*>(sx);  // free now: [0, 64) sums, [64, 128) maxima
-    if (g == 0) {
-        stats[16 * wave + c] = lsum;
-        stats[64 + 16 * wave + c] = m_ref;
-    }
-    lds_barrier();
-    float inv[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-        const float ls = stats[16 * hb + c];
-        inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
-    }
-    // The 64 x 512 bf16 result goes through the (now free) tile LDS, rows padded
-    // to 1040 bytes so that these 8-byte writes hit every bank once, and then
-    // out as whole 1 KiB rows: one 16-byte store per lane per head.
-    char* st8 = reinterpret_cast<char*>(stage);
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const f32x4_t& o = acc.o[d][hb];
-            *reinterpret_cast<uint2*>(st8 + (16 * hb + c) * kStageRow + 2 * (128 * wave + 16 * d + 4 * g)) =
-                make_uint2(pack_bf16x2(o[0] * inv[hb], o[1] * inv[hb]), pack_bf16x2(o[2] * inv[hb], o[3] * inv[hb]));
-        }
-    lds_barrier();
-    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int h = 16 * wave + i;
-        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
-            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
-    }
-    const int head = 16 * wave + c;
-    if (DIRECT) {
-        if (lse && g == 0)
-            lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (m_ref + log2f(lsum)) * 0.69314718055994531f : -INFINITY;
-        return;
-    }
-    // Normalised partial output (bf16) and its log2-sum-exp; an empty split has lse -inf.
-    if (g == 0) part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? m_ref + log2f(lsum) : -INFINITY;
-}
+// Output rows staged in LDS by the epilogue: 64 rows of 512 bf16, padded to
+// 1040 bytes so that the 8-byte staging writes hit every bank once (65 KiB).
+constexpr int kStageRow = 2 * kDv + 16;
 
 // ------------------------------------------------------------------ P.V helpers of the bf16 tiles
 __device__ __forceinline__ void load_p(const bf16x8_t* __restrict__ pl, int lane, bf16x8_t (&pbv)[4]) {
@@ -453,7 +400,7 @@ __device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ 
         const int n = wave + 4 * i;                 // < 18 for the loads this wave issues
         const int slot = 64 * n + lane;
         const int r = min(slot / kChunks8, kRows - 1);
-        // rows_lds holds -1 for masked or missing rows: they read row 0 (finite values, P = 0)
+        // rows_lds holds -1 for masked or missing rows: they read row 0 (scores discarded, values cleared)
         const uint32_t rid = (uint32_t)max(rows_lds[t * kRows + r], 0);
         const int s = (slot - kChunks8 * r) ^ swz8(r);
         gp.off[i] = slot < kRows * kChunks8 ? rid * kRow8 + 16u * (uint32_t)s : 0u;  // L <= 2^22 rows
@@ -764,6 +711,21 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         static_assert(FP8 || (STAGES >= 3 && STAGES <= 4), "bf16 wait counts cover one or two later tiles in flight");
         for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
         __syncthreads();  // rows_lds ready
+        // Masked or missing entries gather row 0, and their scores are discarded;
+        // their value rows are cleared before P.V (P = 0 would not hide an Inf or
+        // NaN there).  Wave vw clears the rows r = vw (mod 4) of tile t.
+        auto clear_masked = [&](int t) __attribute__((always_inline)) {
+            uint32_t m = ~(uint32_t)__ballot(rows_lds[t * kRows + (lane & 31)] >= 0) & (0x11111111u << vw);
+            while (m) {
+                const int r = __builtin_ctz(m);
+                m &= m - 1;
+                if constexpr (FP8) {  // value bytes 0..511: chunk positions 36r .. 36r+31
+                    if (lane < 32) *reinterpret_cast<u32x4_t*>(buf(t) + kRow8 * r + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+                } else {              // the 1 KiB main part holds the 512 value dims
+                    *reinterpret_cast<u32x4_t*>(buf(t) + 1024 * r + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+        };
         for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
             const auto gp = plan_tile<FP8>(kvb, rows_lds, t, buf(t), vw, lane);
 #pragma unroll
@@ -780,6 +742,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         auto next = plan_tile<FP8>(kvb, rows_lds, min(kStages - 1, ntiles - 1), buf(kStages - 1), vw, lane);
         next.active = kStages - 1 < ntiles;
         lds_barrier();  // tile 0 in LDS
+        clear_masked(0);  // beside the score waves' Q.K^T, whose masked scores are discarded
         lds_barrier();  // (score waves: partials of tile 0 exchanged)
         bf16x8_t pbv[4];
         for (int t = 0; t + 1 < ntiles; ++t) {
@@ -797,6 +760,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
             nx.active = t + kStages < ntiles;
             if constexpr (FP8) pv_tile8(buf(t), ad8, pbv, vw, acc);
             else pv_tile(buf16(t), ad, pbv, vw, acc);
+            clear_masked(t + 1);  // its Q.K^T is done; its P.V comes after the next barriers
             next = nx;
         }
         lds_barrier();  // P^T and rescale record of the last tile visible
@@ -840,7 +804,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 // split s, out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
 // the numerator summed in split order.  One wave per (query, head), 8 dims
 // per lane (16-byte loads and stores); blocks numbered like the split kernel
-// so each reads partials from its own XCD's L2.
+// so each reads partials from its own XCD's L2.  (Eight heads per workgroup,
+// 256 workgroups instead of 2048 at decode 128K, measured the same: 5.2 us.)
 constexpr int kCombineThreads = kWave;
 static_assert(kCombineThreads * 8 == kDv, "8 value dims per lane");
 

@@ -14,15 +14,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16];
 // result register r of lane l is D[4*(l/16) + r][l%16].
@@ -57,50 +48,50 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
-// Exclusive prefix sum across a block of NW waves; `scratch` holds NW words of LDS.
-// Every thread of the block must call it.
-template <int NW>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* scratch, uint32_t* total) {
-    const int w = threadIdx.x / kWave;
-    uint32_t inc = wave_incl_scan(x);
-    if (lane_id() == kWave - 1) scratch[w] = inc;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        uint32_t v = scratch[i];
-        before += (i < w) ? v : 0u;
-        tot += v;
-    }
-    __syncthreads();
-    *total = tot;
-    return before + inc - x;
-}
-
 // ------------------------------------------------------------- launch interfaces
-// Words [r*stride, r*stride + count) of a uint32 buffer, for every row r: a
-// range some later kernel needs zeroed, which the indexer clears on the way.
-struct ZeroRange {
+// Top-k state the indexer prepares for the selection that follows it (layer
+// group): for every row r, the uint32 words at base + r*stride.  Words
+// [zero_off, zero_off + zero_count) are cleared; when `hist` is set, the row's
+// histogram of the top 11 bits of the order-preserving score keys (visible
+// keys only) is added into words [0, 2048), which must hold zeros when the
+// indexer starts.
+struct TopkPrep {
     uint32_t* base = nullptr;
     int64_t stride = 0;
-    int count = 0;
+    int zero_off = 0;
+    int zero_count = 0;
+    bool hist = false;
 };
+
+constexpr int kTopBins = 2048;  // bins of the top score-key digit (11 bits)
+
+// Whether the indexer launch for chunks of T queries per sequence can add the
+// top-digit histogram (TopkPrep::hist): the per-query decode kernels can, the
+// multi-query tile kernels cannot.
+bool indexer_counts_histogram(int T);
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                           const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                          ZeroRange zero = ZeroRange());
+                          TopkPrep prep = TopkPrep());
 
 // The same scores from E4M3 index queries and keys (one byte per element).
 hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                               const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                              ZeroRange zero = ZeroRange());
+                              TopkPrep prep = TopkPrep());
 
 size_t topk_ws_bytes(int rows, int L, int k);
-// The part of the top-k workspace that must be zero when the selection starts.
-ZeroRange topk_state_range(void* ws, int rows, int L);
-// state_zeroed: the caller has already cleared topk_state_range (e.g. through the indexer).
+// What the indexer prepares before a selection: with `hist`, it clears the
+// counters and adds the top-digit histogram (the histogram words must be zero
+// before it starts: every selection leaves them zero); without, it clears both.
+TopkPrep topk_prep(void* ws, int rows, int L, bool hist);
+// How much of the selection's state is ready when launch_topk is called.
+enum class TopkState {
+    kNone,       // nothing: clear the state and build the histogram
+    kCleared,    // the histogram and counters are zero (TopkPrep without hist)
+    kHistogram,  // counters zero and the histogram complete (TopkPrep with hist)
+};
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, bool state_zeroed = false);
+                       hipStream_t stream, TopkState state = TopkState::kNone);
 
 int attn_num_splits(int rows, int k);
 size_t attn_ws_bytes(int rows, int k);

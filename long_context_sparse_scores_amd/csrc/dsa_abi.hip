@@ -209,14 +209,18 @@ int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void*
     void* topk_ws = base + dsa::align_up((size_t)rows * L * sizeof(float), 256);
     void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
     hipStream_t s = (hipStream_t)stream;
-    // the indexer also clears the top-k state, which saves the selection a launch
-    const dsa::ZeroRange topk_state = dsa::topk_state_range(topk_ws, rows, L);
+    // The indexer prepares the selection: the per-query decode kernels clear its
+    // counters and add the top-digit histogram of the scores (two launches
+    // fewer); the multi-query tile kernels clear the state for the histogram pass.
+    const bool hist = dsa::indexer_counts_histogram(T);
+    const dsa::TopkPrep prep = dsa::topk_prep(topk_ws, rows, L, hist);
     hipError_t e = idx_fp8 ? dsa::launch_indexer_fp8(a->q_idx_fp8, a->w, a->k_idx_fp8, a->k_bstride, a->q_pos, B, T,
-                                                     L, scores, s, topk_state)
+                                                     L, scores, s, prep)
                            : dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores,
-                                                 s, topk_state);
+                                                 s, prep);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
-    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s, /*state_zeroed=*/true);
+    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s,
+                         hist ? dsa::TopkState::kHistogram : dsa::TopkState::kCleared);
     if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
     for (int l = 0; l < a->n_layers; ++l) {
         e = a->kv_fp8[l] ? dsa::launch_attn_fp8(a->q[l], a->kv_fp8[l], a->kv_bstride[l], a->idx_out, B, T, L, k,

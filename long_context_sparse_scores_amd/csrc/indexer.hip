@@ -35,13 +35,38 @@ constexpr int kAhead = 4;                      // tiles loaded ahead of the one 
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeTiles = 16;               // tiles per wave
 
+// Top-k preparation (TopkPrep) by a decode launch: the first key block of each
+// row clears the row's counters; with `hist`, every block counts the top 11-bit
+// digit of each visible score in LDS as it is computed and, at the end, adds
+// the non-zero bins to the row's histogram.
+__device__ __forceinline__ void prep_start(const TopkPrep& prep, int row, int blk, uint32_t* hist_lds, int nthreads) {
+    if (prep.base && blk == 0)
+        for (int i = threadIdx.x; i < prep.zero_count; i += nthreads)
+            prep.base[row * prep.stride + prep.zero_off + i] = 0u;
+    if (prep.hist) {
+        for (int i = threadIdx.x; i < kTopBins; i += nthreads) hist_lds[i] = 0u;
+        __syncthreads();  // before the first key is counted (and before any key load is in flight)
+    }
+}
+
+__device__ __forceinline__ void prep_flush(const TopkPrep& prep, int row, const uint32_t* hist_lds, int nthreads) {
+    __syncthreads();  // every wave's counts are in
+    uint32_t* gh = prep.base + row * prep.stride;
+    for (int i = threadIdx.x; i < kTopBins; i += nthreads) {
+        const uint32_t v = hist_lds[i];
+        if (v) atomicAdd(&gh[i], v);
+    }
+}
+
 template <int kWaves, int kTilesPerWave>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
-    ZeroRange zero) {
+    TopkPrep prep) {
     constexpr int kKeysPerBlock = kWaves * kTile * kTilesPerWave;
+    static_assert(kTilesPerWave % 4 == 0, "the four lane groups take whole tiles each");
     __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * 2 * kTileBytes / 2];
+    __shared__ uint32_t hist_lds[kTopBins];
     const int row = blockIdx.x / nblk;  // b*T + t
     const int blk = blockIdx.x % nblk;
     const int b = row / T;
@@ -50,8 +75,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     const int c = lane & 15;  // key within tile (B/C column)
     const int g = lane >> 4;  // lane group: 8-dim slice of each 32-dim step; head row block in C
     const int64_t p = q_pos[row];
-    if (zero.base && blk == 0)
-        for (int i = threadIdx.x; i < zero.count; i += kWaves * kWave) zero.base[row * zero.stride + i] = 0u;
+    prep_start(prep, row, blk, hist_lds, kWaves * kWave);
 
     // A operands: q rows (heads) 16*ht + c, dims 32*kk + 8*g .. +7.
     bf16x8_t qa[2][4];
@@ -114,6 +138,10 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
         part += __shfl_xor(part, 16, kWave);
         part += __shfl_xor(part, 32, kWave);
         sc[j] = part;
+        if (prep.hist && g == (j & 3)) {  // lane group g counts the tiles j = g (mod 4)
+            const int64_t key = tile_key0(j) + c;
+            if (key < L && key <= p) atomicAdd(&hist_lds[score_key(part) >> 21], 1u);
+        }
     }
     float* out = scores + (int64_t)row * L;
     if (g == 0) {
@@ -123,6 +151,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
             if (key < L) out[key] = key <= p ? sc[j] : -INFINITY;
         }
     }
+    if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
 }
 
 // ------------------------------------------------------------------ FP8 (E4M3) index keys
@@ -158,9 +187,11 @@ template <int kWaves, int kTilesPerWave, int kAhead8>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
-    ZeroRange zero) {
+    TopkPrep prep) {
     constexpr int kKeysPerBlock = kWaves * kTile8 * kTilesPerWave;
+    static_assert(kTilesPerWave % 2 == 0, "lane groups 2, 3 take the odd tiles");
     __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * kTile8Bytes];
+    __shared__ uint32_t hist_lds[kTopBins];
     const int row = blockIdx.x / nblk;  // b*T + t
     const int blk = blockIdx.x % nblk;
     const int b = row / T;
@@ -169,8 +200,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
     const int c = lane & 15;
     const int g = lane >> 4;
     const int64_t p = q_pos[row];
-    if (zero.base && blk == 0)
-        for (int i = threadIdx.x; i < zero.count; i += kWaves * kWave) zero.base[row * zero.stride + i] = 0u;
+    prep_start(prep, row, blk, hist_lds, kWaves * kWave);
 
     // A operands: head 16*ht + c, dims 32*kk + 8*g .. +7 (8 codes).
     long qa[2][4];
@@ -236,8 +266,12 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
             v += __shfl_xor(v, 32, kWave);
             part[kbk] = v;
         }
-        // every lane of column c now holds both sums; lane group g < 2 keeps key 16*g + c
+        // every lane of column c now holds both sums; lane group g keeps key 16*(g & 1) + c
         sc[j] = (g & 1) ? part[1] : part[0];
+        if (prep.hist && (g >> 1) == (j & 1)) {  // groups 0, 1 count the even tiles, groups 2, 3 the odd ones
+            const int64_t key = tile_key0(j) + 16 * (g & 1) + c;
+            if (key < L && key <= p) atomicAdd(&hist_lds[score_key(sc[j]) >> 21], 1u);
+        }
     }
     float* out = scores + (int64_t)row * L;
     if (g < 2) {
@@ -247,6 +281,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
             if (key < L) out[key] = key <= p ? sc[j] : -INFINITY;
         }
     }
+    if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
 }
 
 // ------------------------------------------------------------------ multi-query (prefill) chunks
@@ -269,7 +304,7 @@ constexpr int kPrefillMinQueries = 8;          // chunks of at least this many q
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb,
-    float* __restrict__ scores, ZeroRange zero) {
+    float* __restrict__ scores, TopkPrep prep) {
     __shared__ __attribute__((aligned(16))) uint16_t stage[2 * kPfTileBytes / 2];
     const int kb_i = blockIdx.x % nkb;           // key block
     const int qg = (blockIdx.x / nkb) % nqg;     // query group within the sequence
@@ -280,16 +315,15 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const int g = lane >> 4;
     const int t0 = qg * kPfQueries + kPfQPerWave * wave;  // this wave's first query
 
-    if (zero.base && kb_i == 0)  // rows of this group, once
-        for (int i = threadIdx.x; i < kPfQueries * zero.count; i += 256) {
-            const int t = qg * kPfQueries + i / zero.count;
-            if (t < T) zero.base[((int64_t)b * T + t) * zero.stride + i % zero.count] = 0u;
+    if (prep.base && kb_i == 0)  // rows of this group, once
+        for (int i = threadIdx.x; i < kPfQueries * prep.zero_count; i += 256) {
+            const int t = qg * kPfQueries + i / prep.zero_count;
+            if (t < T) prep.base[((int64_t)b * T + t) * prep.stride + prep.zero_off + i % prep.zero_count] = 0u;
         }
 
     // A operands and head weights of the wave's 4 queries (past the end: the last query, never stored)
     bf16x8_t qa[kPfQPerWave][2][4];
     float wv[kPfQPerWave][2][4];
-    int64_t prow[kPfQPerWave];
 #pragma unroll
     for (int i = 0; i < kPfQPerWave; ++i) {
         const int t = min(t0 + i, T - 1);
@@ -304,7 +338,6 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
             for (int r = 0; r < 4; ++r) wv[i][ht][r] = w[row * kH + 16 * ht + 4 * g + r];
-        prow[i] = row;
     }
     // this lane stores query 4w+g
     const int my_t = t0 + g;
@@ -377,7 +410,6 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         if (j + 1 < ntiles) store_tile(j + 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    (void)prow;
 }
 
 
@@ -403,7 +435,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x128_fp8(i32x8_t a, i32x8_t b, f32x4
 __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb, float* __restrict__ scores,
-    ZeroRange zero) {
+    TopkPrep prep) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2 * kPf8TileBytes];
     const int kb_i = blockIdx.x % nkb;
     const int qg = (blockIdx.x / nkb) % nqg;
@@ -414,10 +446,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     const int g = lane >> 4;
     const int t0 = qg * kPfQueries + kPfQPerWave * wave;
 
-    if (zero.base && kb_i == 0)
-        for (int i = threadIdx.x; i < kPfQueries * zero.count; i += 256) {
-            const int t = qg * kPfQueries + i / zero.count;
-            if (t < T) zero.base[((int64_t)b * T + t) * zero.stride + i % zero.count] = 0u;
+    if (prep.base && kb_i == 0)
+        for (int i = threadIdx.x; i < kPfQueries * prep.zero_count; i += 256) {
+            const int t = qg * kPfQueries + i / prep.zero_count;
+            if (t < T) prep.base[((int64_t)b * T + t) * prep.stride + prep.zero_off + i % prep.zero_count] = 0u;
         }
 
     // A operands: head 16*ht + c of the wave's 4 queries, bytes 32g .. 32g+31
@@ -507,56 +539,58 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
 }
 }  // namespace
 
+bool indexer_counts_histogram(int T) { return T < kPrefillMinQueries; }
+
 template <int W, int N>
 hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                               const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                              ZeroRange zero) {
+                              TopkPrep prep) {
     constexpr int keys_per_block = W * kTile * N;
     const int nblk = (L + keys_per_block - 1) / keys_per_block;
     dim3 grid((unsigned)((int64_t)nblk * B * T));
     hipLaunchKernelGGL((indexer_decode_kernel<W, N>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx, k_bstride,
-                       q_pos, T, L, nblk, scores, zero);
+                       q_pos, T, L, nblk, scores, prep);
     return hipGetLastError();
 }
 
 template <int W, int N, int A>
 hipError_t launch_indexer_fp8_cfg(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                                   const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                                  ZeroRange zero) {
+                                  TopkPrep prep) {
     constexpr int keys_per_block = W * kTile8 * N;
     const int nblk = (L + keys_per_block - 1) / keys_per_block;
     dim3 grid((unsigned)((int64_t)nblk * B * T));
     hipLaunchKernelGGL((indexer_decode_fp8_kernel<W, N, A>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx,
-                       k_bstride, q_pos, T, L, nblk, scores, zero);
+                       k_bstride, q_pos, T, L, nblk, scores, prep);
     return hipGetLastError();
 }
 
 hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                               const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                              ZeroRange zero) {
+                              TopkPrep prep) {
     if (T >= kPrefillMinQueries) {
         const int nqg = (T + kPfQueries - 1) / kPfQueries;
         const int nkb = (L + kPfKeysPerBlock - 1) / kPfKeysPerBlock;
         hipLaunchKernelGGL(indexer_prefill_fp8_kernel, dim3((unsigned)((int64_t)B * nqg * nkb)), dim3(256), 0, stream,
-                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
+                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, prep);
         return hipGetLastError();
     }
     return launch_indexer_fp8_cfg<kDecode8Waves, kDecode8Tiles, kDecode8Ahead>(q_idx, w, k_idx, k_bstride, q_pos, B,
-                                                                               T, L, scores, stream, zero);
+                                                                               T, L, scores, stream, prep);
 }
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                           const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                          ZeroRange zero) {
+                          TopkPrep prep) {
     if (T >= kPrefillMinQueries) {
         const int nqg = (T + kPfQueries - 1) / kPfQueries;
         const int nkb = (L + kPfKeysPerBlock - 1) / kPfKeysPerBlock;
         hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)((int64_t)B * nqg * nkb)), dim3(256), 0, stream,
-                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, zero);
+                           q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, prep);
         return hipGetLastError();
     }
     return launch_indexer_cfg<kDecodeWaves, kDecodeTiles>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, stream,
-                                                          zero);
+                                                          prep);
 }
 
 }  // namespace dsa

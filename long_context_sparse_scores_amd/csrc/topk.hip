@@ -10,8 +10,7 @@
 // significant first).  Each row is cut into slices (a few hundred workgroups
 // over all rows, so a few long rows still fill the chip); a slice is cut
 // into one contiguous range per wave.  The passes:
-//   init    zero the row's global histogram and counters (the layer group
-//           lets the indexer do this instead);
+//   init    zero the row's global histogram and counters;
 //   hist    histogram of the top digit (LDS per slice, non-zero bins added
 //           to the row's histogram);
 //   filter  every slice finds the threshold digit T from that histogram and
@@ -26,9 +25,17 @@
 //           are compacted into LDS and written out in ascending order from a
 //           bitmap of the row's positions (393216 per chunk, in the space the
 //           candidate copy used).
-// The scores are thus read twice (hist, filter), and select never touches
-// them.  (Running select in the last filter workgroup of each row would save
-// a launch, but publishing the candidates across XCDs then takes an L2
+// In the layer group the decode indexer does the first two: it clears the
+// counters and adds the top-digit histogram of the scores it holds in
+// registers, so the scores are read once (filter) and select never touches
+// them.  That histogram must start from zero, and no launch of the group can
+// clear it before the indexer adds to it; so the selection, its last user,
+// clears it for the next call, and a workspace must be zero-filled once before
+// its first use.  The filter checks that the histogram counts the row's
+// visible keys exactly; if not (the workspace was not zero-filled), it counts
+// the row itself, so the result never depends on that.
+// (Running select in the last filter workgroup of each row would save a
+// launch, but publishing the candidates across XCDs then takes an L2
 // write-back per workgroup, which costs far more on this part.)
 // When a row's candidate list overflows its capacity (heavily tied scores),
 // select scans the whole row instead; the result is the same.
@@ -40,7 +47,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSelectThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBins = 2048;
+constexpr int kBins = kTopBins;
 constexpr int kTargetBlocks = 512;   // slices over all rows
 constexpr int kMinSlice = 4096;
 constexpr int kMaxSlices = 512;      // per row
@@ -140,7 +147,8 @@ struct BinPick {
 };
 
 template <int NT>
-__device__ __forceinline__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, uint32_t* scratch, BinPick* result) {
+__device__ __forceinline__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, uint32_t need, uint32_t* scratch,
+                                            BinPick* result, uint32_t* total_out = nullptr) {
     constexpr int per = kBins / NT;
     uint32_t s = 0;
 #pragma unroll
@@ -148,6 +156,7 @@ __device__ __forceinline__ BinPick pick_bin(const HistPart<NT>& hp, int nbins, u
     if (threadIdx.x == 0) *result = BinPick{0u, 0u, 0u};
     uint32_t total;
     const uint32_t above = excl_scan<NT>(s, scratch, &total);  // count in higher bins (also orders the reset)
+    if (total_out) *total_out = total;
     if (above < need && need <= above + s) {
         uint32_t acc = above;
 #pragma unroll
@@ -476,6 +485,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     __shared__ uint32_t stage_pos[kWaves][kStage], stage_key[kWaves][kStage];
     __shared__ uint32_t scratch[kWaves];
     __shared__ BinPick pick;
+    __shared__ uint32_t own_hist[kBins];  // only when the row's histogram cannot be trusted
 
     // the row's top-digit histogram, then this wave's first batch of scores
     const HistPart<kThreads> hp = load_hist<kThreads>(rw.hist1, kBins);
@@ -491,7 +501,19 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         }
     };
     load_batch(w0);
-    const BinPick b0 = pick_bin<kThreads>(hp, kBins, (uint32_t)k, scratch, &pick);
+    uint32_t total;
+    BinPick b0 = pick_bin<kThreads>(hp, kBins, (uint32_t)k, scratch, &pick, &total);
+    if (total != (uint32_t)n) {
+        // The histogram does not count the row's n visible keys exactly once: it
+        // did not start from zero (a workspace that was not zero-filled before
+        // its first use).  Count this row here, from its scores.
+        for (int i = threadIdx.x; i < kBins; i += kThreads) own_hist[i] = 0u;
+        lds_sync();
+        for (int64_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&own_hist[score_key(row_scores[i]) >> 21], 1u);
+        lds_sync();
+        const HistPart<kThreads> hp2 = load_hist<kThreads>(own_hist, kBins);
+        b0 = pick_bin<kThreads>(hp2, kBins, (uint32_t)k, scratch, &pick);
+    }
     const uint32_t T = b0.bin;
     if (slice == 0 && threadIdx.x == 0) {  // for the selection
         rw.ctr[kStT] = T;
@@ -550,12 +572,16 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float
     const int row = blockIdx.x;
     const int64_t n = n_visible(q_pos, row, L);
     int32_t* out = idx + (int64_t)row * k;
+    const RowWs rw = row_ws(ws, row, lo);
+    // The filter pass was the histogram's last reader: leave it zero for the
+    // next selection, whose indexer adds into it.
+    for (int i = threadIdx.x; i < kBins; i += kSelectThreads) rw.hist1[i] = 0u;
     if (n <= k) {
         for (int j = threadIdx.x; j < k; j += kSelectThreads) out[j] = j < n ? j : -1;
         return;
     }
     __shared__ SelectLds<kSelectThreads> sl;
-    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, row_ws(ws, row, lo), lo.cap, out, sl);
+    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, rw, lo.cap, out, sl);
 }
 
 Layout make_layout(int rows, int L) {
@@ -582,24 +608,26 @@ size_t topk_ws_bytes(int rows, int L, int k) {
     return align_up((size_t)rows * make_layout(rows, L).row_words() * sizeof(uint32_t), 256);
 }
 
-ZeroRange topk_state_range(void* ws, int rows, int L) {
-    (void)rows;
+TopkPrep topk_prep(void* ws, int rows, int L, bool hist) {
     const Layout lo = make_layout(rows, L);
-    ZeroRange z;
-    z.base = reinterpret_cast<uint32_t*>(ws);  // each row's words start with hist1, then the counters
-    z.stride = (int64_t)lo.row_words();
-    z.count = kBins + kCtrWords;
-    return z;
+    TopkPrep p;
+    p.base = reinterpret_cast<uint32_t*>(ws);  // each row's words start with hist1, then the counters
+    p.stride = (int64_t)lo.row_words();
+    p.zero_off = hist ? kBins : 0;
+    p.zero_count = hist ? kCtrWords : kBins + kCtrWords;
+    p.hist = hist;
+    return p;
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, bool state_zeroed) {
+                       hipStream_t stream, TopkState state) {
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
-    if (!state_zeroed) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
+    if (state == TopkState::kNone) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
     // finer LDS bins for long slices (measured: prefill 4096 x 128K rows, one slice per row)
-    hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
-                       dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
+    if (state != TopkState::kHistogram)
+        hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
+                           dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        idx);

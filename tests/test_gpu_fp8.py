@@ -346,3 +346,24 @@ def test_fullsize_prefill_fp8_index_equals_bf16(dsa):
         say("  oracle row t=%d" % t)
         ref = oracle.indexer_scores(qi8[:, t:t + 1], w[:, t:t + 1], ki, pos[:, t:t + 1], fp8=True)
         _bits_equal(s8[0, t].cpu().numpy(), ref[0, 0])
+
+
+def test_attn_fp8_nan_row_not_selected(dsa):
+    # E4M3 rows 0 and 1 hold NaN codes and are never selected; masked entries
+    # gather row 0 and must not carry its NaNs into the output.
+    rng = np.random.default_rng(54)
+    B, T, L, k = 1, 3, 3000, 300
+    say("fp8 attn NaN rows not selected")
+    q = synth.normal_bf16(55, 1, (B, T, 64, 576))
+    kv = synth.to_e4m3(synth.bf16_to_f32(synth.normal_bf16(55, 2, (B, L, 576))))
+    kv[0, 0, :] = 0x7F
+    kv[0, 1, :] = 0xFF
+    idx = np.sort(rng.choice(np.arange(2, L), size=(B, T, k)), axis=2).astype(np.int32)
+    idx[0, 0, ::4] = -1
+    idx[0, 1, -30:] = L + 1
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), u8_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16, kv_fp8=True)
+    assert_attn_close(got, ref)
+    np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)

@@ -309,6 +309,61 @@ def test_attn_direct_ragged_k(dsa):
     assert_attn_close(got, ref)
 
 
+def _unordered_list(rng, L, k, T):
+    """Index lists in no particular order, with repeated rows and masked
+    entries (-1 and positions >= L) spread through them."""
+    idx = rng.integers(2, L, size=(1, T, k)).astype(np.int32)
+    idx[0, :, 1::9] = idx[0, :, 0::9][:, :idx[0, :, 1::9].shape[1]]  # every ninth pair repeats a row
+    idx[0, :, 5::13] = -1
+    idx[0, :, 7::29] = L + 11
+    return idx
+
+
+@pytest.mark.parametrize("T", [3, 300])
+def test_attn_unordered_duplicates_masked(dsa, T):
+    # The entry point accepts any order: a permuted list with repeated rows
+    # (each counted once per occurrence) and masked entries in the middle.
+    # T=3: split lists and the combine; T=300: one workgroup per whole list.
+    rng = np.random.default_rng(50 + T)
+    B, L, k = 1, 5000, 700
+    say("attn unordered, duplicates, masked T=%d" % T)
+    q = synth.normal_bf16(51, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(51, 2, (B, L, 576))
+    idx = _unordered_list(rng, L, k, T)
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    sample = list(range(T)) if T < 8 else [0, 150, 299]
+    ref, ref_lse = oracle.sparse_mla_attn(q[:, sample], kv, idx[:, sample], 1 / 16)
+    assert_attn_close(host(out)[:, sample], ref)
+    np.testing.assert_allclose(host(lse)[:, sample], ref_lse, atol=LSE_TOL, rtol=0)
+    # the same multiset of rows in ascending order gives the same result (within rounding)
+    srt = np.sort(idx, axis=2)
+    out2 = host(dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(srt), 1 / 16))
+    assert_attn_close(out2[:, sample], ref)
+
+
+def test_attn_nonfinite_rows_not_selected(dsa):
+    # Rows 0 and 1 hold NaN and Inf and are never selected; masked entries
+    # (which gather row 0) must not carry them into the output.
+    rng = np.random.default_rng(52)
+    B, T, L, k = 1, 3, 3000, 300
+    say("attn non-finite rows not selected")
+    q = synth.normal_bf16(53, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(53, 2, (B, L, 576))
+    kv[0, 0, :] = 0x7FC0  # bf16 NaN
+    kv[0, 1, :] = 0x7F80  # bf16 +Inf
+    idx = np.sort(rng.choice(np.arange(2, L), size=(B, T, k)), axis=2).astype(np.int32)
+    idx[0, 0, ::3] = -1
+    idx[0, 1, -40:] = L + 5
+    idx[0, 2, :] = -1
+    idx[0, 2, 17] = 1234
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    got = host(out)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(host(lse)))
+    ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16)
+    assert_attn_close(got, ref)
+    np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
 # ------------------------------------------------------------------ IndexShare group
 def test_group_tiny(dsa):
     cfg = synth.TINY
@@ -487,3 +542,29 @@ def test_verify_out_of_vocab_token_rejected(dsa):
     ur = np.array([0.5], np.float32)
     _, na, nx = dsa.mtp_draft_verify(f32_dev(t), f32_dev(d), i32_dev(tok), f32_dev(u), f32_dev(ur))
     assert int(host(na)[0]) == 0 and 0 <= int(host(nx)[0]) < V
+
+
+def test_group_workspace_not_zero_filled(dsa):
+    # A workspace should be zero-filled before its first use, because the
+    # indexer adds the top-k histogram into it and every call leaves it zero for
+    # the next.  One that is not (here: every byte 0xAB) still gives the exact
+    # result: the selection sees that the histogram does not count the visible
+    # keys and counts the rows itself.  The second call takes the normal path.
+    cfg = synth.TINY
+    say("group with a workspace that was not zero-filled")
+    qi, w, ki, pos = cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos()
+    qs = [cfg.q_attn(l) for l in range(2)]
+    kvs = [cfg.kv(l) for l in range(2)]
+    dq = [bf16_dev(q) for q in qs]
+    dkv = [bf16_dev(kv) for kv in kvs]
+    _, ref_idx, ref_outs, _ = oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
+    args = dsa.make_group_args(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k, dq, dkv, cfg.sm_scale,
+                               torch.empty((cfg.B, cfg.T, cfg.k), dtype=torch.int32, device=DEV),
+                               [torch.empty((cfg.B, cfg.T, 64, 512), dtype=torch.bfloat16, device=DEV)] * 2)
+    ws = torch.full((dsa.layer_group_workspace_size(args),), 0xAB, dtype=torch.uint8, device=DEV)
+    for call in range(2):
+        idx, outs, _ = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k, dq, dkv,
+                                       cfg.sm_scale, ws=ws)
+        np.testing.assert_array_equal(host(idx), ref_idx, err_msg="call %d" % call)
+        for l in range(2):
+            assert_attn_close(host(outs[l]), ref_outs[l], "call %d layer %d" % (call, l))
