@@ -138,7 +138,7 @@ def main():
     outs = [torch.empty((B, T, cfg.Hq, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
     args_c = dsa.make_group_args(q_idx, w, k_idx, q_pos, k, qs, kvs, cfg.sm_scale, idx, outs)
     ws_bytes = dsa.layer_group_workspace_size(args_c)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled before first use
     lib = dsa.lib()
     import ctypes
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -209,26 +209,30 @@ def main():
                  "attn_ms_per_layer": [round(x, 4) for x in phase[2:]]}
     log("bench: breakdown %s" % breakdown)
 
-    # ---------------- without IndexShare: every layer runs its own indexer and top-k over its own
-    # index-key cache (the same kernels, called per layer); the measured saving of sharing
+    # ---------------- without IndexShare (dsa_layer_group with share = 0): every layer runs its own
+    # indexer and top-k over its own index queries, weights and index-key cache; the measured saving
     ns_ms = None
     if not args.no_nonshared and T == 1:
         def layer_keys(l):
             kb = synth.int_bf16(cfg.seed, synth.T_K_IDX + 100 + l, (B, L, cfg.D))
             return torch.from_numpy(synth.to_e4m3(synth.bf16_to_f32(kb))).to(dev) if args.index_fp8 else to_dev(kb)
 
+        def layer_queries(l):
+            qb = synth.int_bf16(cfg.seed, synth.T_K_IDX + 200 + l, (B, T, cfg.H, cfg.D))
+            return torch.from_numpy(synth.to_e4m3(synth.bf16_to_f32(qb))).to(dev) if args.index_fp8 else to_dev(qb)
+
         k_idx_l = [k_idx] + [layer_keys(l) for l in range(1, nl)]
+        q_idx_l = [q_idx] + [layer_queries(l) for l in range(1, nl)]
+        w_l = [w] + [torch.from_numpy(synth.pow2_f32(cfg.seed, synth.T_K_IDX + 300 + l, (B, T, cfg.H))).to(dev)
+                     for l in range(1, nl)]
         idx_l = [torch.empty_like(idx) for _ in range(nl)]
-        # one single-layer group per layer (the group entry point with n_layers = 1), args built once
-        args_l = [dsa.make_group_args(q_idx, w, k_idx_l[l], q_pos, k, [qs[l]], [kvs[l]], cfg.sm_scale, idx_l[l],
-                                      [outs[l]]) for l in range(nl)]
-        argp_l = [ctypes.byref(a) for a in args_l]
+        args_ns = dsa.make_group_args(q_idx_l, w_l, k_idx_l, q_pos, k, qs, kvs, cfg.sm_scale, idx_l, outs)
+        argp_ns = ctypes.byref(args_ns)
 
         def nonshared_step():
-            for l in range(nl):
-                rc = lib.dsa_layer_group(argp_l[l], ws.data_ptr(), ws_bytes, stream)
-                if rc != 0:
-                    raise RuntimeError(dsa.last_error())
+            rc = lib.dsa_layer_group(argp_ns, ws.data_ptr(), ws_bytes, stream)
+            if rc != 0:
+                raise RuntimeError(dsa.last_error())
 
         for _ in range(2):
             nonshared_step()
@@ -240,7 +244,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ns_ms = e0.elapsed_time(e1) / reps
-        del k_idx_l, idx_l, args_l, argp_l
+        del k_idx_l, q_idx_l, w_l, idx_l, args_ns, argp_ns
         log("bench: without IndexShare %.3f ms per group (shared %.3f ms)" % (ns_ms, ms))
 
     qtok = B * T
@@ -302,8 +306,8 @@ def main():
     if ns_ms is not None:
         line["indexshare"] = {"shared_ms": round(ms, 4), "non_shared_ms": round(ns_ms, 4),
                               "speedup": round(ns_ms / ms, 3),
-                              "note": "non-shared: a one-layer group per layer (indexer + top-k + attention), "
-                                      "each over its own index-key cache"}
+                              "note": "non-shared: dsa_layer_group with share = 0, an indexer and top-k per layer "
+                                      "over that layer's own index queries, weights and index-key cache"}
     if T > 1:  # a prefill chunk is a dense contraction: report the matrix-core fraction as well
         tflops = (idx_flops + attn_flops) / (ms / 1e3) / 1e12
         line["mfma"] = {"flops_per_step": idx_flops + attn_flops, "achieved_tflops": round(tflops, 1),
@@ -529,7 +533,7 @@ def bench_mtp_rounds(cfg, args):
                                  rounds[r]["q_steps"], [kv_cache] * S, cfg.sm_scale, idx, outs) for r in range(R)]
     gptr = [ctypes.byref(a) for a in gargs]
     g_bytes = max(dsa.layer_group_workspace_size(a) for a in gargs)
-    g_ws = torch.empty(g_bytes, dtype=torch.uint8, device=dev)
+    g_ws = torch.zeros(g_bytes, dtype=torch.uint8, device=dev)  # zero-filled before first use
     ver_ws = torch.empty(max(dsa.verify_workspace_size(B, S, V), dsa.lib().mtp_verify_target_only_workspace_size(B, S, V)),
                          dtype=torch.uint8, device=dev)
     n_acc = torch.empty((R, B), dtype=torch.int32, device=dev)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 /* Shapes fixed by the GLM-5.2 config ([TEARDOWN, 刀一 DSA]: index_n_heads 32,
  * index_head_dim 128, index_topk 2048; [TEARDOWN, 刀三 MLA]: kv_lora_rank
@@ -126,8 +126,19 @@ int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstrid
  * writes the shared list to idx_out, then runs dsa_sparse_mla_attn for each
  * layer with that same list, all on `stream`.  Layers stay separate launches:
  * in a model each layer's query depends on the previous layer's output.
- * struct_size must be sizeof(dsa_group_args) or DSA_GROUP_ARGS_V1_SIZE;
- * fields added later go at the end. */
+ * With share = 0 (ABI version 3) the group runs without IndexShare, as
+ * standard DSA does ([MTPBLOG, "Indexer Share：稀疏注意力的缓存复用"]: one
+ * indexer per layer): every layer l runs its own indexer and top-k over its
+ * own index queries, weights and keys, writes its own list and attends with it.
+ * struct_size must be sizeof(dsa_group_args), DSA_GROUP_ARGS_V2_SIZE or
+ * DSA_GROUP_ARGS_V1_SIZE; fields added later go at the end, and a shorter
+ * struct leaves them NULL / 0 (share = 1).
+ *
+ * Workspace state: the indexer adds the top-k histogram into the workspace,
+ * which every call leaves zero for the next one.  A workspace should
+ * therefore be zero-filled once before its first use and not be modified
+ * between calls; one that is not (or one last used with another shape) gives
+ * the same result through a slower recount inside the selection. */
 typedef struct {
     uint32_t struct_size;
     int n_layers;                          /* 1..DSA_GROUP_LAYERS_MAX (4 for a group) */
@@ -154,10 +165,25 @@ typedef struct {
     const uint8_t* q_idx_fp8;                   /* [B,T,32,128] E4M3 */
     const uint8_t* k_idx_fp8;                   /* rows of 128 E4M3 codes */
     const uint8_t* kv_fp8[DSA_GROUP_LAYERS_MAX];  /* rows of 576 E4M3 codes */
+    /* ABI version 3: without IndexShare.  share = 1 is IndexShare (the fields
+     * below are then ignored).  share = 0: layer l scores with layer_q_idx[l],
+     * layer_w[l] and layer_k_idx[l] (bf16; k_bstride as above), or with
+     * layer_q_idx_fp8[l] and layer_k_idx_fp8[l] (E4M3) when those are set,
+     * selects its own top-k list into layer_idx_out[l] and attends with it;
+     * q_idx, w, k_idx, q_idx_fp8, k_idx_fp8 and idx_out are then unused. */
+    int share;
+    const uint16_t* layer_q_idx[DSA_GROUP_LAYERS_MAX];      /* [B,T,32,128] per layer */
+    const float* layer_w[DSA_GROUP_LAYERS_MAX];             /* [B,T,32] per layer */
+    const uint16_t* layer_k_idx[DSA_GROUP_LAYERS_MAX];      /* each layer's index-key cache */
+    const uint8_t* layer_q_idx_fp8[DSA_GROUP_LAYERS_MAX];
+    const uint8_t* layer_k_idx_fp8[DSA_GROUP_LAYERS_MAX];
+    int32_t* layer_idx_out[DSA_GROUP_LAYERS_MAX];          /* [B,T,k] per layer (output) */
 } dsa_group_args;
-/* Size of the version-1 struct (without the FP8 fields); still accepted as
- * struct_size, with every FP8 field taken as NULL. */
+/* Sizes of the version-1 struct (no FP8 fields) and of the version-2 struct
+ * (no share fields); both are still accepted as struct_size, with the missing
+ * fields taken as NULL and share as 1. */
 #define DSA_GROUP_ARGS_V1_SIZE offsetof(dsa_group_args, q_idx_fp8)
+#define DSA_GROUP_ARGS_V2_SIZE offsetof(dsa_group_args, share)
 
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a);
 int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream);

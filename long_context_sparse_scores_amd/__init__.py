@@ -55,6 +55,9 @@ class GroupArgs(ctypes.Structure):
         ("q", _P * GROUP_LAYERS_MAX), ("kv", _P * GROUP_LAYERS_MAX), ("kv_bstride", _I64 * GROUP_LAYERS_MAX),
         ("out", _P * GROUP_LAYERS_MAX), ("lse", _P * GROUP_LAYERS_MAX),
         ("q_idx_fp8", _P), ("k_idx_fp8", _P), ("kv_fp8", _P * GROUP_LAYERS_MAX),
+        ("share", _I), ("layer_q_idx", _P * GROUP_LAYERS_MAX), ("layer_w", _P * GROUP_LAYERS_MAX),
+        ("layer_k_idx", _P * GROUP_LAYERS_MAX), ("layer_q_idx_fp8", _P * GROUP_LAYERS_MAX),
+        ("layer_k_idx_fp8", _P * GROUP_LAYERS_MAX), ("layer_idx_out", _P * GROUP_LAYERS_MAX),
     ]
 
 
@@ -233,26 +236,46 @@ def sparse_mla_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, sm_sca
 
 # ------------------------------------------------------------------ IndexShare group
 def make_group_args(q_idx, w, k_idx, q_pos, k: int, qs: Sequence[torch.Tensor], kvs: Sequence[torch.Tensor],
-                    sm_scale: float, idx_out: torch.Tensor, outs: Sequence[torch.Tensor],
+                    sm_scale: float, idx_out, outs: Sequence[torch.Tensor],
                     lses: Optional[Sequence[Optional[torch.Tensor]]] = None) -> GroupArgs:
-    B, T, H, D = q_idx.shape
-    L = k_idx.shape[1]
+    """Fill dsa_group_args.  With IndexShare, q_idx, w, k_idx and idx_out are
+    tensors; without it (share = 0), they are lists with one tensor per layer."""
+    share = isinstance(q_idx, torch.Tensor)
     n = len(qs)
     if not 1 <= n <= GROUP_LAYERS_MAX or len(kvs) != n or len(outs) != n:
         raise ValueError("need 1..%d layers with matching q/kv/out lists" % GROUP_LAYERS_MAX)
+    if not share and not (len(q_idx) == len(w) == len(k_idx) == len(idx_out) == n):
+        raise ValueError("without IndexShare every layer needs its own q_idx, w, k_idx and idx_out")
+    q0, k0 = (q_idx, k_idx) if share else (q_idx[0], k_idx[0])
+    B, T, H, D = q0.shape
+    L = k0.shape[1]
     a = GroupArgs()
     a.struct_size = ctypes.sizeof(GroupArgs)
     a.n_layers, a.B, a.T, a.L, a.k, a.sm_scale = n, B, T, L, k, float(sm_scale)
-    if q_idx.dtype in _FP8:  # E4M3 index queries and keys
-        a.q_idx_fp8 = _dev(q_idx, "q_idx", _FP8, 4)
-        a.k_idx_fp8 = _dev(k_idx, "k_idx", _FP8, 3)
-    else:
-        a.q_idx = _dev(q_idx, "q_idx", _BF16, 4)
-        a.k_idx = _dev(k_idx, "k_idx", _BF16, 3)
-    a.w = _dev(w, "w", (torch.float32,), 3)
-    a.k_bstride = k_idx.shape[1] * k_idx.shape[2]
+    a.share = 1 if share else 0
+    a.k_bstride = k0.shape[1] * k0.shape[2]
     a.q_pos = _dev(q_pos, "q_pos", (torch.int32,), 2)
-    a.idx_out = _dev(idx_out, "idx_out", (torch.int32,), 3)
+    if share:
+        if q_idx.dtype in _FP8:  # E4M3 index queries and keys
+            a.q_idx_fp8 = _dev(q_idx, "q_idx", _FP8, 4)
+            a.k_idx_fp8 = _dev(k_idx, "k_idx", _FP8, 3)
+        else:
+            a.q_idx = _dev(q_idx, "q_idx", _BF16, 4)
+            a.k_idx = _dev(k_idx, "k_idx", _BF16, 3)
+        a.w = _dev(w, "w", (torch.float32,), 3)
+        a.idx_out = _dev(idx_out, "idx_out", (torch.int32,), 3)
+    else:
+        for l in range(n):
+            if tuple(k_idx[l].shape) != tuple(k0.shape):
+                raise ValueError("every layer's index-key cache must have the shape of layer 0's")
+            if q_idx[l].dtype in _FP8:
+                a.layer_q_idx_fp8[l] = _dev(q_idx[l], "q_idx[%d]" % l, _FP8, 4)
+                a.layer_k_idx_fp8[l] = _dev(k_idx[l], "k_idx[%d]" % l, _FP8, 3)
+            else:
+                a.layer_q_idx[l] = _dev(q_idx[l], "q_idx[%d]" % l, _BF16, 4)
+                a.layer_k_idx[l] = _dev(k_idx[l], "k_idx[%d]" % l, _BF16, 3)
+            a.layer_w[l] = _dev(w[l], "w[%d]" % l, (torch.float32,), 3)
+            a.layer_idx_out[l] = _dev(idx_out[l], "idx_out[%d]" % l, (torch.int32,), 3)
     for l in range(n):
         a.q[l] = _dev(qs[l], "q[%d]" % l, _BF16, 4)
         if kvs[l].dtype in _FP8:
@@ -281,10 +304,29 @@ def layer_group(q_idx, w, k_idx, q_pos, k: int, qs, kvs, sm_scale: float, want_l
     without one, a zero-filled one is allocated.  Returns
     (idx, [out_l], [lse_l] or None)."""
     B, T = q_idx.shape[:2]
-    dev = q_idx.device
-    n = len(qs)
     if idx_out is None:
-        idx_out = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+        idx_out = torch.empty((B, T, k), dtype=torch.int32, device=q_idx.device)
+    return _run_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_out, outs, lses)
+
+
+def layer_group_unshared(q_idx: Sequence[torch.Tensor], w: Sequence[torch.Tensor], k_idx: Sequence[torch.Tensor],
+                         q_pos, k: int, qs, kvs, sm_scale: float, want_lse: bool = False,
+                         ws: Optional[torch.Tensor] = None, idx_out=None, outs=None, lses=None):
+    """The group without IndexShare (dsa_layer_group with share = 0): every
+    layer l runs its own indexer and top-k over q_idx[l], w[l], k_idx[l] and
+    attends with its own list.  Returns ([idx_l], [out_l], [lse_l] or None)."""
+    B, T = q_idx[0].shape[:2]
+    if idx_out is None:
+        idx_out = [torch.empty((B, T, k), dtype=torch.int32, device=q_idx[0].device) for _ in range(len(qs))]
+    return _run_group(list(q_idx), list(w), list(k_idx), q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_out, outs,
+                      lses)
+
+
+def _run_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_out, outs, lses):
+    q0 = q_idx if isinstance(q_idx, torch.Tensor) else q_idx[0]
+    B, T = q0.shape[:2]
+    dev = q0.device
+    n = len(qs)
     if outs is None:
         outs = [torch.empty((B, T, ATTN_HEADS, VALUE_DIM), dtype=torch.bfloat16, device=dev) for _ in range(n)]
     if lses is None and want_lse:
@@ -292,9 +334,9 @@ def layer_group(q_idx, w, k_idx, q_pos, k: int, qs, kvs, sm_scale: float, want_l
     a = make_group_args(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, idx_out, outs, lses)
     need = layer_group_workspace_size(a)
     if ws is None:  # zero-filled, as dsa_layer_group asks of a workspace's first use
-        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=q_idx.device)
-    ws = _workspace(need, q_idx, ws)
-    _check(lib().dsa_layer_group(ctypes.byref(a), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q_idx)))
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    ws = _workspace(need, q0, ws)
+    _check(lib().dsa_layer_group(ctypes.byref(a), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q0)))
     return idx_out, outs, lses
 
 

@@ -2,6 +2,7 @@
 // The operations themselves are described in include/dsa.h with the page
 // passages that define them.
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,7 +36,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxBlocks = (int64_t)1 << 31;
 
-bool group_size_ok(uint32_t n) { return n == sizeof(dsa_group_args) || n == DSA_GROUP_ARGS_V1_SIZE; }
+bool group_size_ok(uint32_t n) {
+    return n == sizeof(dsa_group_args) || n == DSA_GROUP_ARGS_V2_SIZE || n == DSA_GROUP_ARGS_V1_SIZE;
+}
 
 // elem_bytes: 2 for bf16 index queries/keys, 1 for E4M3.
 int check_indexer(const void* q_idx, const float* w, const void* k_idx, int64_t k_bstride, const int32_t* q_pos,
@@ -82,6 +85,112 @@ int check_attn(const uint16_t* q, const void* kv, int64_t kv_bstride, const int3
         ((kv_bstride * elem_bytes) % 16) != 0)
         return fail(DSA_ERR_ALIGN, "attn: pointers and the kv batch stride in bytes must be 16-byte aligned");
     return DSA_OK;
+}
+
+
+// One layer's indexer inputs: bf16 (q_idx, k_idx) or E4M3 (q_idx8, k_idx8).
+struct IndexerIn {
+    const uint16_t* q_idx;
+    const uint8_t* q_idx8;
+    const float* w;
+    const uint16_t* k_idx;
+    const uint8_t* k_idx8;
+    int32_t* idx_out;
+};
+
+IndexerIn indexer_in(const dsa_group_args& a, int l) {
+    if (a.share) return IndexerIn{a.q_idx, a.q_idx_fp8, a.w, a.k_idx, a.k_idx_fp8, a.idx_out};
+    return IndexerIn{a.layer_q_idx[l], a.layer_q_idx_fp8[l], a.layer_w[l], a.layer_k_idx[l], a.layer_k_idx_fp8[l],
+                     a.layer_idx_out[l]};
+}
+
+size_t group_ws_bytes(int rows, int L, int k) {
+    return dsa::align_up((size_t)rows * L * sizeof(float), 256) + dsa::topk_ws_bytes(rows, L, k) +
+           dsa::attn_ws_bytes(rows, k);
+}
+
+// Validate a group call and copy its arguments into *full: the caller's struct
+// may be an older, shorter version, whose missing fields read as NULL and
+// share as 1.  Nothing is enqueued.
+int check_group(const dsa_group_args* args, dsa_group_args* full) {
+    if (!args) return fail(DSA_ERR_NULL, "group: NULL args");
+    if (!group_size_ok(args->struct_size))
+        return fail(DSA_ERR_SHAPE, "group: struct_size %u, expected %zu, %zu or %zu", args->struct_size,
+                    sizeof(dsa_group_args), (size_t)DSA_GROUP_ARGS_V2_SIZE, (size_t)DSA_GROUP_ARGS_V1_SIZE);
+    std::memset(full, 0, sizeof(*full));
+    std::memcpy(full, args, args->struct_size);
+    if (args->struct_size <= offsetof(dsa_group_args, share)) full->share = 1;
+    const dsa_group_args* a = full;
+    if (a->n_layers < 1 || a->n_layers > DSA_GROUP_LAYERS_MAX)
+        return fail(DSA_ERR_SHAPE, "group: n_layers=%d outside [1, %d]", a->n_layers, DSA_GROUP_LAYERS_MAX);
+    if (a->share != 0 && a->share != 1) return fail(DSA_ERR_SHAPE, "group: share=%d must be 0 or 1", a->share);
+    const int B = a->B, T = a->T, L = a->L, k = a->k;
+    const float* some_scores = reinterpret_cast<const float*>(16);  // the workspace is checked by the caller
+    const int n_index = a->share ? 1 : a->n_layers;  // indexer + top-k runs
+    for (int l = 0; l < n_index; ++l) {
+        const IndexerIn in = indexer_in(*a, l);
+        const bool fp8 = in.q_idx8 || in.k_idx8;
+        if (fp8 && (!in.q_idx8 || !in.k_idx8 || in.q_idx || in.k_idx))
+            return fail(DSA_ERR_SHAPE, "group: %s: set the E4M3 index queries and keys together, with the bf16 ones "
+                        "NULL", a->share ? "q_idx_fp8/k_idx_fp8" : "layer_q_idx_fp8/layer_k_idx_fp8");
+        int st = fp8 ? check_indexer(in.q_idx8, in.w, in.k_idx8, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS,
+                                     DSA_INDEX_DIM, some_scores, 1)
+                     : check_indexer(in.q_idx, in.w, in.k_idx, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS,
+                                     DSA_INDEX_DIM, some_scores, 2);
+        if (st != DSA_OK && !a->share) {  // name the layer whose indexer inputs are wrong
+            char msg[sizeof(g_err)];
+            std::snprintf(msg, sizeof(msg), "%s", g_err);
+            return fail(st, "group (share = 0): layer %d: %s", l, msg);
+        }
+        if (st != DSA_OK) return st;
+        if (!in.idx_out) return fail(DSA_ERR_NULL, "group: NULL %s", a->share ? "idx_out" : "layer_idx_out");
+        st = check_topk(some_scores, a->q_pos, B, T, L, k, in.idx_out);
+        if (st != DSA_OK) return st;
+    }
+    for (int l = 0; l < a->n_layers; ++l) {
+        if (a->kv_fp8[l] && a->kv[l])
+            return fail(DSA_ERR_SHAPE, "group: layer %d has both kv and kv_fp8; set one of them", l);
+        const int32_t* idx = indexer_in(*a, l).idx_out;
+        const int st = a->kv_fp8[l] ? check_attn(a->q[l], a->kv_fp8[l], a->kv_bstride[l], idx, B, T, L, DSA_ATTN_HEADS,
+                                                 DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 1)
+                                    : check_attn(a->q[l], a->kv[l], a->kv_bstride[l], idx, B, T, L, DSA_ATTN_HEADS,
+                                                 DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 2);
+        if (st != DSA_OK) return st;
+    }
+    return DSA_OK;
+}
+
+// Enqueue a validated group on a workspace of at least group_ws_bytes.
+int launch_group(const dsa_group_args& a, void* ws, hipStream_t s) {
+    const int B = a.B, T = a.T, L = a.L, k = a.k, rows = B * T;
+    char* base = reinterpret_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base);
+    void* topk_ws = base + dsa::align_up((size_t)rows * L * sizeof(float), 256);
+    void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
+    // The indexer prepares the selection: the per-query decode kernels clear its
+    // counters and add the top-digit histogram of the scores (two launches
+    // fewer); the multi-query tile kernels clear the state for the histogram pass.
+    const bool hist = dsa::indexer_counts_histogram(T);
+    const dsa::TopkPrep prep = dsa::topk_prep(topk_ws, rows, L, hist);
+    for (int l = 0; l < a.n_layers; ++l) {
+        const IndexerIn in = indexer_in(a, l);
+        if (l == 0 || !a.share) {
+            hipError_t e = in.q_idx8 ? dsa::launch_indexer_fp8(in.q_idx8, in.w, in.k_idx8, a.k_bstride, a.q_pos, B, T,
+                                                               L, scores, s, prep)
+                                     : dsa::launch_indexer(in.q_idx, in.w, in.k_idx, a.k_bstride, a.q_pos, B, T, L,
+                                                           scores, s, prep);
+            if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
+            e = dsa::launch_topk(scores, a.q_pos, rows, L, k, in.idx_out, topk_ws, s,
+                                 hist ? dsa::TopkState::kHistogram : dsa::TopkState::kCleared);
+            if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
+        }
+        const hipError_t e = a.kv_fp8[l] ? dsa::launch_attn_fp8(a.q[l], a.kv_fp8[l], a.kv_bstride[l], in.idx_out, B, T,
+                                                                L, k, a.sm_scale, a.out[l], a.lse[l], attn_ws, s)
+                                         : dsa::launch_attn(a.q[l], a.kv[l], a.kv_bstride[l], in.idx_out, B, T, L, k,
+                                                            a.sm_scale, a.out[l], a.lse[l], attn_ws, s);
+        if (e != hipSuccess) return hip_status(e, "dsa_layer_group/attention");
+    }
+    return ok();
 }
 
 }  // namespace
@@ -159,77 +268,18 @@ int dsa_sparse_mla_attn_fp8kv(const uint16_t* q, const uint8_t* kv, int64_t kv_b
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a) {
     if (!a || !group_size_ok(a->struct_size) || a->B < 1 || a->T < 1 || a->L < 1 || a->k < 1 || a->k > DSA_TOPK_MAX)
         return 0;
-    const int rows = a->B * a->T;
-    return dsa::align_up((size_t)rows * a->L * sizeof(float), 256) + dsa::topk_ws_bytes(rows, a->L, a->k) +
-           dsa::attn_ws_bytes(rows, a->k);
+    return group_ws_bytes(a->B * a->T, a->L, a->k);
 }
 
 int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void* stream) {
-    if (!args) return fail(DSA_ERR_NULL, "group: NULL args");
-    if (!group_size_ok(args->struct_size))
-        return fail(DSA_ERR_SHAPE, "group: struct_size %u, expected %zu or %zu", args->struct_size,
-                    sizeof(dsa_group_args), (size_t)DSA_GROUP_ARGS_V1_SIZE);
-    // a version-1 struct ends before the FP8 fields: read only its bytes, the rest stays NULL
     dsa_group_args full;
-    std::memset(&full, 0, sizeof(full));
-    std::memcpy(&full, args, args->struct_size);
-    const dsa_group_args* a = &full;
-    if (a->n_layers < 1 || a->n_layers > DSA_GROUP_LAYERS_MAX)
-        return fail(DSA_ERR_SHAPE, "group: n_layers=%d outside [1, %d]", a->n_layers, DSA_GROUP_LAYERS_MAX);
-    const int B = a->B, T = a->T, L = a->L, k = a->k;
-    // validate everything before enqueueing anything
-    const bool idx_fp8 = a->q_idx_fp8 || a->k_idx_fp8;
-    if (idx_fp8 && (!a->q_idx_fp8 || !a->k_idx_fp8 || a->q_idx || a->k_idx))
-        return fail(DSA_ERR_SHAPE, "group: set q_idx_fp8 and k_idx_fp8 together, with q_idx and k_idx NULL");
-    const float* ws_scores = reinterpret_cast<const float*>(ws ? ws : (void*)16);
-    int st = idx_fp8 ? check_indexer(a->q_idx_fp8, a->w, a->k_idx_fp8, a->k_bstride, a->q_pos, B, T, L,
-                                     DSA_INDEX_HEADS, DSA_INDEX_DIM, ws_scores, 1)
-                     : check_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, DSA_INDEX_HEADS,
-                                     DSA_INDEX_DIM, ws_scores, 2);
+    int st = check_group(args, &full);
     if (st != DSA_OK) return st;
-    if (!a->idx_out) return fail(DSA_ERR_NULL, "group: NULL idx_out");
-    st = check_topk(reinterpret_cast<const float*>(16), a->q_pos, B, T, L, k, a->idx_out);
-    if (st != DSA_OK) return st;
-    for (int l = 0; l < a->n_layers; ++l) {
-        if (a->kv_fp8[l] && a->kv[l])
-            return fail(DSA_ERR_SHAPE, "group: layer %d has both kv and kv_fp8; set one of them", l);
-        st = a->kv_fp8[l] ? check_attn(a->q[l], a->kv_fp8[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS,
-                                       DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 1)
-                          : check_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, DSA_ATTN_HEADS,
-                                       DSA_LATENT_DIM, DSA_VALUE_DIM, k, a->sm_scale, a->out[l], a->lse[l], 2);
-        if (st != DSA_OK) return st;
-    }
-    const size_t need = dsa_layer_group_workspace_size(a);
+    const size_t need = group_ws_bytes(full.B * full.T, full.L, full.k);
     if (!ws || ws_bytes < need || !aligned16(ws))
         return fail(DSA_ERR_WORKSPACE, "group: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
                     need);
-    const int rows = B * T;
-    char* base = reinterpret_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(base);
-    void* topk_ws = base + dsa::align_up((size_t)rows * L * sizeof(float), 256);
-    void* attn_ws = reinterpret_cast<char*>(topk_ws) + dsa::topk_ws_bytes(rows, L, k);
-    hipStream_t s = (hipStream_t)stream;
-    // The indexer prepares the selection: the per-query decode kernels clear its
-    // counters and add the top-digit histogram of the scores (two launches
-    // fewer); the multi-query tile kernels clear the state for the histogram pass.
-    const bool hist = dsa::indexer_counts_histogram(T);
-    const dsa::TopkPrep prep = dsa::topk_prep(topk_ws, rows, L, hist);
-    hipError_t e = idx_fp8 ? dsa::launch_indexer_fp8(a->q_idx_fp8, a->w, a->k_idx_fp8, a->k_bstride, a->q_pos, B, T,
-                                                     L, scores, s, prep)
-                           : dsa::launch_indexer(a->q_idx, a->w, a->k_idx, a->k_bstride, a->q_pos, B, T, L, scores,
-                                                 s, prep);
-    if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
-    e = dsa::launch_topk(scores, a->q_pos, rows, L, k, a->idx_out, topk_ws, s,
-                         hist ? dsa::TopkState::kHistogram : dsa::TopkState::kCleared);
-    if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
-    for (int l = 0; l < a->n_layers; ++l) {
-        e = a->kv_fp8[l] ? dsa::launch_attn_fp8(a->q[l], a->kv_fp8[l], a->kv_bstride[l], a->idx_out, B, T, L, k,
-                                                a->sm_scale, a->out[l], a->lse[l], attn_ws, s)
-                         : dsa::launch_attn(a->q[l], a->kv[l], a->kv_bstride[l], a->idx_out, B, T, L, k, a->sm_scale,
-                                            a->out[l], a->lse[l], attn_ws, s);
-        if (e != hipSuccess) return hip_status(e, "dsa_layer_group/attention");
-    }
-    return ok();
+    return launch_group(full, ws, (hipStream_t)stream);
 }
 
 size_t mtp_verify_workspace_size(int B, int S, int V) {

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(dsa):
 
 
 def test_version_and_error_string(dsa):
-    assert dsa.abi_version() == 2
+    assert dsa.abi_version() == 3
     assert isinstance(dsa.last_error(), str)
 
 
@@ -52,13 +52,17 @@ def test_group_struct_layout_matches_c(dsa, tmp_path):
                    ' offsetof(dsa_group_args, q), offsetof(dsa_group_args, kv_bstride),'
                    ' offsetof(dsa_group_args, lse));'
                    ' printf("%zu %zu %zu\\n", offsetof(dsa_group_args, q_idx_fp8),'
-                   ' offsetof(dsa_group_args, kv_fp8), (size_t)DSA_GROUP_ARGS_V1_SIZE); return 0;}\n')
+                   ' offsetof(dsa_group_args, kv_fp8), (size_t)DSA_GROUP_ARGS_V1_SIZE);'
+                   ' printf("%zu %zu %zu %zu\\n", offsetof(dsa_group_args, share),'
+                   ' offsetof(dsa_group_args, layer_q_idx), offsetof(dsa_group_args, layer_idx_out),'
+                   ' (size_t)DSA_GROUP_ARGS_V2_SIZE); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
     vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
     G = dsa.GroupArgs
     assert vals == [ctypes.sizeof(G), G.q_idx.offset, G.idx_out.offset, G.q.offset, G.kv_bstride.offset,
-                    G.lse.offset, G.q_idx_fp8.offset, G.kv_fp8.offset, G.q_idx_fp8.offset]
+                    G.lse.offset, G.q_idx_fp8.offset, G.kv_fp8.offset, G.q_idx_fp8.offset,
+                    G.share.offset, G.layer_q_idx.offset, G.layer_idx_out.offset, G.share.offset]
 
 
 def test_validation_rejects_before_launch(dsa):
@@ -102,6 +106,7 @@ def test_validation_rejects_before_launch(dsa):
 def _small_group(dsa, fake):
     a = dsa.GroupArgs()
     a.struct_size = ctypes.sizeof(dsa.GroupArgs)
+    a.share = 1
     a.n_layers, a.B, a.T, a.L, a.k, a.sm_scale = 1, 1, 1, 64, 16, 0.0625
     a.w, a.q_pos, a.idx_out = fake, fake, fake
     a.k_bstride = 64 * 128
@@ -137,6 +142,42 @@ def test_group_accepts_version1_struct(dsa):
     assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5
     a.struct_size = dsa.GroupArgs.q_idx_fp8.offset + 8
     assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+
+
+def test_group_version2_struct_means_indexshare(dsa):
+    # a version-2 struct ends before `share`: the group is the IndexShare group
+    # whatever follows it in memory (here share = 0 and no per-layer inputs)
+    lib = dsa.lib()
+    fake = 4096
+    a = _small_group(dsa, fake)
+    a.q_idx, a.k_idx, a.kv[0] = fake, fake, fake
+    a.share = 0
+    a.struct_size = dsa.GroupArgs.share.offset
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5  # only the missing workspace is reported
+    a.struct_size = ctypes.sizeof(dsa.GroupArgs)
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -1  # share = 0 needs each layer's inputs
+    assert "layer" in dsa.last_error()
+
+
+def test_group_share_field_rules(dsa):
+    lib = dsa.lib()
+    fake = 4096
+    a = _small_group(dsa, fake)
+    a.kv[0] = fake
+    a.share = 2
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    assert "share" in dsa.last_error()
+    a.share = 0
+    a.layer_q_idx[0], a.layer_w[0], a.layer_k_idx[0], a.layer_idx_out[0] = fake, fake, fake, fake
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5
+    a.layer_q_idx_fp8[0] = fake  # bf16 and E4M3 inputs for one layer
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -2
+    a.layer_q_idx[0] = a.layer_k_idx[0] = None
+    a.layer_k_idx_fp8[0] = fake
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -5
+    a.n_layers = 2
+    a.q[1], a.out[1], a.kv[1], a.kv_bstride[1] = fake, fake, fake, 64 * 576
+    assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -1  # layer 1 has no indexer inputs
 
 
 def test_workspace_sizes(dsa):

@@ -367,3 +367,26 @@ def test_attn_fp8_nan_row_not_selected(dsa):
     ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16, kv_fp8=True)
     assert_attn_close(got, ref)
     np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
+def test_group_fp8_without_indexshare(dsa):
+    # share = 0 with E4M3 index caches: two layers, each its own E4M3 indexer
+    # inputs, lists bit-exact against the oracle's E4M3 indexer and top-k
+    cfg = synth.TINY
+    n = 2
+    say("fp8 group without IndexShare")
+    B, T, L = cfg.B, cfg.T, cfg.L
+    pos = cfg.q_pos()
+    qis = [synth.to_e4m3(synth.bf16_to_f32(synth.int_bf16(70 + l, 1, (B, T, 32, 128)))) for l in range(n)]
+    ws_ = [synth.pow2_f32(70 + l, 2, (B, T, 32)) for l in range(n)]
+    kis = [synth.to_e4m3(synth.bf16_to_f32(synth.int_bf16(70 + l, 3, (B, L, 128)))) for l in range(n)]
+    qs = [cfg.q_attn(l) for l in range(n)]
+    kvs = [cfg.kv(l) for l in range(n)]
+    idxs, outs, _ = dsa.layer_group_unshared([u8_dev(x) for x in qis], [f32_dev(x) for x in ws_],
+                                             [u8_dev(x) for x in kis], i32_dev(pos), cfg.k,
+                                             [bf16_dev(q) for q in qs], [bf16_dev(kv) for kv in kvs], cfg.sm_scale)
+    for l in range(n):
+        ref_idx = oracle.topk(oracle.indexer_scores(qis[l], ws_[l], kis[l], pos, fp8=True), pos, cfg.k)
+        np.testing.assert_array_equal(host(idxs[l]), ref_idx, err_msg="layer %d" % l)
+        ref, _ = oracle.sparse_mla_attn(qs[l], kvs[l], ref_idx, cfg.sm_scale)
+        assert_attn_close(host(outs[l]), ref, "layer %d" % l)

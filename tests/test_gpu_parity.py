@@ -568,3 +568,34 @@ def test_group_workspace_not_zero_filled(dsa):
         np.testing.assert_array_equal(host(idx), ref_idx, err_msg="call %d" % call)
         for l in range(2):
             assert_attn_close(host(outs[l]), ref_outs[l], "call %d layer %d" % (call, l))
+
+
+def test_group_without_indexshare(dsa):
+    # share = 0, standard DSA: every layer runs its own indexer and top-k over
+    # its own index queries, weights and index-key cache.  Each layer's list is
+    # bit-exact against the oracle's indexer and top-k for that layer, the
+    # lists differ between layers, and each output matches the oracle's
+    # attention with that layer's list.
+    cfg = synth.TINY
+    n = 4
+    say("group without IndexShare, %d layers" % n)
+    B, T, L = cfg.B, cfg.T, cfg.L
+    pos = cfg.q_pos()
+    qis = [synth.int_bf16(60 + l, 1, (B, T, 32, 128)) for l in range(n)]
+    ws_ = [synth.pow2_f32(60 + l, 2, (B, T, 32)) for l in range(n)]
+    kis = [synth.int_bf16(60 + l, 3, (B, L, 128)) for l in range(n)]
+    qs = [cfg.q_attn(l) for l in range(n)]
+    kvs = [cfg.kv(l) for l in range(n)]
+    idxs, outs, lses = dsa.layer_group_unshared([bf16_dev(x) for x in qis], [f32_dev(x) for x in ws_],
+                                                [bf16_dev(x) for x in kis], i32_dev(pos), cfg.k,
+                                                [bf16_dev(q) for q in qs], [bf16_dev(kv) for kv in kvs], cfg.sm_scale,
+                                                want_lse=True)
+    got_idx = [host(i) for i in idxs]
+    for l in range(n):
+        ref_idx = oracle.topk(oracle.indexer_scores(qis[l], ws_[l], kis[l], pos), pos, cfg.k)
+        np.testing.assert_array_equal(got_idx[l], ref_idx, err_msg="layer %d" % l)
+        ref, ref_lse = oracle.sparse_mla_attn(qs[l], kvs[l], ref_idx, cfg.sm_scale)
+        assert_attn_close(host(outs[l]), ref, "layer %d" % l)
+        np.testing.assert_allclose(host(lses[l]), ref_lse, atol=LSE_TOL, rtol=0)
+    for l in range(1, n):
+        assert not np.array_equal(got_idx[l], got_idx[0]), "layer %d selected the same rows as layer 0" % l
