@@ -134,11 +134,13 @@ int dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstrid
  * DSA_GROUP_ARGS_V1_SIZE; fields added later go at the end, and a shorter
  * struct leaves them NULL / 0 (share = 1).
  *
- * Workspace state: the indexer adds the top-k histogram into the workspace,
- * which every call leaves zero for the next one.  A workspace should
- * therefore be zero-filled once before its first use and not be modified
- * between calls; one that is not (or one last used with another shape) gives
- * the same result through a slower recount inside the selection. */
+ * Workspace state: the indexer adds the top-k histogram into the workspace
+ * onto what the previous call left there, which every call leaves zero and
+ * marked with the shape.  So the workspace carries state from one call to the
+ * next: the first call on a workspace, or the first after a call of another
+ * shape, finds no mark and counts the histogram again inside the selection
+ * (slower, same result); later calls of one shape skip that.  Do not modify
+ * the workspace between calls of one shape. */
 typedef struct {
     uint32_t struct_size;
     int n_layers;                          /* 1..DSA_GROUP_LAYERS_MAX (4 for a group) */

@@ -299,9 +299,9 @@ def layer_group(q_idx, w, k_idx, q_pos, k: int, qs, kvs, sm_scale: float, want_l
                 ws: Optional[torch.Tensor] = None, idx_out=None, outs=None, lses=None):
     """One IndexShare group (dsa_layer_group): indexer and top-k once, then
     attention for every layer with that one index list.  q_idx and k_idx are
-    bf16, or both E4M3 (uint8 codes / float8_e4m3fn).  A workspace `ws` kept
-    across calls should be zero-filled before its first use (torch.zeros);
-    without one, a zero-filled one is allocated.  Returns
+    bf16, or both E4M3 (uint8 codes / float8_e4m3fn).  A workspace `ws`
+    passed to consecutive calls of one shape lets them skip a recount of the
+    top-k histogram (the first call on it recounts).  Returns
     (idx, [out_l], [lse_l] or None)."""
     B, T = q_idx.shape[:2]
     if idx_out is None:
@@ -333,7 +333,7 @@ def _run_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_o
         lses = [torch.empty((B, T, ATTN_HEADS), dtype=torch.float32, device=dev) for _ in range(n)]
     a = make_group_args(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, idx_out, outs, lses)
     need = layer_group_workspace_size(a)
-    if ws is None:  # zero-filled, as dsa_layer_group asks of a workspace's first use
+    if ws is None:
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     ws = _workspace(need, q0, ws)
     _check(lib().dsa_layer_group(ctypes.byref(a), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(q0)))

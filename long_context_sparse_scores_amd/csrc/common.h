@@ -53,8 +53,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // group): for every row r, the uint32 words at base + r*stride.  Words
 // [zero_off, zero_off + zero_count) are cleared; when `hist` is set, the row's
 // histogram of the top 11 bits of the order-preserving score keys (visible
-// keys only) is added into words [0, 2048), which must hold zeros when the
-// indexer starts.
+// keys only) is added into words [0, 2048), which the previous selection on
+// this workspace left zero (the filter checks that it did).
 struct TopkPrep {
     uint32_t* base = nullptr;
     int64_t stride = 0;
@@ -81,8 +81,8 @@ hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_
 
 size_t topk_ws_bytes(int rows, int L, int k);
 // What the indexer prepares before a selection: with `hist`, it clears the
-// counters and adds the top-digit histogram (the histogram words must be zero
-// before it starts: every selection leaves them zero); without, it clears both.
+// counters and adds the top-digit histogram onto what the last selection left
+// (zero, and stamped as such); without, it clears both.
 TopkPrep topk_prep(void* ws, int rows, int L, bool hist);
 // How much of the selection's state is ready when launch_topk is called.
 enum class TopkState {

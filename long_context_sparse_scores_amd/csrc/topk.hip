@@ -30,10 +30,11 @@
 // registers, so the scores are read once (filter) and select never touches
 // them.  That histogram must start from zero, and no launch of the group can
 // clear it before the indexer adds to it; so the selection, its last user,
-// clears it for the next call, and a workspace must be zero-filled once before
-// its first use.  The filter checks that the histogram counts the row's
-// visible keys exactly; if not (the workspace was not zero-filled), it counts
-// the row itself, so the result never depends on that.
+// clears it for the next call and leaves a stamp of the row and the shape.
+// The filter uses the histogram only when it finds that stamp and the counts
+// add up to the row's visible keys; otherwise (a workspace's first use, or
+// the first after a change of shape) it counts the row itself, slower but
+// with the same result.
 // (Running select in the last filter workgroup of each row would save a
 // launch, but publishing the candidates across XCDs then takes an L2
 // write-back per workgroup, which costs far more on this part.)
@@ -60,9 +61,13 @@ constexpr int kSelBatch = kCandLds / kSelectThreads;  // loads in flight per thr
 
 // Per-row workspace (32-bit words).
 // kStT, kStAbove: the threshold digit T and the count of keys whose top digit is above it.
-enum : int { kCtrCand = 0, kStT = 1, kStAbove = 2, kCtrWords = 8 };
+// kStamp: written by the selection once it has cleared the row's histogram
+// (see histogram_stamp); the counters before it are cleared for every call.
+enum : int { kCtrCand = 0, kStT = 1, kStAbove = 2, kStamp = 7, kCtrWords = 8 };
 
 struct Layout {
+    int rows;     // rows (queries) of the call
+    int L;        // keys per row
     int slice;    // elements per slice (multiple of 256)
     int nslice;   // slices per row
     int cap;      // candidate capacity per row
@@ -84,6 +89,21 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int row, const Layout& lo) {
     r.cpos = r.ctr + kCtrWords;
     r.ckey = r.cpos + lo.cap;
     return r;
+}
+
+// The mark a selection leaves on a row whose histogram it has cleared: a hash
+// of the row and of everything that places the row's words in the workspace,
+// never 0.  A later call of the same shape that finds it (and a histogram that
+// counts the row's visible keys exactly) can trust the histogram its indexer
+// added; after a change of shape, or in a workspace never used before, the
+// mark does not match and the filter counts the row itself.
+__device__ __forceinline__ uint32_t histogram_stamp(const Layout& lo, int row) {
+    uint64_t x = ((uint64_t)(uint32_t)lo.rows << 32) ^ (uint64_t)(uint32_t)lo.L;
+    x ^= ((uint64_t)lo.row_words() << 20) ^ ((uint64_t)(uint32_t)row * 0x9E3779B97F4A7C15ull);
+    x ^= x >> 31;
+    x *= 0xBF58476D1CE4E5B9ull;  // SplitMix64 finaliser (Steele, Lea & Flood 2014)
+    x ^= x >> 29;
+    return (uint32_t)x | 1u;
 }
 
 __device__ __forceinline__ int64_t n_visible(const int32_t* q_pos, int row, int L) {
@@ -470,9 +490,13 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
     }
 }
 
+// hist_checked: the histogram was added by the indexer onto what the last
+// selection left, so it is used only when that selection's stamp is there and
+// it counts the row's visible keys exactly; otherwise it was built from zero
+// in this call.
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ q_pos, int L, int k,
-                                                               Layout lo, void* ws) {
+                                                               Layout lo, void* ws, int hist_checked) {
     const int row = blockIdx.x / lo.nslice;
     const int slice = blockIdx.x % lo.nslice;
     const int64_t n = n_visible(q_pos, row, L);
@@ -503,10 +527,10 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     load_batch(w0);
     uint32_t total;
     BinPick b0 = pick_bin<kThreads>(hp, kBins, (uint32_t)k, scratch, &pick, &total);
-    if (total != (uint32_t)n) {
-        // The histogram does not count the row's n visible keys exactly once: it
-        // did not start from zero (a workspace that was not zero-filled before
-        // its first use).  Count this row here, from its scores.
+    if (hist_checked && (rw.ctr[kStamp] != histogram_stamp(lo, row) || total != (uint32_t)n)) {
+        // The histogram did not start from zero: no selection of this shape
+        // cleared it before the indexer added to it (a workspace's first use, or
+        // the first after a change of shape).  Count this row here, from its scores.
         for (int i = threadIdx.x; i < kBins; i += kThreads) own_hist[i] = 0u;
         lds_sync();
         for (int64_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&own_hist[score_key(row_scores[i]) >> 21], 1u);
@@ -574,8 +598,9 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float
     int32_t* out = idx + (int64_t)row * k;
     const RowWs rw = row_ws(ws, row, lo);
     // The filter pass was the histogram's last reader: leave it zero for the
-    // next selection, whose indexer adds into it.
+    // next selection, whose indexer adds into it, and mark it so.
     for (int i = threadIdx.x; i < kBins; i += kSelectThreads) rw.hist1[i] = 0u;
+    if (threadIdx.x == 0) rw.ctr[kStamp] = histogram_stamp(lo, row);
     if (n <= k) {
         for (int j = threadIdx.x; j < k; j += kSelectThreads) out[j] = j < n ? j : -1;
         return;
@@ -593,6 +618,8 @@ Layout make_layout(int rows, int L) {
     int64_t slice = ((int64_t)L + ns - 1) / ns;
     slice = (slice + 255) / 256 * 256;
     Layout lo;
+    lo.rows = rows;
+    lo.L = L;
     lo.slice = (int)slice;
     lo.nslice = (int)(((int64_t)L + slice - 1) / slice);
     int64_t cap = (int64_t)L / 8;
@@ -614,7 +641,7 @@ TopkPrep topk_prep(void* ws, int rows, int L, bool hist) {
     p.base = reinterpret_cast<uint32_t*>(ws);  // each row's words start with hist1, then the counters
     p.stride = (int64_t)lo.row_words();
     p.zero_off = hist ? kBins : 0;
-    p.zero_count = hist ? kCtrWords : kBins + kCtrWords;
+    p.zero_count = hist ? kStamp : kBins + kStamp;  // the counters before the stamp (and the histogram)
     p.hist = hist;
     return p;
 }
@@ -628,7 +655,8 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     if (state != TopkState::kHistogram)
         hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
                            dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws,
+                       state == TopkState::kHistogram ? 1 : 0);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        idx);
     return hipGetLastError();

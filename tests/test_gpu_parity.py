@@ -2,6 +2,8 @@
 same seeded inputs — small cases element by element, ragged shapes and edge
 cases.  Bit-exact for scores and indices; attention within 2e-2 of the
 output scale; verification exact outside the fp32 ambiguity band."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -544,30 +546,50 @@ def test_verify_out_of_vocab_token_rejected(dsa):
     assert int(host(na)[0]) == 0 and 0 <= int(host(nx)[0]) < V
 
 
-def test_group_workspace_not_zero_filled(dsa):
-    # A workspace should be zero-filled before its first use, because the
-    # indexer adds the top-k histogram into it and every call leaves it zero for
-    # the next.  One that is not (here: every byte 0xAB) still gives the exact
-    # result: the selection sees that the histogram does not count the visible
-    # keys and counts the rows itself.  The second call takes the normal path.
-    cfg = synth.TINY
-    say("group with a workspace that was not zero-filled")
-    qi, w, ki, pos = cfg.q_idx(), cfg.w(), cfg.k_idx(), cfg.q_pos()
-    qs = [cfg.q_attn(l) for l in range(2)]
-    kvs = [cfg.kv(l) for l in range(2)]
-    dq = [bf16_dev(q) for q in qs]
-    dkv = [bf16_dev(kv) for kv in kvs]
-    _, ref_idx, ref_outs, _ = oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale)
-    args = dsa.make_group_args(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k, dq, dkv, cfg.sm_scale,
-                               torch.empty((cfg.B, cfg.T, cfg.k), dtype=torch.int32, device=DEV),
-                               [torch.empty((cfg.B, cfg.T, 64, 512), dtype=torch.bfloat16, device=DEV)] * 2)
-    ws = torch.full((dsa.layer_group_workspace_size(args),), 0xAB, dtype=torch.uint8, device=DEV)
-    for call in range(2):
-        idx, outs, _ = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), cfg.k, dq, dkv,
-                                       cfg.sm_scale, ws=ws)
-        np.testing.assert_array_equal(host(idx), ref_idx, err_msg="call %d" % call)
-        for l in range(2):
-            assert_attn_close(host(outs[l]), ref_outs[l], "call %d layer %d" % (call, l))
+@pytest.mark.parametrize("fill", ["zeros", "bytes_ab", "neg_inf_words"])
+def test_group_workspace_state(dsa, fill):
+    # The decode indexer adds the top-k histogram onto what the previous call
+    # left in the workspace (zero, with a stamp of the shape).  A workspace
+    # that holds anything else on its first use -- zeros, bytes 0xAB, or the
+    # bits of -inf floats, whose 2048-word sums wrap to exactly 0 -- gives the
+    # exact result through a recount, and so do the second call of the shape
+    # and the first call after a change of shape.
+    say("group workspace state: %s" % fill)
+    lib = dsa.lib()
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    shapes = [(3, 9000, 0), (3, 9000, 1), (2, 12000, 0), (3, 9000, 0)]
+    cases = {}
+    for B, L, _ in shapes:
+        if (B, L) in cases:
+            continue
+        qi = synth.int_bf16(90 + L, 1, (B, 1, 32, 128))
+        w = synth.pow2_f32(90 + L, 2, (B, 1, 32))
+        ki = synth.int_bf16(90 + L, 3, (B, L, 128))
+        pos = np.full((B, 1), L - 1, np.int32)
+        pos[0, 0] = L // 3
+        q = synth.normal_bf16(90 + L, 4, (B, 1, 64, 576))
+        kv = synth.normal_bf16(90 + L, 5, (B, L, 576))
+        _, ref_idx, ref_outs, _ = oracle.layer_group(qi, w, ki, pos, 2048, [q], [kv], 1 / 16)
+        cases[(B, L)] = ((bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), [bf16_dev(q)], [bf16_dev(kv)]),
+                         ref_idx, ref_outs[0])
+    nbytes = max(dsa.layer_group_workspace_size(dsa.make_group_args(
+        *d[:4], 2048, d[4], d[5], 1 / 16, torch.empty((B, 1, 2048), dtype=torch.int32, device=DEV),
+        [torch.empty((B, 1, 64, 512), dtype=torch.bfloat16, device=DEV)])) for (B, L), (d, _, _) in cases.items())
+    if fill == "zeros":
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    elif fill == "bytes_ab":
+        ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=DEV)
+    else:
+        ws = torch.full((nbytes // 4,), float("-inf"), dtype=torch.float32, device=DEV).view(torch.uint8)
+    for call, (B, L, _) in enumerate(shapes):
+        d, ref_idx, ref_out = cases[(B, L)]
+        idx = torch.full((B, 1, 2048), -9, dtype=torch.int32, device=DEV)
+        out = torch.zeros((B, 1, 64, 512), dtype=torch.bfloat16, device=DEV)
+        a = dsa.make_group_args(*d[:4], 2048, d[4], d[5], 1 / 16, idx, [out])
+        assert lib.dsa_layer_group(ctypes.byref(a), ws.data_ptr(), nbytes, stream) == 0, dsa.last_error()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(idx), ref_idx, err_msg="call %d B=%d L=%d" % (call, B, L))
+        assert_attn_close(host(out), ref_out, "call %d" % call)
 
 
 def test_group_without_indexshare(dsa):
