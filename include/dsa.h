@@ -190,6 +190,26 @@ typedef struct {
 size_t dsa_layer_group_workspace_size(const dsa_group_args* a);
 int dsa_layer_group(const dsa_group_args* a, void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_layer_group_noalloc: for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation).  It is
+ * dsa_layer_group with the library's own scratch in place of `ws`: a static
+ * device array of DSA_NOALLOC_SCRATCH_BYTES on each GPU, kept until the
+ * process ends, whose address is looked up once per device on the first call
+ * there (the stream must belong to the current device).  The call allocates
+ * and frees nothing.  A group whose dsa_layer_group_workspace_size exceeds
+ * DSA_NOALLOC_SCRATCH_BYTES is rejected with DSA_ERR_WORKSPACE before any
+ * work is enqueued (48 MiB holds decode groups such as 32 queries over 128K
+ * rows or 4 over 1M rows; a 4096-query prefill chunk does not fit).  Every
+ * call on a GPU shares that GPU's scratch and finds the previous call's
+ * contents there, as a workspace keeps them between dsa_layer_group calls
+ * (see "Workspace state" above): the first call, and the first after a call
+ * of another shape, recount the histogram, so the result never depends on
+ * what an earlier call left.  Calls that overlap on one GPU (concurrent
+ * streams or host threads) race on the scratch and must not be issued. */
+#define DSA_NOALLOC_SCRATCH_BYTES (48u << 20)
+int dsa_layer_group_noalloc(const dsa_group_args* a, void* stream);
+
 /* ---------------------------------------------------------------- FP8 caches
  * [CTXFR, "Entraînement par renforcement de l'agent intelligent"] names an FP8
  * KV cache (it keeps rollout memory within budget).  These entry points take

@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_layer_group_workspace_size.argtypes = [ctypes.POINTER(GroupArgs)]
         L.dsa_layer_group.restype = _I
         L.dsa_layer_group.argtypes = [ctypes.POINTER(GroupArgs), _P, _SZ, _P]
+        L.dsa_layer_group_noalloc.restype = _I
+        L.dsa_layer_group_noalloc.argtypes = [ctypes.POINTER(GroupArgs), _P]
         L.mtp_verify_target_only_workspace_size.restype = _SZ
         L.mtp_verify_target_only_workspace_size.argtypes = [_I, _I, _I]
         L.mtp_verify_target_only.restype = _I
@@ -320,6 +322,19 @@ def layer_group_unshared(q_idx: Sequence[torch.Tensor], w: Sequence[torch.Tensor
         idx_out = [torch.empty((B, T, k), dtype=torch.int32, device=q_idx[0].device) for _ in range(len(qs))]
     return _run_group(list(q_idx), list(w), list(k_idx), q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_out, outs,
                       lses)
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def layer_group_noalloc(q_idx, w, k_idx, q_pos, k: int, qs, kvs, sm_scale: float, idx_out: torch.Tensor,
+                        outs: Sequence[torch.Tensor], lses=None):
+    """The IndexShare group on the library's own per-GPU scratch
+    (dsa_layer_group_noalloc): no workspace, nothing allocated by the call.
+    The caller passes every output."""
+    a = make_group_args(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, idx_out, outs, lses)
+    _check(lib().dsa_layer_group_noalloc(ctypes.byref(a), _stream(q_idx)))
+    return idx_out, outs, lses
 
 
 def _run_group(q_idx, w, k_idx, q_pos, k, qs, kvs, sm_scale, want_lse, ws, idx_out, outs, lses):

@@ -6,9 +6,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "common.h"
+
+// Scratch of dsa_layer_group_noalloc, one copy on each GPU the library runs on,
+// held until the process ends.  Host code never uses this name as an address:
+// it takes the device address from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -193,6 +199,31 @@ int launch_group(const dsa_group_args& a, void* ws, hipStream_t s) {
     return ok();
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "group (no allocation): hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DSA_ERR_UNSUPPORTED, "group (no allocation): device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DSA_ERR_HIP, "group (no allocation): hipGetSymbolAddress of the scratch on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +310,20 @@ int dsa_layer_group(const dsa_group_args* args, void* ws, size_t ws_bytes, void*
     if (!ws || ws_bytes < need || !aligned16(ws))
         return fail(DSA_ERR_WORKSPACE, "group: workspace %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
                     need);
+    return launch_group(full, ws, (hipStream_t)stream);
+}
+
+int dsa_layer_group_noalloc(const dsa_group_args* args, void* stream) {
+    dsa_group_args full;
+    int st = check_group(args, &full);
+    if (st != DSA_OK) return st;
+    const size_t need = group_ws_bytes(full.B * full.T, full.L, full.k);
+    if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+        return fail(DSA_ERR_WORKSPACE, "group (no allocation): needs %zu bytes of scratch, above the %zu the library "
+                    "holds per GPU; use dsa_layer_group with a workspace", need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != DSA_OK) return st;
     return launch_group(full, ws, (hipStream_t)stream);
 }
 

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(dsa):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = dsa.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -178,6 +178,20 @@ def test_group_share_field_rules(dsa):
     a.n_layers = 2
     a.q[1], a.out[1], a.kv[1], a.kv_bstride[1] = fake, fake, fake, 64 * 576
     assert lib.dsa_layer_group(ctypes.byref(a), None, 0, None) == -1  # layer 1 has no indexer inputs
+
+
+def test_noalloc_rejects_groups_above_its_scratch(dsa):
+    # rejected on the host, before the device is touched
+    lib = dsa.lib()
+    fake = 4096
+    a = _small_group(dsa, fake)
+    a.q_idx, a.k_idx, a.kv[0] = fake, fake, fake
+    a.B, a.L, a.k_bstride, a.kv_bstride[0] = 64, 262144, 262144 * 128, 262144 * 576
+    assert lib.dsa_layer_group_workspace_size(ctypes.byref(a)) > dsa.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_layer_group_noalloc(ctypes.byref(a), None) == -5
+    assert "scratch" in dsa.last_error()
+    a.n_layers = 0
+    assert lib.dsa_layer_group_noalloc(ctypes.byref(a), None) == -2
 
 
 def test_workspace_sizes(dsa):
