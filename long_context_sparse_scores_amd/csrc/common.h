@@ -69,6 +69,8 @@ constexpr int kTopBins = 2048;  // bins of the top score-key digit (11 bits)
 // top-digit histogram (TopkPrep::hist): the per-query decode kernels can, the
 // multi-query tile kernels cannot.
 bool indexer_counts_histogram(int T);
+// Workgroups of the indexer launch for these sizes (bf16 or E4M3 keys).
+int64_t indexer_grid_blocks(int B, int T, int L, bool fp8);
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                           const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,

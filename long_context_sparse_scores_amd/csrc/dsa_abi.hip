@@ -56,7 +56,8 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, int64_t 
                     DSA_INDEX_DIM);
     if (B > 1 && k_bstride < (int64_t)L * D)
         return fail(DSA_ERR_SHAPE, "indexer: k_bstride %lld < L*D", (long long)k_bstride);
-    if ((int64_t)B * T * ((L + 2047) / 2048) >= kMaxBlocks) return fail(DSA_ERR_SHAPE, "indexer: grid too large");
+    if (dsa::indexer_grid_blocks(B, T, L, elem_bytes == 1) >= kMaxBlocks)
+        return fail(DSA_ERR_SHAPE, "indexer: grid too large");
     if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(scores) ||
         ((k_bstride * elem_bytes) % 16) != 0)
         return fail(DSA_ERR_ALIGN, "indexer: pointers and the key batch stride in bytes must be 16-byte aligned");

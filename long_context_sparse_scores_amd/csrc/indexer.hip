@@ -541,6 +541,13 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
 
 bool indexer_counts_histogram(int T) { return T < kPrefillMinQueries; }
 
+int64_t indexer_grid_blocks(int B, int T, int L, bool fp8) {
+    if (T >= kPrefillMinQueries)
+        return (int64_t)B * ((T + kPfQueries - 1) / kPfQueries) * ((L + kPfKeysPerBlock - 1) / kPfKeysPerBlock);
+    const int keys_per_block = fp8 ? kDecode8Waves * kTile8 * kDecode8Tiles : kDecodeWaves * kTile * kDecodeTiles;
+    return (int64_t)B * T * ((L + keys_per_block - 1) / keys_per_block);
+}
+
 template <int W, int N>
 hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                               const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
