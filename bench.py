@@ -9,7 +9,10 @@ are synthetic and seeded (synth/), resident in HBM before timing starts.
 
 Prints ONE JSON line: throughput in query tokens per second, the HBM
 roofline of the dominant kernel (the index-key scan), a per-phase breakdown
-and the CPU oracle timed on a bounded sample of the same workload.
+and the CPU oracle timed on a bounded sample of the same workload.  The
+default run then times decode_1m_b4, prefill_4096_at_128k and
+mtp_draft_b16_128k the same way (fewer steps, shorter oracle samples) and
+reports each under "extra_workloads"; --no-extras skips them.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
@@ -57,6 +60,10 @@ def parse():
     ap.add_argument("--index-fp8", action="store_true", help="E4M3 index queries and keys (FP8 index cache)")
     ap.add_argument("--kv-fp8", action="store_true", help="E4M3 latent rows (FP8 latent cache)")
     ap.add_argument("--no-nonshared", action="store_true", help="skip timing the group without IndexShare")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (default run: also decode_1m_b4, prefill_4096_at_128k "
+                         "and mtp_draft_b16_128k under extra_workloads)")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=4.0, help="oracle sample time per extra workload")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -76,6 +83,11 @@ def traffic_from_profiles(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+# Workloads timed after the headline in the default run, each reported under
+# "extra_workloads" with its own roofline and oracle baseline.
+EXTRA_WORKLOADS = ("decode_1m_b4", "prefill_4096_at_128k", "mtp_draft_b16_128k")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -83,23 +95,57 @@ def main():
               "context-parallel path is a design, not a measured configuration." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibrate:
         copy_calibrate(torch)
         return
 
+    import synth
+
+    line = run_workload(synth.CONFIGS[args.workload], args)
+    if line is None:
+        return
+    if (args.workload == "decode_128k_b32" and not args.no_extras and not args.index_fp8 and not args.kv_fp8):
+        extras = {}
+        for name in EXTRA_WORKLOADS:
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**vars(args))
+            sub.steps, sub.warmup = max(5, args.steps // 2), max(2, args.warmup // 2)
+            sub.cpu_seconds = args.extra_cpu_seconds
+            sub.workload = name
+            sub.cpu_queries = 8 if name.startswith("prefill") else None
+            r = run_workload(synth.CONFIGS[name], sub)
+            extras[name] = {key: r[key] for key in ("metric", "value", "unit", "ms_per_step", "steps", "warmup",
+                                                    "config", "hbm_roofline_frac", "algorithmic_bytes_per_step",
+                                                    "mfma", "roofline", "breakdown", "indexshare",
+                                                    "draft_steps_per_s", "mean_acceptance_length", "cpu_baseline")
+                            if key in r}
+        line["extra_workloads"] = extras
+    print(json.dumps(line), flush=True)
+
+
+def run_workload(cfg, args):
+    """Time one workload; returns its JSON record (None for counter-only runs)."""
+    import synth
+
+    if isinstance(cfg, synth.MtpConfig):
+        return bench_mtp(cfg, args)
+    if isinstance(cfg, synth.MtpRoundsConfig):
+        return bench_mtp_rounds(cfg, args)
+    return bench_group(cfg, args)
+
+
+def bench_group(cfg, args):
+    """One dsa_layer_group per step (indexer, top-k, every layer's attention)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
     import long_context_sparse_scores_amd as dsa
     import synth
 
-    cfg = synth.CONFIGS[args.workload]
-    if isinstance(cfg, synth.MtpConfig):
-        bench_mtp(cfg, args)
-        return
-    if isinstance(cfg, synth.MtpRoundsConfig):
-        bench_mtp_rounds(cfg, args)
-        return
     dev = torch.device("cuda:0")
     B, T, L, k, nl = cfg.B, cfg.T, cfg.L, cfg.k, cfg.n_layers
     log("bench: workload %s B=%d T=%d L=%d k=%d layers=%d" % (cfg.name, B, T, L, k, nl))
@@ -140,7 +186,6 @@ def main():
     ws_bytes = dsa.layer_group_workspace_size(args_c)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled before first use
     lib = dsa.lib()
-    import ctypes
     stream = torch.cuda.current_stream(dev).cuda_stream
     argp = ctypes.byref(args_c)
 
@@ -184,7 +229,7 @@ def main():
     idx_bytes = B * T * (L * cfg.D * idx_elem + cfg.H * cfg.D * idx_elem + cfg.H * 4)
     log("bench: indexer %.3f ms, %.1f GB/s" % (idx_ms, idx_bytes / idx_ms / 1e6))
     if args.indexer_only:
-        return
+        return None
 
     # ---------------- per-phase breakdown (same kernels, called one entry point at a time)
     topk_ws = torch.empty(dsa.topk_workspace_size(B, T, L, k), dtype=torch.uint8, device=dev)
@@ -314,8 +359,12 @@ def main():
                         "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                         "indexer_tflops": round(idx_flops / (idx_ms / 1e3) / 1e12, 1)}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, index_fp8=args.index_fp8, kv_fp8=args.kv_fp8)
-    print(json.dumps(line), flush=True)
+        prefill = cfg.T >= PREFILL_MIN_QUERIES
+        line["cpu_baseline"] = cpu_baseline(
+            cfg, args.cpu_seconds, index_fp8=args.index_fp8, kv_fp8=args.kv_fp8,
+            queries=getattr(args, "cpu_queries", None) or (64 if prefill else None),
+            single_thread=args.workload == "decode_128k_b32")
+    return line
 
 
 def copy_calibrate(torch):
@@ -331,42 +380,79 @@ def copy_calibrate(torch):
     log("bench: 5 copies of %d bytes done" % n)
 
 
-def cpu_baseline(cfg, target_s, index_fp8=False, kv_fp8=False):
-    """The CPU oracle (oracle/, plain C fp64 + OpenMP), untuned, on whole
-    sequences of the same workload: indexer over all L keys, top-k, and the
-    attention of every layer.  Runs sequences until about target_s seconds.
-    index_fp8: the oracle reads E4M3 index queries and keys, as the GPU run does."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def omp_set_threads(n):
+    """OpenMP threads for the oracle's next parallel regions started by this thread."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def cpu_baseline(cfg, target_s, index_fp8=False, kv_fp8=False, queries=None, single_thread=False):
+    """The CPU oracle (oracle/, plain C fp64 + OpenMP), untuned, on query
+    tokens of the same workload, each through the whole pipeline: indexer over
+    its visible keys, top-k, and the attention of every layer.  Runs tokens
+    until about target_s seconds on all host threads.  queries: a seeded
+    sample of that many query rows of each sequence (long prefill chunks),
+    else the rows in order.  single_thread: also time one query token on one
+    thread.  index_fp8 / kv_fp8: E4M3 caches, as the GPU run reads them."""
     import numpy as np
 
     import oracle
-    import synth
 
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
-    done, spent = 0, 0.0
-    b = 0
-    rows_per_call = min(cfg.T, 4)  # long chunks: a few query rows at a time, scaled by query tokens
-    t_next = 0
-    while spent < target_s and b < cfg.B:
-        t1 = min(cfg.T, t_next + rows_per_call)
-        sl = slice(t_next, t1)
-        qi = (cfg.q_idx_fp8() if index_fp8 else cfg.q_idx())[b:b + 1, sl]
-        w = cfg.w()[b:b + 1, sl]
+    rows = np.arange(cfg.T)
+    if queries is not None and queries < cfg.T:
+        rows = np.sort(np.random.default_rng(cfg.seed).choice(cfg.T, size=queries, replace=False))
+    qi_all = cfg.q_idx_fp8() if index_fp8 else cfg.q_idx()
+    w_all, pos_all = cfg.w(), cfg.q_pos()
+    q_all = [cfg.q_attn(l) for l in range(cfg.n_layers)]
+
+    def run(b, sel):
         ki = (cfg.k_idx_rows_fp8(b) if index_fp8 else cfg.k_idx_rows(b))[None]
-        pos = cfg.q_pos()[b:b + 1, sl]
-        qs = [cfg.q_attn(l)[b:b + 1, sl] for l in range(cfg.n_layers)]
         kvs = [cfg.kv_seq_fp8(l, b) if kv_fp8 else cfg.kv_seq(l, b) for l in range(cfg.n_layers)]
         t0 = time.perf_counter()
-        oracle.layer_group(qi, w, ki, pos, cfg.k, qs, kvs, cfg.sm_scale, idx_fp8=index_fp8, kv_fp8=kv_fp8)
-        spent += time.perf_counter() - t0
-        done += t1 - t_next
-        t_next = t1
-        if t_next >= cfg.T:
-            b, t_next = b + 1, 0
+        oracle.layer_group(qi_all[b:b + 1, sel], w_all[b:b + 1, sel], ki, pos_all[b:b + 1, sel], cfg.k,
+                           [q[b:b + 1, sel] for q in q_all], kvs, cfg.sm_scale, idx_fp8=index_fp8, kv_fp8=kv_fp8)
+        return time.perf_counter() - t0
+
+    done, spent, b, j = 0, 0.0, 0, 0
+    per_call = min(len(rows), 4)  # a few query rows per call, scaled by query tokens
+    while spent < target_s and b < cfg.B:
+        sel = rows[j:j + per_call]
+        spent += run(b, sel)
+        done += len(sel)
+        j += len(sel)
+        if j >= len(rows):
+            b, j = b + 1, 0
         log("bench: cpu oracle %d query token(s), %.2f s" % (done, spent))
-    return {"value": round(done / spent, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d query tokens of %s (%d sequences x %d tokens), the whole pipeline per token: indexer over "
-                      "the visible keys, top-%d, %d attention layers; fp64 plain C with OpenMP"
-                      % (done, cfg.name, cfg.B, cfg.T, cfg.k, cfg.n_layers)}
+    res = {"value": round(done / spent, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%d query tokens of %s (%d sequences x %d tokens%s), the whole pipeline per token: indexer "
+                     "over the visible keys, top-%d, %d attention layers; fp64 plain C with OpenMP on %d threads"
+                     % (done, cfg.name, cfg.B, cfg.T,
+                        "; a seeded sample of %d of each sequence's %d query rows, the rate extrapolates to all of "
+                        "them" % (len(rows), cfg.T) if len(rows) < cfg.T else "", cfg.k, cfg.n_layers, threads)}
+    if single_thread:
+        omp_set_threads(1)
+        try:
+            t1 = run(0, rows[:1])
+        finally:
+            omp_set_threads(threads)
+        log("bench: cpu oracle 1 query token on one thread, %.2f s" % t1)
+        res["single_thread"] = {"value": round(1.0 / t1, 4), "unit": "query-tokens/s", "cores": 1,
+                                "sample": "query token 0 of sequence 0 of %s, the whole pipeline" % cfg.name}
+    return res
 
 
 def bench_mtp(cfg, args):
@@ -408,15 +494,24 @@ def bench_mtp(cfg, args):
     topk_ws = torch.empty(dsa.topk_workspace_size(B, 1, L, k), dtype=torch.uint8, device=dev)
     attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, 1, k)), dtype=torch.uint8, device=dev)
     ver_ws = torch.empty(dsa.verify_workspace_size(B, S, V), dtype=torch.uint8, device=dev)
+    # the draft path is one dsa_layer_group call whose layers are the S draft
+    # steps: indexer and top-k once over the backbone keys, then S attention
+    # launches over the one backbone latent cache with the step-1 list
+    gargs = dsa.make_group_args(q_idx, w, k_idx, pos, k, q_steps, [kv] * S, cfg.sm_scale, idx, outs)
+    g_bytes = dsa.layer_group_workspace_size(gargs)
+    g_ws = torch.zeros(g_bytes, dtype=torch.uint8, device=dev)
+    lib = dsa.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    import ctypes
+    gptr = ctypes.byref(gargs)
 
     def indexer_step():
         dsa.indexer_scores(q_idx, w, k_idx, pos, scores=scores)
 
     def round_step():
-        indexer_step()
-        dsa.topk(scores, pos, k, idx=idx, ws=topk_ws)
-        for s in range(S):
-            dsa.sparse_mla_attn(q_steps[s], kv, idx, cfg.sm_scale, out=outs[s], ws=attn_ws)
+        rc = lib.dsa_layer_group(gptr, g_ws.data_ptr(), g_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(dsa.last_error())
         return dsa.mtp_draft_verify(t_d, d_d, tok_d, u_d, ur_d, ws=ver_ws)
 
     def timed(fn, steps):
@@ -470,7 +565,7 @@ def bench_mtp(cfg, args):
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_mtp(cfg, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def bench_mtp_rounds(cfg, args):
@@ -623,7 +718,7 @@ def bench_mtp_rounds(cfg, args):
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline_mtp_rounds(cfg, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def cpu_baseline_mtp_rounds(cfg, target_s):
@@ -660,6 +755,7 @@ def cpu_baseline_mtp_rounds(cfg, target_s):
             if spent >= target_s:
                 break
     return {"value": round(tokens / spent, 3), "unit": "verified-tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d round(s) of sequence 0 of %s, each the whole round: indexer over the visible keys, top-%d, "
                       "%d draft attention steps, rejection-sampling verification over V=%d, commit; fp64 plain C "
                       "with OpenMP" % (done, cfg.name, cfg.k, cfg.S, cfg.V)}
@@ -692,6 +788,7 @@ def cpu_baseline_mtp(cfg, target_s):
         done += 1
         log("bench: cpu oracle %d sequence-round(s), %.2f s" % (done, spent))
     return {"value": round(done / spent, 4), "unit": "sequence-rounds/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d of %d sequences of %s, the whole round per sequence; fp64 plain C with OpenMP"
                       % (done, cfg.B, cfg.name)}
 
