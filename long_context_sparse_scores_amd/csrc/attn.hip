@@ -694,10 +694,12 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         const int head = 16 * sw + c;
         if (g == 0) {
             if (DIRECT) {
-                if (lse) lse[(int64_t)bt * kHq + head] = lsum > 0.0f ? (st.m_ref + log2f(lsum)) * 0.69314718055994531f
-                                                                      : -INFINITY;
+                if (lse)
+                    store_wt4(wt_rsrc(lse + (int64_t)bt * kHq), 4u * head,
+                              lsum > 0.0f ? (st.m_ref + log2f(lsum)) * 0.69314718055994531f : -INFINITY);
             } else {
-                part_lse[((int64_t)bt * nsplit + split) * kHq + head] = lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY;
+                store_wt4(wt_rsrc(part_lse + ((int64_t)bt * nsplit + split) * kHq), 4u * head,
+                          lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY);
             }
         }
     } else {
@@ -791,12 +793,12 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         lds_barrier();  // output rows staged
     }
     // every wave stores 8 of the 64 head rows, one 16-byte store per lane per row
-    uint16_t* dst = DIRECT ? out + (int64_t)bt * kHq * kDv : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv;
+    const __amdgpu_buffer_rsrc_t dst = wt_rsrc(DIRECT ? out + (int64_t)bt * kHq * kDv
+                                                      : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int h = 8 * wave + i;
-        *reinterpret_cast<u32x4_t*>(dst + h * kDv + 8 * lane) =
-            *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane);
+        store_wt16(dst, 2u * (h * kDv + 8 * lane), *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane));
     }
 }
 
@@ -856,9 +858,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const uin
     u32x4_t o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    *reinterpret_cast<u32x4_t*>(out + ((int64_t)bt * kHq + head) * kDv + 8 * lane) = o;
+    store_wt16(wt_rsrc(out + ((int64_t)bt * kHq + head) * kDv), 16u * lane, o);
     if (lse && lane == 0)
-        lse[(int64_t)bt * kHq + head] = den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+        store_wt4(wt_rsrc(lse + (int64_t)bt * kHq), 4u * head,
+                  den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY);
 }
 
 struct SplitPlan {

@@ -14,6 +14,24 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Stores written through the L2 to memory (sc1) for results a later kernel
+// reads: the data leaves the L2 while the kernel runs instead of in the
+// write-back that ends it (measured at decode 128K: the index scan 169 -> 166
+// us, an attention layer's split-and-combine 26 -> 24.4 us).  The base must
+// be wave-uniform; offsets are bytes, below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void store_wt16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+}
+__device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 16);
+}
+__device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    store_wt4(r, off, __float_as_uint(v));
+}
+
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16];
 // result register r of lane l is D[4*(l/16) + r][l%16].

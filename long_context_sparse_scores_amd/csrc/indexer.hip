@@ -143,12 +143,12 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
             if (key < L && key <= p) atomicAdd(&hist_lds[score_key(part) >> 21], 1u);
         }
     }
-    float* out = scores + (int64_t)row * L;
+    const __amdgpu_buffer_rsrc_t out = wt_rsrc(scores + (int64_t)row * L);
     if (g == 0) {
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
             const int64_t key = tile_key0(j) + c;
-            if (key < L) out[key] = key <= p ? sc[j] : -INFINITY;
+            if (key < L) store_wt4(out, 4u * (uint32_t)key, key <= p ? sc[j] : -INFINITY);
         }
     }
     if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
@@ -273,12 +273,12 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
             if (key < L && key <= p) atomicAdd(&hist_lds[score_key(sc[j]) >> 21], 1u);
         }
     }
-    float* out = scores + (int64_t)row * L;
+    const __amdgpu_buffer_rsrc_t out = wt_rsrc(scores + (int64_t)row * L);
     if (g < 2) {
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
             const int64_t key = tile_key0(j) + 16 * g + c;
-            if (key < L) out[key] = key <= p ? sc[j] : -INFINITY;
+            if (key < L) store_wt4(out, 4u * (uint32_t)key, key <= p ? sc[j] : -INFINITY);
         }
     }
     if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
@@ -343,7 +343,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const int my_t = t0 + g;
     const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
     const int64_t my_p = q_pos[my_row];
-    float* my_out = scores + my_row * L;
+    // this workgroup's 16 score rows (offsets below 16 * L * 4 bytes)
+    const __amdgpu_buffer_rsrc_t grp_out = wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L);
 
     const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
@@ -405,7 +406,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
             const float rr = __shfl_xor(lo ? k0 : k1, 16, kWave);
             const float score = (lo ? k1 : k0) + rr;
             const int64_t key = key0 + (int64_t)j * kPfTileKeys + 16 * st + c;
-            if (my_t < T && key < L) my_out[key] = key <= my_p ? score : -INFINITY;
+            if (my_t < T && key < L)
+                store_wt4(grp_out, 4u * (uint32_t)((int64_t)(my_t - qg * kPfQueries) * L + key),
+                          key <= my_p ? score : -INFINITY);
         }
         if (j + 1 < ntiles) store_tile(j + 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -470,7 +473,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     const int my_t = t0 + g;
     const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
     const int64_t my_p = q_pos[my_row];
-    float* my_out = scores + my_row * L;
+    // this workgroup's 16 score rows (offsets below 16 * L * 4 bytes)
+    const __amdgpu_buffer_rsrc_t grp_out = wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L);
 
     const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
@@ -531,7 +535,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
             const float rr = __shfl_xor(lo_g ? k0 : k1, 16, kWave);
             const float score = (lo_g ? k1 : k0) + rr;
             const int64_t key = key0 + (int64_t)j * kPf8TileKeys + 16 * st + c;
-            if (my_t < T && key < L) my_out[key] = key <= my_p ? score : -INFINITY;
+            if (my_t < T && key < L)
+                store_wt4(grp_out, 4u * (uint32_t)((int64_t)(my_t - qg * kPfQueries) * L + key),
+                          key <= my_p ? score : -INFINITY);
         }
         if (j + 1 < ntiles) store_tile(j + 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -405,6 +405,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
     static_assert(kPer % 2 == 0, "odd padded stride");
     auto pw = [](int w) { return w + w / kPer; };
     uint32_t base = 0;
+    const __amdgpu_buffer_rsrc_t out_wt = wt_rsrc(out);
     for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kCandLds * 32) {
         const int nw = (int)min((int64_t)kCandLds, (n - c0 + 31) / 32);
         for (int i = threadIdx.x; i < pw(nw - 1) + 1; i += NT) s.order.bits[i] = 0u;
@@ -434,7 +435,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
             if (p >= 0 && p < (int64_t)nw * 32) {
                 const int w = pw((int)(p >> 5));
                 const uint32_t below = s.order.bits[w] & ((1u << (p & 31)) - 1u);
-                out[base + s.order.wpre[w] + (uint32_t)__popc(below)] = (int32_t)s.sel[j];
+                store_wt4(out_wt, 4u * (base + s.order.wpre[w] + (uint32_t)__popc(below)), s.sel[j]);
             }
         }
         base += total;
@@ -547,6 +548,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     // Candidates are staged per wave in LDS and appended to the row's list in
     // batches: one global atomic per batch rather than per 64 keys.
     uint32_t staged = 0;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t cpos_out = wt_rsrc(rw.cpos), ckey_out = wt_rsrc(rw.ckey);
     uint32_t* sp = stage_pos[wave];
     uint32_t* sk = stage_key[wave];
     auto flush = [&]() {
@@ -557,8 +559,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         for (uint32_t j = lane; j < staged; j += kWave) {
             const uint32_t slot = base + j;
             if (slot < (uint32_t)lo.cap) {
-                rw.cpos[slot] = sp[j];
-                rw.ckey[slot] = sk[j];
+                store_wt4(cpos_out, 4u * slot, sp[j]);
+                store_wt4(ckey_out, 4u * slot, sk[j]);
             }
         }
         __builtin_amdgcn_wave_barrier();
