@@ -110,19 +110,36 @@ enum class TopkState {
     kCleared,    // the histogram and counters are zero (TopkPrep without hist)
     kHistogram,  // counters zero and the histogram complete (TopkPrep with hist)
 };
+// clear_after: per-row words the selection clears after its work (the next
+// attention launch's merge counters), words per row at base + row * words.
+struct RowClear {
+    uint32_t* base = nullptr;
+    int words = 0;
+};
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, TopkState state = TopkState::kNone);
+                       hipStream_t stream, TopkState state = TopkState::kNone, RowClear clear_after = RowClear());
 
 int attn_num_splits(int rows, int k);
 size_t attn_ws_bytes(int rows, int k);
+// Per-query counters in an attention workspace that a launch with merge = true
+// needs zero when it starts (each such launch leaves them zero): `words` words
+// per query at base + row * words; base == nullptr when the shape has none.
+struct AttnSync {
+    uint32_t* base = nullptr;
+    int words = 0;
+};
+AttnSync attn_sync(void* ws, int rows, int k);
+// merge: merge the splits of a query inside the split launch when they can all
+// be resident at once (the workspace's counters must then be zero); otherwise,
+// and always with merge = false, a combine launch follows.
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                        int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool merge = false);
 
 // The same attention over latent rows stored as E4M3 codes (kv_bstride in bytes).
 hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                            int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, bool merge = false);
 
 size_t verify_ws_bytes(int B, int S, int V);
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* draft_tokens, const float* u_acc,

@@ -594,8 +594,10 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                      const int32_t* __restrict__ q_pos, int L,
                                                                      int k, Layout lo, void* ws,
-                                                                     int32_t* __restrict__ idx) {
+                                                                     int32_t* __restrict__ idx, RowClear clear) {
     const int row = blockIdx.x;
+    if (clear.base)
+        for (int i = threadIdx.x; i < clear.words; i += kSelectThreads) clear.base[(int64_t)row * clear.words + i] = 0u;
     const int64_t n = n_visible(q_pos, row, L);
     int32_t* out = idx + (int64_t)row * k;
     const RowWs rw = row_ws(ws, row, lo);
@@ -649,7 +651,7 @@ TopkPrep topk_prep(void* ws, int rows, int L, bool hist) {
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, TopkState state) {
+                       hipStream_t stream, TopkState state, RowClear clear_after) {
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
     if (state == TopkState::kNone) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
@@ -660,7 +662,7 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        state == TopkState::kHistogram ? 1 : 0);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
-                       idx);
+                       idx, clear_after);
     return hipGetLastError();
 }
 

@@ -621,3 +621,35 @@ def test_group_without_indexshare(dsa):
         np.testing.assert_allclose(host(lses[l]), ref_lse, atol=LSE_TOL, rtol=0)
     for l in range(1, n):
         assert not np.array_equal(got_idx[l], got_idx[0]), "layer %d selected the same rows as layer 0" % l
+
+
+@pytest.mark.parametrize("B", [32, 40, 64, 100])
+def test_group_splits_merged_in_kernel(dsa, B):
+    # Batches of 32+ one-token queries split each list into at most 8 parts
+    # whose partials the attention launch merges itself (B = 40: 6 splits with
+    # uneven head groups; B = 100: 2 splits).  Lists bit-exact against the
+    # oracle, outputs within tolerance on sampled queries, and, where the
+    # standalone entry point splits the same way (B = 32, 64), bit-equal to it.
+    L, k = 3000, 2048
+    say("group with in-kernel split merge B=%d" % B)
+    qi = synth.int_bf16(100 + B, 1, (B, 1, 32, 128))
+    w = synth.pow2_f32(100 + B, 2, (B, 1, 32))
+    ki = synth.int_bf16(100 + B, 3, (B, L, 128))
+    pos = np.full((B, 1), L - 1, np.int32)
+    pos[1, 0] = 1000
+    pos[2, 0] = 5  # fewer visible keys than k: -1 padded list
+    qs = [synth.normal_bf16(100 + B, 4 + l, (B, 1, 64, 576)) for l in range(2)]
+    kvs = [synth.normal_bf16(100 + B, 6 + l, (B, L, 576)) for l in range(2)]
+    dq, dkv = [bf16_dev(q) for q in qs], [bf16_dev(kv) for kv in kvs]
+    idx, outs, lses = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), k, dq, dkv, 1 / 16,
+                                      want_lse=True)
+    ref_idx = oracle.topk(oracle.indexer_scores(qi, w, ki, pos), pos, k)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    sample = [0, 1, 2, B - 1]
+    for l in range(2):
+        ref, ref_lse = oracle.sparse_mla_attn(qs[l][sample], kvs[l][sample], ref_idx[sample], 1 / 16)
+        assert_attn_close(host(outs[l])[sample], ref, "layer %d" % l)
+        np.testing.assert_allclose(host(lses[l])[sample], ref_lse, atol=LSE_TOL, rtol=0)
+        if B in (32, 64):
+            alone = dsa.sparse_mla_attn(dq[l], dkv[l], idx, 1 / 16)
+            assert torch.equal(alone.view(torch.int16), outs[l].view(torch.int16)), "layer %d" % l
