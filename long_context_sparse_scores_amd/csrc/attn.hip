@@ -570,13 +570,6 @@ __device__ __forceinline__ void wait_gathers(int tiles_left, int nload) {
 constexpr int kMergeNB = 8;
 static_assert(kWave * 8 == kDv, "8 value dims per lane");
 
-__device__ __forceinline__ u32x4_t load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
-}
-__device__ __forceinline__ float load_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 16));
-}
-
 template <int NB>
 __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                                              int bt, int head, int nsplit, uint16_t* __restrict__ out,

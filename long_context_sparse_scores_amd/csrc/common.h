@@ -32,6 +32,18 @@ __device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off
     store_wt4(r, off, __float_as_uint(v));
 }
 
+// Device-scope loads (sc1): they miss in this XCD's L2, so they see what
+// workgroups on other XCDs wrote through to memory during the same launch.
+__device__ __forceinline__ u32x4_t load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+}
+__device__ __forceinline__ uint32_t load_dev4u(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 16);
+}
+__device__ __forceinline__ float load_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(load_dev4u(r, off));
+}
+
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16];
 // result register r of lane l is D[4*(l/16) + r][l%16].
@@ -55,14 +67,21 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum across one wave.
+// Inclusive prefix sum across one wave, in DPP moves (no LDS permutes): row
+// shifts by 1, 2, 4, 8 scan each row of 16 lanes (a lane shifted in from
+// outside the row adds 0), then row_bcast:15 adds the end of rows 0 and 2 to
+// rows 1 and 3, and row_bcast:31 the end of row 1 to rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t x) {
+    return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        uint32_t y = __shfl_up(x, off, kWave);
-        if (l >= off) x += y;
-    }
+    x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 

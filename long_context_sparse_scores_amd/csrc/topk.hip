@@ -17,29 +17,34 @@
 //           appends every key whose top digit is T or above to the row's
 //           candidate list (fewer than k lie above T, so the list is the
 //           top-k plus the keys that share T's bin);
-//   select  one workgroup per row, from the candidates alone: the middle and
-//           low digits of K*, the number of keys equal to K* to take and,
-//           when ties straddle the cut, the lowest positions among them (a
-//           second radix select, on the complemented position, or a direct
-//           ranking when there are at most 64 of them); the k kept positions
-//           are compacted into LDS and written out in ascending order from a
-//           bitmap of the row's positions (393216 per chunk, in the space the
-//           candidate copy used).
+//   select  one workgroup per row, from the candidates alone: the middle
+//           digit of K*; then, when at most 64 keys share K*'s top 22 bits
+//           (the usual case), one wave ranks them by key and position;
+//           otherwise the low digit, the number of keys equal to K* to take
+//           and, when ties straddle the cut, the lowest positions among them
+//           (a second radix select, on the complemented position, or a direct
+//           ranking of at most 64); the k kept positions are compacted into
+//           LDS and written out in ascending order from a bitmap of the row's
+//           positions (393216 per chunk, in the space the candidate copy used).
 // In the layer group the decode indexer does the first two: it clears the
 // counters and adds the top-digit histogram of the scores it holds in
-// registers, so the scores are read once (filter) and select never touches
-// them.  That histogram must start from zero, and no launch of the group can
-// clear it before the indexer adds to it; so the selection, its last user,
-// clears it for the next call and leaves a stamp of the row and the shape.
-// The filter uses the histogram only when it finds that stamp and the counts
-// add up to the row's visible keys; otherwise (a workspace's first use, or
-// the first after a change of shape) it counts the row itself, slower but
-// with the same result.
-// (Running select in the last filter workgroup of each row would save a
-// launch, but publishing the candidates across XCDs then takes an L2
-// write-back per workgroup, which costs far more on this part.)
-// When a row's candidate list overflows its capacity (heavily tied scores),
-// select scans the whole row instead; the result is the same.
+// registers.  That histogram must start from zero, and no launch of the group
+// can clear it before the indexer adds to it; so the selection, its last
+// user, clears it for the next call and leaves a stamp of the row and the
+// shape.  The histogram is used only when that stamp is there and the counts
+// add up to the row's visible keys; otherwise (a workspace's first use, or the
+// first after a change of shape) the row is counted again from its scores,
+// slower but with the same result.
+// Filter and select then run as one launch (also for standalone calls of up
+// to 256 rows, after the histogram pass): each slice workgroup writes its
+// candidates in position order to a region of its own, through to memory, and
+// the last one of the row to arrive selects from all regions, so the kept
+// positions come out of one ordered compaction with no sort (see
+// topk_fused_kernel).  Many rows without the indexer's histogram (prefill)
+// keep the separate filter and select launches, whose small filter
+// workgroups stream long rows with more of them resident per CU.
+// When a row's candidates overflow what the selection can hold (heavily tied
+// scores), it scans the whole row instead; the result is the same.
 #include "common.h"
 
 namespace dsa {
@@ -58,12 +63,17 @@ constexpr int kFineSlice = 65536;    // slices at least this long take the 8192-
 constexpr int kSelMax = 2048;        // the kept positions (k <= 2048) are compacted in LDS
 constexpr int kCandLds = 12288;      // candidates the selection holds in LDS
 constexpr int kSelBatch = kCandLds / kSelectThreads;  // loads in flight per thread in its passes
+constexpr int kFusedTarget = 256;    // slice workgroups over all rows in the fused pass (one per CU)
+constexpr int kFusedMaxSlices = 256; // slices per row in the fused pass (count words per row)
+constexpr int kFPer = 16;            // keys per thread and batch in the fused pass
+constexpr int kFusedMinSlice = kFPer * kSelectThreads;
 
 // Per-row workspace (32-bit words).
 // kStT, kStAbove: the threshold digit T and the count of keys whose top digit is above it.
+// kCtrDone: the fused pass's slice workgroups that have published their candidates.
 // kStamp: written by the selection once it has cleared the row's histogram
 // (see histogram_stamp); the counters before it are cleared for every call.
-enum : int { kCtrCand = 0, kStT = 1, kStAbove = 2, kStamp = 7, kCtrWords = 8 };
+enum : int { kCtrCand = 0, kStT = 1, kStAbove = 2, kCtrDone = 3, kStamp = 7, kCtrWords = 8 };
 
 struct Layout {
     int rows;     // rows (queries) of the call
@@ -71,13 +81,17 @@ struct Layout {
     int slice;    // elements per slice (multiple of 256)
     int nslice;   // slices per row
     int cap;      // candidate capacity per row
-    __host__ __device__ size_t row_words() const { return kBins + kCtrWords + 2 * (size_t)cap; }
+    int fslice;   // fused pass: elements per slice (multiple of kSelectThreads)
+    int fnslice;  // fused pass: slices per row
+    int pcap;     // fused pass: candidate capacity per slice (cap / fnslice)
+    __host__ __device__ size_t row_words() const { return kBins + kCtrWords + kFusedMaxSlices + 2 * (size_t)cap; }
 };
 
 struct RowWs {
     uint32_t* hist1;   // [kBins] top digit
     uint32_t* ctr;     // [kCtrWords]
-    uint32_t* cpos;    // [cap] candidate positions
+    uint32_t* scnt;    // [kFusedMaxSlices] fused pass: candidates per slice
+    uint32_t* cpos;    // [cap] candidate positions (fused pass: pcap per slice, in position order)
     uint32_t* ckey;    // [cap] candidate keys
 };
 
@@ -86,7 +100,8 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int row, const Layout& lo) {
     RowWs r;
     r.hist1 = b;
     r.ctr = b + kBins;
-    r.cpos = r.ctr + kCtrWords;
+    r.scnt = r.ctr + kCtrWords;
+    r.cpos = r.scnt + kFusedMaxSlices;
     r.ckey = r.cpos + lo.cap;
     return r;
 }
@@ -210,8 +225,10 @@ struct SelectLds {
     uint32_t h[kBins];
     uint32_t sel[kSelMax];
     uint32_t scratch[NT / kWave];
+    uint32_t sbase[kFusedMaxSlices], scnt[kFusedMaxSlices];  // fused pass: slice offsets and counts
+    uint32_t gkey[kWave];                                     // a small group's keys (positions in sel)
     BinPick pick;
-    uint32_t nsel, cut;
+    uint32_t nsel, cut, cut_key;
 };
 
 // Clear h[0, nbins), let fill(h) add to it, then pick the bin of the need-th largest.
@@ -225,16 +242,181 @@ __device__ __forceinline__ BinPick hist_pick(SelectLds<NT>& s, int nbins, uint32
     return pick_bin<NT>(hp, nbins, need, s.scratch, &s.pick);
 }
 
+// Ordered compaction of one batch over the workgroup: item j of thread t is
+// item j*NT + t of the batch (so wave w holds items j*NT + 64w .. +63); every
+// flagged item gets emit(slot, j), the slots numbered 0, 1, .. in item order.
+// `cnt` holds PER * NT / 64 words of LDS.  Returns the batch's flagged count.
+template <int NT, int PER, typename Emit>
+__device__ __forceinline__ uint32_t ordered_slots(const bool (&f)[PER], uint32_t* cnt, uint32_t* scratch, Emit&& emit) {
+    constexpr int NW = NT / kWave;
+    static_assert(PER * NW <= NT, "one count per thread in the scan");
+    const int wave = threadIdx.x / kWave;
+    uint64_t m[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) m[j] = __ballot(f[j]);
+    if (lane_id() == 0) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) cnt[j * NW + wave] = (uint32_t)__popcll(m[j]);
+    }
+    lds_sync();
+    const uint32_t x = (int)threadIdx.x < PER * NW ? cnt[threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t ex = excl_scan<NT>(x, scratch, &total);
+    if ((int)threadIdx.x < PER * NW) cnt[threadIdx.x] = ex;
+    lds_sync();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (f[j]) emit(cnt[j * NW + wave] + lane_rank(m[j]), j);
+    lds_sync();  // before cnt is reused
+    return total;
+}
+
+// The row's threshold digit T (and the count of keys above its bin) from the
+// top-digit histogram in the workspace.  checked: the indexer added that
+// histogram onto what the last selection left, so it is used only when that
+// selection's stamp is there and it counts the row's visible keys exactly;
+// otherwise (a workspace's first use, or the first after a change of shape)
+// the row is counted here into own_hist (kBins words of LDS), from its scores.
+// hp and stamp: this thread's part of the workspace histogram and the row's
+// stamp word, loaded by the caller (with its other first loads).
+template <int NT>
+__device__ __forceinline__ BinPick row_threshold(const HistPart<NT>& hp, uint32_t stamp,
+                                                 const float* __restrict__ row_scores, int64_t n, int k,
+                                                 const Layout& lo, int row, bool checked, uint32_t* own_hist,
+                                                 uint32_t* scratch, BinPick* pick) {
+    uint32_t total;
+    BinPick b0 = pick_bin<NT>(hp, kBins, (uint32_t)k, scratch, pick, &total);
+    if (checked && (stamp != histogram_stamp(lo, row) || total != (uint32_t)n)) {
+        for (int i = threadIdx.x; i < kBins; i += NT) own_hist[i] = 0u;
+        lds_sync();
+        for (int64_t i = threadIdx.x; i < n; i += NT) atomicAdd(&own_hist[score_key(row_scores[i]) >> 21], 1u);
+        lds_sync();
+        const HistPart<NT> hp2 = load_hist<NT>(own_hist, kBins);
+        b0 = pick_bin<NT>(hp2, kBins, (uint32_t)k, scratch, pick);
+    }
+    return b0;
+}
+
+// The selection is done with the row's histogram (every reader has read it):
+// leave it zero for the next selection, whose indexer adds into it, and mark
+// it so; clear the words the caller asked to be cleared.
+template <int NT>
+__device__ __forceinline__ void finish_row(const RowWs& rw, const Layout& lo, int row, RowClear clear) {
+    if (clear.base)
+        for (int i = threadIdx.x; i < clear.words; i += NT) clear.base[(int64_t)row * clear.words + i] = 0u;
+    for (int i = threadIdx.x; i < kBins; i += NT) rw.hist1[i] = 0u;
+    if (threadIdx.x == 0) rw.ctr[kStamp] = histogram_stamp(lo, row);
+}
+
+// The last kept key K* and, among the keys equal to it, the highest kept
+// position: the kept set is {key > K*} + {key == K*, position <= pos_cut}.
+struct Cut {
+    uint32_t kstar, pos_cut;
+};
+
+// The cut from b1, the bin of K*'s middle digit among the keys whose top digit
+// is T (need = k minus the count of keys above T's bin).  for_candidates(f)
+// calls f(key, position) for every candidate (every thread takes part).
+// Usually few keys share K*'s top 22 bits: then one wave ranks them directly
+// (by key, then position); otherwise the low digit and, when ties straddle the
+// cut, the positions are radix selected.
+template <int NT, typename ForCand>
+__device__ __forceinline__ Cut find_cut(SelectLds<NT>& s, uint32_t T, uint32_t need, const BinPick& b1,
+                                        ForCand&& for_candidates) {
+    const int lane = lane_id();
+    const uint32_t need1 = need - b1.above;
+    const uint32_t prefix = (T << 11) | b1.bin;  // top 22 bits of K*
+    if (b1.count <= (uint32_t)kWave) {
+        if (threadIdx.x == 0) s.nsel = 0u;
+        lds_sync();
+        for_candidates([&](uint32_t key, uint32_t pos) {
+            if ((key >> 10) == prefix) {
+                const uint32_t slot = atomicAdd(&s.nsel, 1u);
+                s.gkey[slot] = key;
+                s.sel[slot] = pos;
+            }
+        });
+        lds_sync();
+        if (threadIdx.x < kWave) {
+            const bool have = (uint32_t)lane < b1.count;
+            const uint32_t mk = have ? s.gkey[lane] : 0u, mp = have ? s.sel[lane] : 0xFFFFFFFFu;
+            uint32_t rank = 0;  // group members before this one: larger key, or equal key and lower position
+            for (uint32_t j = 0; j < b1.count; ++j) {
+                const uint32_t ok = s.gkey[j], op = s.sel[j];
+                rank += (ok > mk || (ok == mk && op < mp)) ? 1u : 0u;
+            }
+            if (have && rank == need1 - 1u) {
+                s.cut_key = mk;
+                s.cut = mp;
+            }
+        }
+        lds_sync();
+        const Cut c{s.cut_key, s.cut};
+        lds_sync();
+        return c;
+    }
+    const BinPick b2 = hist_pick<NT>(s, 1024, need1, [&](uint32_t* h) {
+        for_candidates([&](uint32_t key, uint32_t) {
+            if ((key >> 10) == prefix) atomicAdd(&h[key & 0x3FFu], 1u);
+        });
+    });
+    const uint32_t kstar = (prefix << 10) | b2.bin;
+    const uint32_t take_eq = need1 - b2.above;  // of the b2.count keys equal to K*
+    // ties kept: position <= pos_cut.  When only some are taken, the take_eq
+    // lowest positions are the take_eq largest values of ~position (distinct).
+    uint32_t pos_cut = 0xFFFFFFFFu;
+    if (take_eq < b2.count && b2.count <= (uint32_t)kWave) {
+        // few ties: gather them, and one wave ranks each by position
+        if (threadIdx.x == 0) s.nsel = 0u;
+        lds_sync();
+        for_candidates([&](uint32_t key, uint32_t pos) {
+            if (key == kstar) s.sel[atomicAdd(&s.nsel, 1u)] = pos;
+        });
+        lds_sync();
+        if (threadIdx.x < kWave) {
+            const uint32_t my = (uint32_t)lane < b2.count ? s.sel[lane] : 0xFFFFFFFFu;
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < b2.count; ++j) rank += s.sel[j] < my ? 1u : 0u;
+            if ((uint32_t)lane < b2.count && rank == take_eq - 1u) s.cut = my;
+        }
+        lds_sync();
+        pos_cut = s.cut;
+    } else if (take_eq < b2.count) {
+        auto ties = [&](auto&& g) {
+            for_candidates([&](uint32_t key, uint32_t pos) {
+                if (key == kstar) g(~pos);
+            });
+        };
+        const BinPick t0 = hist_pick<NT>(s, kBins, take_eq, [&](uint32_t* h) {
+            ties([&](uint32_t v) { atomicAdd(&h[v >> 21], 1u); });
+        });
+        const uint32_t tneed1 = take_eq - t0.above;
+        const BinPick t1 = hist_pick<NT>(s, kBins, tneed1, [&](uint32_t* h) {
+            ties([&](uint32_t v) {
+                if ((v >> 21) == t0.bin) atomicAdd(&h[(v >> 10) & 0x7FFu], 1u);
+            });
+        });
+        const uint32_t tneed2 = tneed1 - t1.above;
+        const uint32_t tprefix = (t0.bin << 11) | t1.bin;
+        const BinPick t2 = hist_pick<NT>(s, 1024, tneed2, [&](uint32_t* h) {
+            ties([&](uint32_t v) {
+                if ((v >> 10) == tprefix) atomicAdd(&h[v & 0x3FFu], 1u);
+            });
+        });
+        pos_cut = ~((tprefix << 10) | t2.bin);
+    }
+    return Cut{kstar, pos_cut};
+}
+
 // The k kept positions of one row with n > k visible keys, ascending, into
-// out[0, k): NT threads, the candidate list (keys with top digit >= T) of the
-// filter pass, or the row's scores after an overflow.
+// out[0, k): NT threads.  The candidates (the keys whose top digit is T or
+// above; need = k minus the count of keys above T's bin) come from the filter
+// pass's list of ncand entries when from_list, else from the row's scores
+// (the list overflowed).
 template <int NT>
 __device__ __forceinline__ void select_row(const float* __restrict__ row_scores, int64_t n, int k, const RowWs& rw,
-                                           int cap, int32_t* __restrict__ out, SelectLds<NT>& s) {
-    const uint32_t ncand = rw.ctr[kCtrCand];
-    const uint32_t T = rw.ctr[kStT];
-    const uint32_t need = (uint32_t)k - rw.ctr[kStAbove];
-    const bool from_list = ncand <= (uint32_t)cap;                  // else the list overflowed
+                                           bool from_list, uint32_t ncand, uint32_t T, uint32_t need,
+                                           int32_t* __restrict__ out, SelectLds<NT>& s) {
     const bool in_lds = from_list && ncand <= (uint32_t)kCandLds;
     const int lane = lane_id();
     constexpr uint32_t kStep = kSelBatch * NT;
@@ -311,64 +493,14 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
                 if (ok[j]) f(ck[j], cp[j]);
         });
     };
-    // K*: its middle and low digits among the keys whose top digit is T
+    // K*: its middle digit among the keys whose top digit is T, then the cut
     const BinPick b1 = hist_pick<NT>(s, kBins, need, [&](uint32_t* h) {
         for_candidates([&](uint32_t key, uint32_t) {
             if ((key >> 21) == T) atomicAdd(&h[(key >> 10) & 0x7FFu], 1u);
         });
     });
-    const uint32_t need1 = need - b1.above;
-    const uint32_t prefix = (T << 11) | b1.bin;  // top 22 bits of K*
-    const BinPick b2 = hist_pick<NT>(s, 1024, need1, [&](uint32_t* h) {
-        for_candidates([&](uint32_t key, uint32_t) {
-            if ((key >> 10) == prefix) atomicAdd(&h[key & 0x3FFu], 1u);
-        });
-    });
-    const uint32_t kstar = (prefix << 10) | b2.bin;
-    const uint32_t take_eq = need1 - b2.above;  // of the b2.count keys equal to K*
-    // ties kept: position <= pos_cut.  When only some are taken, the take_eq
-    // lowest positions are the take_eq largest values of ~position (distinct).
-    uint32_t pos_cut = 0xFFFFFFFFu;
-    if (take_eq < b2.count && b2.count <= (uint32_t)kWave) {
-        // few ties: gather them, and one wave ranks each by position
-        if (threadIdx.x == 0) s.nsel = 0u;
-        lds_sync();
-        for_candidates([&](uint32_t key, uint32_t pos) {
-            if (key == kstar) s.sel[atomicAdd(&s.nsel, 1u)] = pos;
-        });
-        lds_sync();
-        if (threadIdx.x < kWave) {
-            const uint32_t my = (uint32_t)lane < b2.count ? s.sel[lane] : 0xFFFFFFFFu;
-            uint32_t rank = 0;
-            for (uint32_t j = 0; j < b2.count; ++j) rank += s.sel[j] < my ? 1u : 0u;
-            if ((uint32_t)lane < b2.count && rank == take_eq - 1u) s.cut = my;
-        }
-        lds_sync();
-        pos_cut = s.cut;
-    } else if (take_eq < b2.count) {
-        auto ties = [&](auto&& g) {
-            for_candidates([&](uint32_t key, uint32_t pos) {
-                if (key == kstar) g(~pos);
-            });
-        };
-        const BinPick t0 = hist_pick<NT>(s, kBins, take_eq, [&](uint32_t* h) {
-            ties([&](uint32_t v) { atomicAdd(&h[v >> 21], 1u); });
-        });
-        const uint32_t tneed1 = take_eq - t0.above;
-        const BinPick t1 = hist_pick<NT>(s, kBins, tneed1, [&](uint32_t* h) {
-            ties([&](uint32_t v) {
-                if ((v >> 21) == t0.bin) atomicAdd(&h[(v >> 10) & 0x7FFu], 1u);
-            });
-        });
-        const uint32_t tneed2 = tneed1 - t1.above;
-        const uint32_t tprefix = (t0.bin << 11) | t1.bin;
-        const BinPick t2 = hist_pick<NT>(s, 1024, tneed2, [&](uint32_t* h) {
-            ties([&](uint32_t v) {
-                if ((v >> 10) == tprefix) atomicAdd(&h[v & 0x3FFu], 1u);
-            });
-        });
-        pos_cut = ~((tprefix << 10) | t2.bin);
-    }
+    const Cut cut = find_cut<NT>(s, T, need, b1, for_candidates);
+    const uint32_t kstar = cut.kstar, pos_cut = cut.pos_cut;
     // compact the k kept positions: per batch, one LDS atomic per wave
     if (threadIdx.x == 0) s.nsel = 0u;
     lds_sync();
@@ -512,8 +644,9 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     __shared__ BinPick pick;
     __shared__ uint32_t own_hist[kBins];  // only when the row's histogram cannot be trusted
 
-    // the row's top-digit histogram, then this wave's first batch of scores
+    // the histogram, the stamp and this wave's first batch of scores in flight together
     const HistPart<kThreads> hp = load_hist<kThreads>(rw.hist1, kBins);
+    const uint32_t stamp = rw.ctr[kStamp];
     const int64_t w0 = start + (int64_t)wave * (lo.slice / kWaves);
     const int64_t w1 = min(w0 + lo.slice / kWaves, n);
     const float* row_scores = scores + (int64_t)row * L;
@@ -522,23 +655,12 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int64_t i = i0 + j * kWave + lane;
-            v[j] = i < w1 ? row_scores[i] : 0.0f;
+            v[j] = row_scores[i < w1 ? i : w1 - 1];  // w1 >= 1; past w1 never used
         }
     };
     load_batch(w0);
-    uint32_t total;
-    BinPick b0 = pick_bin<kThreads>(hp, kBins, (uint32_t)k, scratch, &pick, &total);
-    if (hist_checked && (rw.ctr[kStamp] != histogram_stamp(lo, row) || total != (uint32_t)n)) {
-        // The histogram did not start from zero: no selection of this shape
-        // cleared it before the indexer added to it (a workspace's first use, or
-        // the first after a change of shape).  Count this row here, from its scores.
-        for (int i = threadIdx.x; i < kBins; i += kThreads) own_hist[i] = 0u;
-        lds_sync();
-        for (int64_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&own_hist[score_key(row_scores[i]) >> 21], 1u);
-        lds_sync();
-        const HistPart<kThreads> hp2 = load_hist<kThreads>(own_hist, kBins);
-        b0 = pick_bin<kThreads>(hp2, kBins, (uint32_t)k, scratch, &pick);
-    }
+    const BinPick b0 = row_threshold<kThreads>(hp, stamp, row_scores, n, k, lo, row, hist_checked != 0, own_hist,
+                                               scratch, &pick);
     const uint32_t T = b0.bin;
     if (slice == 0 && threadIdx.x == 0) {  // for the selection
         rw.ctr[kStT] = T;
@@ -601,17 +723,224 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float
     const int64_t n = n_visible(q_pos, row, L);
     int32_t* out = idx + (int64_t)row * k;
     const RowWs rw = row_ws(ws, row, lo);
-    // The filter pass was the histogram's last reader: leave it zero for the
-    // next selection, whose indexer adds into it, and mark it so.
-    for (int i = threadIdx.x; i < kBins; i += kSelectThreads) rw.hist1[i] = 0u;
-    if (threadIdx.x == 0) rw.ctr[kStamp] = histogram_stamp(lo, row);
+    finish_row<kSelectThreads>(rw, lo, row, RowClear());  // the filter pass was the histogram's last reader
     if (n <= k) {
         for (int j = threadIdx.x; j < k; j += kSelectThreads) out[j] = j < n ? j : -1;
         return;
     }
     __shared__ SelectLds<kSelectThreads> sl;
-    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, rw, lo.cap, out, sl);
+    const uint32_t ncand = rw.ctr[kCtrCand];
+    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, rw, ncand <= (uint32_t)lo.cap, ncand, rw.ctr[kStT],
+                               (uint32_t)k - rw.ctr[kStAbove], out, sl);
 }
+
+// Filter and selection in one launch, for rows whose top-digit histogram the
+// indexer added (the layer group).  Each row is cut into slices of whole
+// batches (about one workgroup per CU over all rows).  A slice workgroup finds
+// T from the histogram, and writes the keys of its slice whose top digit is T
+// or above, in position order (a workgroup prefix scan per batch, no global
+// atomics), to its own region of pcap entries, then its count; those stores
+// go through to memory and are acknowledged before the workgroup counts its
+// arrival.  The last slice workgroup of the row to arrive selects: it reads
+// the counts and the regions with device-scope loads (they were written on
+// other XCDs in this launch), so the candidates land in LDS in position
+// order, re-reads the scores of any slice whose region overflowed, finds the
+// cut, and writes the kept positions through one ordered compaction, already
+// ascending.  No workgroup waits for another.  More candidates than the LDS
+// copy holds: the selection scans the row's scores (same result, slower).
+__global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float* __restrict__ scores,
+                                                                    const int32_t* __restrict__ q_pos, int L, int k,
+                                                                    Layout lo, void* ws, int hist_checked,
+                                                                    int32_t* __restrict__ idx, RowClear clear) {
+    constexpr int NT = kSelectThreads;
+    const int row = blockIdx.x / lo.fnslice;
+    const int slice = blockIdx.x % lo.fnslice;
+    const RowWs rw = row_ws(ws, row, lo);
+    int32_t* out = idx + (int64_t)row * k;
+    __shared__ SelectLds<NT> sl;
+    const float* row_scores = scores + (int64_t)row * L;
+    const int64_t start = (int64_t)slice * lo.fslice;
+    const int64_t lim = min(start + (int64_t)lo.fslice, (int64_t)L);  // the slice within the row
+    float v[kFPer];
+    auto load_batch = [&](int64_t i0, int64_t i1) {  // i0 < i1; past i1 a valid key is read, never used
+#pragma unroll
+        for (int j = 0; j < kFPer; ++j) {
+            const int64_t i = i0 + j * NT + threadIdx.x;
+            v[j] = row_scores[i < i1 ? i : i1 - 1];
+        }
+    };
+    // Every first load in one round trip: the row's length, the histogram and
+    // its stamp, and this thread's first batch of the slice (up to the row's
+    // end; keys past the visible ones are masked below).  The threshold comes
+    // before any branch on the length, so no load waits for it.  (Rows with
+    // n <= k get a meaningless threshold, unused.)
+    const int64_t n = n_visible(q_pos, row, L);
+    const HistPart<NT> hp = load_hist<NT>(rw.hist1, kBins);
+    const uint32_t stamp = rw.ctr[kStamp];
+    load_batch(start, lim);
+    const BinPick b0 =
+        row_threshold<NT>(hp, stamp, row_scores, n, k, lo, row, hist_checked != 0, sl.h, sl.scratch, &sl.pick);
+    const uint32_t T = b0.bin;
+    if (n <= k) {
+        if (slice == 0) {
+            finish_row<NT>(rw, lo, row, clear);
+            for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
+        }
+        return;
+    }
+    if (start >= n) return;  // not counted: the row has nact active slices
+    const int64_t end = min(lim, n);
+    const int nact = (int)((n + lo.fslice - 1) / lo.fslice);
+
+    // This slice's candidates, in position order, to its region.
+    {
+        const __amdgpu_buffer_rsrc_t pos_r = wt_rsrc(rw.cpos + (int64_t)slice * lo.pcap);
+        const __amdgpu_buffer_rsrc_t key_r = wt_rsrc(rw.ckey + (int64_t)slice * lo.pcap);
+        uint32_t run = 0;
+        for (int64_t i0 = start; i0 < end; i0 += (int64_t)kFPer * NT) {
+            if (i0 != start) load_batch(i0, end);
+            bool f[kFPer];
+            uint32_t key[kFPer];
+#pragma unroll
+            for (int j = 0; j < kFPer; ++j) {
+                key[j] = score_key(v[j]);
+                f[j] = i0 + j * NT + (int)threadIdx.x < end && (key[j] >> 21) >= T;
+            }
+            const uint32_t c = ordered_slots<NT, kFPer>(f, sl.sel, sl.scratch, [&](uint32_t slot, int j) {
+                slot += run;
+                if (slot < (uint32_t)lo.pcap) {
+                    store_wt4(pos_r, 4u * slot, (uint32_t)(i0 + j * NT + threadIdx.x));
+                    store_wt4(key_r, 4u * slot, key[j]);
+                }
+            });
+            run += c;
+        }
+        if (threadIdx.x == 0) store_wt4(wt_rsrc(rw.scnt), 4u * (uint32_t)slice, run);
+    }
+    // Publish: the stores above are acknowledged, then the arrival is counted.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        sl.cut = __hip_atomic_fetch_add(&rw.ctr[kCtrDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
+                         (uint32_t)nact
+                     ? 1u
+                     : 0u;
+    __syncthreads();
+    if (!sl.cut) return;
+
+    // ---- the last slice workgroup of the row selects
+    finish_row<NT>(rw, lo, row, clear);  // every slice has read the histogram
+    const uint32_t need = (uint32_t)k - b0.above;
+    // The counts and the first W entries of every region in one round trip
+    // (W = kCandLds / nact: the regions' usual fill); entries of a region past
+    // W are loaded afterwards.
+    const __amdgpu_buffer_rsrc_t pos_r = wt_rsrc(rw.cpos), key_r = wt_rsrc(rw.ckey);
+    const uint32_t W = (uint32_t)(kCandLds / nact);
+    const uint32_t my_cnt = (int)threadIdx.x < nact ? load_dev4u(wt_rsrc(rw.scnt), 4u * threadIdx.x) : 0u;
+    uint32_t cp[kSelBatch], ck[kSelBatch];
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+        const uint32_t e = j * NT + threadIdx.x;
+        const uint32_t sidx = e / W, o = e - sidx * W;
+        const bool ok = sidx < (uint32_t)nact && o < (uint32_t)lo.pcap;
+        const uint32_t off = 4u * (sidx * (uint32_t)lo.pcap + o);
+        cp[j] = ok ? load_dev4u(pos_r, off) : 0u;
+        ck[j] = ok ? load_dev4u(key_r, off) : 0u;
+    }
+    if (threadIdx.x == 0) sl.nsel = 0u;  // bit 0: a region holds more than W entries; bit 1: one overflowed
+    uint32_t ncand;
+    const uint32_t my_base = excl_scan<NT>(my_cnt, sl.scratch, &ncand);
+    if ((int)threadIdx.x < nact) {
+        sl.sbase[threadIdx.x] = my_base;
+        sl.scnt[threadIdx.x] = my_cnt;
+        if (my_cnt > (uint32_t)lo.pcap) atomicOr(&sl.nsel, 2u);
+        else if (my_cnt > W) atomicOr(&sl.nsel, 1u);
+    }
+    for (int i = threadIdx.x; i < kBins; i += NT) sl.h[i] = 0u;
+    lds_sync();
+    const uint32_t beyond = sl.nsel;
+    if (ncand > (uint32_t)kCandLds) {
+        select_row<NT>(row_scores, n, k, rw, false, ncand, T, need, out, sl);
+        return;
+    }
+    // Candidates to LDS in position order (entry o of slice s's region is
+    // candidate sbase[s] + o), counting the middle digit of those in T's bin.
+    auto place = [&](uint32_t c, uint32_t pos, uint32_t key) {
+        sl.cand.pos[c] = pos;
+        sl.cand.key[c] = key;
+        if ((key >> 21) == T) atomicAdd(&sl.h[(key >> 10) & 0x7FFu], 1u);
+    };
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+        const uint32_t e = j * NT + threadIdx.x;
+        const uint32_t sidx = e / W, o = e - sidx * W;
+        if (sidx < (uint32_t)nact) {
+            const uint32_t cs = sl.scnt[sidx];
+            if (o < cs && cs <= (uint32_t)lo.pcap) place(sl.sbase[sidx] + o, cp[j], ck[j]);  // overflowed: below
+        }
+    }
+    for (int sidx = 0; (beyond & 1u) && sidx < nact; ++sidx) {
+        const uint32_t cs = sl.scnt[sidx];
+        if (cs <= W || cs > (uint32_t)lo.pcap) continue;
+        for (uint32_t o = W + threadIdx.x; o < cs; o += NT) {
+            const uint32_t off = 4u * ((uint32_t)sidx * (uint32_t)lo.pcap + o);
+            place(sl.sbase[sidx] + o, load_dev4u(pos_r, off), load_dev4u(key_r, off));
+        }
+    }
+    const bool overflowed = (beyond & 2u) != 0u;
+    for (int sidx = 0; overflowed && sidx < nact; ++sidx) {
+        if (sl.scnt[sidx] <= (uint32_t)lo.pcap) continue;
+        // this slice's region overflowed: its candidates again, from its scores
+        const int64_t s0 = (int64_t)sidx * lo.fslice, s1 = min(s0 + (int64_t)lo.fslice, n);
+        uint32_t run = sl.sbase[sidx];
+        for (int64_t i0 = s0; i0 < s1; i0 += (int64_t)kFPer * NT) {
+            load_batch(i0, s1);
+            bool f[kFPer];
+            uint32_t key[kFPer];
+#pragma unroll
+            for (int j = 0; j < kFPer; ++j) {
+                key[j] = score_key(v[j]);
+                f[j] = i0 + j * NT + (int)threadIdx.x < s1 && (key[j] >> 21) >= T;
+            }
+            const uint32_t c = ordered_slots<NT, kFPer>(f, sl.sel, sl.scratch, [&](uint32_t slot, int j) {
+                slot += run;  // below ncand: the same scores and T give the same count
+                if (slot < (uint32_t)kCandLds) {
+                    sl.cand.pos[slot] = (uint32_t)(i0 + j * NT + threadIdx.x);
+                    sl.cand.key[slot] = key[j];
+                    if ((key[j] >> 21) == T) atomicAdd(&sl.h[(key[j] >> 10) & 0x7FFu], 1u);
+                }
+            });
+            run += c;
+        }
+    }
+    lds_sync();
+    const HistPart<NT> hmid = load_hist<NT>(sl.h, kBins);
+    const BinPick b1 = pick_bin<NT>(hmid, kBins, need, sl.scratch, &sl.pick);
+    auto for_candidates = [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const uint32_t c = j * NT + threadIdx.x;
+            if (c < ncand) f(sl.cand.key[c], sl.cand.pos[c]);
+        }
+    };
+    const Cut cut = find_cut<NT>(sl, T, need, b1, for_candidates);
+    // the kept candidates, in position order, are the output
+    bool f[kSelBatch];
+    uint32_t kp[kSelBatch];
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+        const uint32_t c = j * NT + threadIdx.x;
+        const uint32_t key = c < ncand ? sl.cand.key[c] : 0u;
+        kp[j] = c < ncand ? sl.cand.pos[c] : 0u;
+        f[j] = c < ncand && (key > cut.kstar || (key == cut.kstar && kp[j] <= cut.pos_cut));
+    }
+    const __amdgpu_buffer_rsrc_t out_wt = wt_rsrc(out);
+    ordered_slots<NT, kSelBatch>(f, sl.sel, sl.scratch,
+                                 [&](uint32_t slot, int j) {
+                                     if (slot < (uint32_t)k) store_wt4(out_wt, 4u * slot, kp[j]);  // exactly k kept
+                                 });
+}
+
 
 Layout make_layout(int rows, int L) {
     const int max_slices = (L + kMinSlice - 1) / kMinSlice;
@@ -629,6 +958,17 @@ Layout make_layout(int rows, int L) {
     int64_t cap = (int64_t)L / 8;
     if (cap < 4096) cap = 4096;
     lo.cap = (int)((cap + 63) / 64 * 64);
+    // fused pass: about one slice workgroup per CU over all rows
+    int fns = (kFusedTarget + rows - 1) / rows;
+    const int fmax = (L + kFusedMinSlice - 1) / kFusedMinSlice;
+    if (fns > fmax) fns = fmax;
+    if (fns > kFusedMaxSlices) fns = kFusedMaxSlices;
+    if (fns < 1) fns = 1;
+    int64_t fslice = ((int64_t)L + fns - 1) / fns;
+    fslice = (fslice + kSelectThreads - 1) / kSelectThreads * kSelectThreads;
+    lo.fslice = (int)fslice;
+    lo.fnslice = (int)(((int64_t)L + fslice - 1) / fslice);
+    lo.pcap = lo.cap / lo.fnslice;
     return lo;
 }
 
@@ -659,8 +999,16 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     if (state != TopkState::kHistogram)
         hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
                            dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws,
-                       state == TopkState::kHistogram ? 1 : 0);
+    // The fused pass unless there are many rows (prefill) and no histogram
+    // from the indexer: there the separate filter's small workgroups stream
+    // the rows with more of them resident per CU.
+    if (state == TopkState::kHistogram || rows <= kFusedTarget) {
+        hipLaunchKernelGGL(topk_fused_kernel, dim3((unsigned)((int64_t)rows * lo.fnslice)), dim3(kSelectThreads), 0,
+                           stream, scores, q_pos, L, k, lo, ws, state == TopkState::kHistogram ? 1 : 0, idx,
+                           clear_after);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws, 0);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        idx, clear_after);
     return hipGetLastError();

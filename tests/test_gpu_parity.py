@@ -164,6 +164,26 @@ def test_topk_candidates_beyond_lds(dsa):
     _topk_case(dsa, s, pos, 2048)
 
 
+def test_topk_candidates_clustered_in_slices(dsa):
+    # Up to 256 rows are cut into slices of 16384 keys (8 per 128K row), each
+    # with a region of L/8/8 = 2048 candidates and a first read of 12288/8 = 1536
+    # per region by the selecting workgroup.  Candidates bunched in one slice:
+    # more than that first read (row 0), more than the region (row 1, its
+    # slice's scores are read again), spread over three slices (row 2), and
+    # a ragged row whose last active slice is short (row 3).
+    rng = np.random.default_rng(17)
+    B, T, L = 1, 4, 131072
+    say("topk candidates clustered in slices")
+    s = (rng.random((B, T, L)) * 0.5).astype(np.float32)
+    s[0, 0, 7 * 16384 + rng.choice(16384, 1800, replace=False)] = (4.0 + rng.random(1800)).astype(np.float32)
+    s[0, 1, 3 * 16384 + rng.choice(16384, 2500, replace=False)] = (4.0 + rng.random(2500)).astype(np.float32)
+    for sl in (1, 4, 6):
+        s[0, 2, sl * 16384 + rng.choice(16384, 600, replace=False)] = (4.0 + rng.random(600)).astype(np.float32)
+    s[0, 3, 100000 + rng.choice(3000, 1700, replace=False)] = (4.0 + rng.random(1700)).astype(np.float32)
+    pos = np.array([[L - 1, L - 1, L - 1, 103000]], np.int32)
+    _topk_case(dsa, s, pos, 1500)
+
+
 @pytest.mark.parametrize("L", [262144, 262145])
 def test_topk_long_rows(dsa, L):
     rng = np.random.default_rng(L)
