@@ -13,13 +13,18 @@
 // v_mfma_f32_16x16x32_bf16, two 16-head blocks sharing each 16-key B operand.
 //
 // Keys are read with plain 16-byte loads in which every instruction covers
-// four whole keys (1 KiB contiguous); a rolling window of five 16-key tiles
-// is in flight per wave.  Each tile is then turned into the MFMA operand
-// layout through a small wave-private LDS slot: lane l writes chunk l%16 of
-// key 4i + l/16, and reads back chunk 4kk + l/16 of key l%16.  Chunk s of key k
-// is stored at position 16k + (s ^ k), which makes both the writes and the
-// reads bank-conflict free.  Scores are kept in registers and stored after the
-// stream, so the loop contains only loads.
+// four whole keys (1 KiB contiguous), one 16-key tile per wave at a time: with
+// two workgroups of four waves per CU that is about 8 MiB in flight over the
+// chip, which streams at the chip's measured read rate (7.0 TB/s at 128K x 32;
+// one or three tiles ahead per wave measured 2% and 7% slower).  Each tile is
+// then turned into the MFMA operand layout through a small wave-private LDS
+// slot: lane l writes chunk l%16 of key 4i + l/16, and reads back chunk
+// 4kk + l/16 of key l%16.  Chunk s of key k is stored at position 16k + (s ^ k),
+// which makes both the writes and the reads bank-conflict free.  Scores wait
+// in LDS and are stored after the stream, so the loop contains only loads.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 
 namespace dsa {
@@ -30,10 +35,11 @@ constexpr int kD = 128;
 constexpr int kTile = 16;                      // keys per MFMA tile
 constexpr int kTileBytes = kTile * kD * 2;     // 4 KiB
 constexpr int kLoads = kTileBytes / (kWave * 16);  // 4 loads of 1 KiB per tile
-// Measured best on MI355X for 128K and 1M rows: 4 waves x 16 tiles, 4 tiles ahead.
-constexpr int kAhead = 4;                      // tiles loaded ahead of the one computed
+// 4 waves x 16 tiles of 16 keys per block (1024 keys), no tile loaded ahead.
+constexpr int kAhead = 0;                      // tiles loaded ahead of the one computed
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeTiles = 16;               // tiles per wave
+constexpr int kDecodeTiles = 16;               // tiles per wave and block
+constexpr int kDecodeMaxPer = 8;               // blocks per workgroup (their scores wait in LDS)
 
 // Top-k preparation (TopkPrep) by a decode launch: the first key block of each
 // row clears the row's counters; with `hist`, every block counts the top 11-bit
@@ -58,24 +64,54 @@ __device__ __forceinline__ void prep_flush(const TopkPrep& prep, int row, const 
     }
 }
 
-template <int kWaves, int kTilesPerWave>
+// A workgroup's range of scores, waiting in LDS (sst[0, nkeys)), to the row
+// at keys key0 .. key0 + nkeys - 1: 16-byte stores when rows start 16-byte aligned.
+__device__ __forceinline__ void store_scores(float* row_out, const float* sst, int64_t key0, int nkeys, int L,
+                                             int nthreads) {
+    const __amdgpu_buffer_rsrc_t out = wt_rsrc(row_out);
+    const bool vec = (L & 3) == 0;
+    for (int i = 4 * (int)threadIdx.x; i < nkeys; i += 4 * nthreads) {
+        if (vec && i + 4 <= nkeys) {
+            store_wt16(out, 4u * (uint32_t)(key0 + i), *reinterpret_cast<const u32x4_t*>(&sst[i]));
+        } else {
+            for (int e = i; e < nkeys && e < i + 4; ++e) store_wt4(out, 4u * (uint32_t)(key0 + e), sst[e]);
+        }
+    }
+}
+
+// Workgroups run through `per` (at most kDecodeMaxPer) consecutive key blocks
+// of one row (about two resident workgroups per CU over all rows), so the
+// query and its weights are loaded once, the histogram is flushed once, and
+// the rolling window of tiles runs on across block boundaries instead of each
+// block starting cold (a workgroup per block left about an eighth of the
+// chip's slots idle between one workgroup's end and the next one's first
+// load).  The scores wait in LDS and are stored once the range is done: a
+// store in flight among the loads would make the compiler wait for every
+// outstanding load at the next use (it cannot order loads after stores).
+template <int kWaves, int kAheadT>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
-    TopkPrep prep) {
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, int wpr, int per,
+    float* __restrict__ scores, TopkPrep prep) {
+    constexpr int kTilesPerWave = kDecodeTiles;
     constexpr int kKeysPerBlock = kWaves * kTile * kTilesPerWave;
+    constexpr int kBufs = kAheadT + 1;
     static_assert(kTilesPerWave % 4 == 0, "the four lane groups take whole tiles each");
+    static_assert(kTilesPerWave % kBufs == 0, "tile j of every block sits in buffer j % kBufs");
     __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * 2 * kTileBytes / 2];
     __shared__ uint32_t hist_lds[kTopBins];
-    const int row = blockIdx.x / nblk;  // b*T + t
-    const int blk = blockIdx.x % nblk;
+    __shared__ __attribute__((aligned(16))) float sst[kDecodeMaxPer * kKeysPerBlock];  // scores of the range
+    const int row = blockIdx.x / wpr;  // b*T + t
+    const int blk0 = (blockIdx.x % wpr) * per;
+    const int blk1 = min(blk0 + per, nblk);
+    if (blk0 >= blk1) return;
     const int b = row / T;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int c = lane & 15;  // key within tile (B/C column)
     const int g = lane >> 4;  // lane group: 8-dim slice of each 32-dim step; head row block in C
     const int64_t p = q_pos[row];
-    prep_start(prep, row, blk, hist_lds, kWaves * kWave);
+    prep_start(prep, row, blk0, hist_lds, kWaves * kWave);
 
     // A operands: q rows (heads) 16*ht + c, dims 32*kk + 8*g .. +7.
     bf16x8_t qa[2][4];
@@ -93,64 +129,78 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
         for (int r = 0; r < 4; ++r) wv[ht][r] = w[(int64_t)row * kH + 16 * ht + 4 * g + r];
 
     const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
-    // Tile j of this wave covers keys tile_key0(j) .. +15; at each step the block's
-    // waves read kWaves*16 consecutive keys.
-    const int64_t block_start = (int64_t)blk * kKeysPerBlock;
-    auto tile_key0 = [&](int j) { return block_start + (int64_t)(kWaves * j + wave) * kTile; };
+    // Tile j of block blk for this wave covers keys blk*kKeysPerBlock + (kWaves*j + wave)*16 .. +15;
+    // at each step the block's waves read kWaves*16 consecutive keys.
+    auto tile_key0 = [&](int blk, int j) {
+        return (int64_t)blk * kKeysPerBlock + (int64_t)(kWaves * j + wave) * kTile;
+    };
     uint16_t* my_stage = stage + wave * kTileBytes;  // two 4 KiB slots per wave
 
-    u32x4_t buf[kAhead + 1][kLoads];
-    auto load_tile = [&](int j, u32x4_t (&dst)[kLoads]) {
+    u32x4_t buf[kBufs][kLoads];
+    auto load_tile = [&](int blk, int j, u32x4_t (&dst)[kLoads]) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            int64_t key = tile_key0(j) + 4 * i + (lane >> 4);
-            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
+            int64_t key = tile_key0(blk, j) + 4 * i + (lane >> 4);
+            key = key < L ? key : (int64_t)L - 1;  // past the row (or the last block's look-ahead): a valid row, never used
             dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + key * kD + 8 * (lane & 15)));
         }
     };
+    // In tile order (no reordering by the scheduler): the loop's first wait,
+    // for tile 0, then counts only the loads issued after it, on entry as on
+    // every later block.
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) load_tile(j, buf[j]);
-
-    float sc[kTilesPerWave];
-#pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-        if (j + kAhead < kTilesPerWave) load_tile(j + kAhead, buf[(j + kAhead) % (kAhead + 1)]);
-        // registers -> LDS (swizzled) -> MFMA operand layout
-        uint16_t* slot = my_stage + (j & 1) * (kTileBytes / 2);
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int k = 4 * i + (lane >> 4);
-            *reinterpret_cast<u32x4_t*>(slot + 8 * (16 * k + ((lane & 15) ^ k))) = buf[j % (kAhead + 1)][i];
-        }
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(slot + 8 * (16 * c + ((4 * kk + g) ^ c)));
-            a0 = mfma16x16x32(qa[0][kk], kv, a0);
-            a1 = mfma16x16x32(qa[1][kk], kv, a1);
-        }
-        float part = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            part = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, part);
-            part = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, part);
-        }
-        part += __shfl_xor(part, 16, kWave);
-        part += __shfl_xor(part, 32, kWave);
-        sc[j] = part;
-        if (prep.hist && g == (j & 3)) {  // lane group g counts the tiles j = g (mod 4)
-            const int64_t key = tile_key0(j) + c;
-            if (key < L && key <= p) atomicAdd(&hist_lds[score_key(part) >> 21], 1u);
-        }
+    for (int j = 0; j < kAheadT; ++j) {
+        load_tile(blk0, j, buf[j]);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    const __amdgpu_buffer_rsrc_t out = wt_rsrc(scores + (int64_t)row * L);
-    if (g == 0) {
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        float sc[kTilesPerWave];
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
-            const int64_t key = tile_key0(j) + c;
-            if (key < L) store_wt4(out, 4u * (uint32_t)key, key <= p ? sc[j] : -INFINITY);
+            // the window runs on into the next block (loaded every time, so the wait counts stay fixed)
+            if (j + kAheadT < kTilesPerWave) load_tile(blk, j + kAheadT, buf[(j + kAheadT) % kBufs]);
+            else load_tile(blk + 1, j + kAheadT - kTilesPerWave, buf[(j + kAheadT) % kBufs]);
+            // registers -> LDS (swizzled) -> MFMA operand layout
+            uint16_t* slot = my_stage + (j & 1) * (kTileBytes / 2);
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int k = 4 * i + (lane >> 4);
+                *reinterpret_cast<u32x4_t*>(slot + 8 * (16 * k + ((lane & 15) ^ k))) = buf[j % kBufs][i];
+            }
+            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(slot + 8 * (16 * c + ((4 * kk + g) ^ c)));
+                a0 = mfma16x16x32(qa[0][kk], kv, a0);
+                a1 = mfma16x16x32(qa[1][kk], kv, a1);
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                part = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, part);
+                part = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, part);
+            }
+            part += __shfl_xor(part, 16, kWave);
+            part += __shfl_xor(part, 32, kWave);
+            sc[j] = part;
+            if (prep.hist && g == (j & 3)) {  // lane group g counts the tiles j = g (mod 4)
+                const int64_t key = tile_key0(blk, j) + c;
+                if (key < L && key <= p) atomicAdd(&hist_lds[score_key(part) >> 21], 1u);
+            }
+        }
+        if (g == 0) {  // lane group 0 keeps the scores (the others hold the same sums)
+#pragma unroll
+            for (int j = 0; j < kTilesPerWave; ++j) {
+                const int64_t key = tile_key0(blk, j) + c;
+                sst[(blk - blk0) * kKeysPerBlock + (kWaves * j + wave) * kTile + c] = key <= p ? sc[j] : -INFINITY;
+            }
         }
     }
+    __syncthreads();  // every wave's scores (and histogram counts) are in LDS
+    store_scores(scores + (int64_t)row * L, sst, (int64_t)blk0 * kKeysPerBlock,
+                 (int)min((int64_t)(blk1 - blk0) * kKeysPerBlock, (int64_t)L - (int64_t)blk0 * kKeysPerBlock), L,
+                 kWaves * kWave);
     if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
 }
 
@@ -174,33 +224,43 @@ constexpr int kD8 = 128;                        // bytes per key
 constexpr int kTile8Bytes = kTile8 * kD8;       // 4 KiB
 constexpr int kLoads8 = kTile8Bytes / (kWave * 16);  // 4 loads of 1 KiB per tile
 
-// Measured best on MI355X for 128K x 32 and 1M x 4: 4 waves x 16 tiles of 32 keys, 6 tiles ahead.
+// 4 waves x 16 tiles of 32 keys per block (2048 keys), one tile loaded ahead
+// (measured at 128K x 32 and 1M x 4: 81.7 us against 82.9 with none, 86.8 with three).
 constexpr int kDecode8Waves = 4;
 constexpr int kDecode8Tiles = 16;
-constexpr int kDecode8Ahead = 6;
+constexpr int kDecode8Ahead = 1;
+constexpr int kDecode8MaxPer = 4;  // blocks per workgroup (their scores wait in LDS)
 
 __device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
-template <int kWaves, int kTilesPerWave, int kAhead8>
+// Like the bf16 scan, each workgroup runs through `per` (at most
+// kDecode8MaxPer) consecutive blocks of one row, the scores waiting in LDS.
+template <int kWaves, int kAhead8>
 __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
-    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, float* __restrict__ scores,
-    TopkPrep prep) {
+    int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nblk, int wpr, int per,
+    float* __restrict__ scores, TopkPrep prep) {
+    constexpr int kTilesPerWave = kDecode8Tiles;
     constexpr int kKeysPerBlock = kWaves * kTile8 * kTilesPerWave;
+    constexpr int kBufs = kAhead8 + 1;
     static_assert(kTilesPerWave % 2 == 0, "lane groups 2, 3 take the odd tiles");
+    static_assert(kTilesPerWave % kBufs == 0, "tile j of every block sits in buffer j % kBufs");
     __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * kTile8Bytes];
     __shared__ uint32_t hist_lds[kTopBins];
-    const int row = blockIdx.x / nblk;  // b*T + t
-    const int blk = blockIdx.x % nblk;
+    __shared__ __attribute__((aligned(16))) float sst[kDecode8MaxPer * kKeysPerBlock];  // scores of the range
+    const int row = blockIdx.x / wpr;  // b*T + t
+    const int blk0 = (blockIdx.x % wpr) * per;
+    const int blk1 = min(blk0 + per, nblk);
+    if (blk0 >= blk1) return;
     const int b = row / T;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane & 15;
     const int g = lane >> 4;
     const int64_t p = q_pos[row];
-    prep_start(prep, row, blk, hist_lds, kWaves * kWave);
+    prep_start(prep, row, blk0, hist_lds, kWaves * kWave);
 
     // A operands: head 16*ht + c, dims 32*kk + 8*g .. +7 (8 codes).
     long qa[2][4];
@@ -217,70 +277,81 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
         for (int r = 0; r < 4; ++r) wv[ht][r] = w[(int64_t)row * kH + 16 * ht + 4 * g + r];
 
     const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
-    const int64_t block_start = (int64_t)blk * kKeysPerBlock;
-    auto tile_key0 = [&](int j) { return block_start + (int64_t)(kWaves * j + wave) * kTile8; };
+    auto tile_key0 = [&](int blk, int j) {
+        return (int64_t)blk * kKeysPerBlock + (int64_t)(kWaves * j + wave) * kTile8;
+    };
     uint8_t* my_stage = stage + wave * 2 * kTile8Bytes;
 
-    u32x4_t buf[kAhead8 + 1][kLoads8];
-    auto load_tile = [&](int j, u32x4_t (&dst)[kLoads8]) {
+    u32x4_t buf[kBufs][kLoads8];
+    auto load_tile = [&](int blk, int j, u32x4_t (&dst)[kLoads8]) {
 #pragma unroll
         for (int i = 0; i < kLoads8; ++i) {
-            int64_t key = tile_key0(j) + 8 * i + (lane >> 3);
-            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
+            int64_t key = tile_key0(blk, j) + 8 * i + (lane >> 3);
+            key = key < L ? key : (int64_t)L - 1;  // past the row (or the last block's look-ahead): a valid row, never used
             dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + key * kD8 + 16 * (lane & 7)));
         }
     };
 #pragma unroll
-    for (int j = 0; j < kAhead8; ++j) load_tile(j, buf[j]);
-
-    float sc[kTilesPerWave];
-#pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-        if (j + kAhead8 < kTilesPerWave) load_tile(j + kAhead8, buf[(j + kAhead8) % (kAhead8 + 1)]);
-        uint8_t* slot = my_stage + (j & 1) * kTile8Bytes;
-#pragma unroll
-        for (int i = 0; i < kLoads8; ++i) {
-            const int k = 8 * i + (lane >> 3);
-            *reinterpret_cast<u32x4_t*>(slot + 16 * (8 * k + ((lane & 7) ^ ((k >> 1) & 7)))) =
-                buf[j % (kAhead8 + 1)][i];
-        }
-        float part[2];
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
-            const int k = 16 * kbk + c;
-            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s = 2 * kk + (g >> 1);
-                const long kv = *reinterpret_cast<const long*>(slot + 16 * (8 * k + (s ^ ((k >> 1) & 7))) + 8 * (g & 1));
-                a0 = mfma16x16x32_fp8(qa[0][kk], kv, a0);
-                a1 = mfma16x16x32_fp8(qa[1][kk], kv, a1);
-            }
-            float v = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
-                v = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
-            }
-            v += __shfl_xor(v, 16, kWave);
-            v += __shfl_xor(v, 32, kWave);
-            part[kbk] = v;
-        }
-        // every lane of column c now holds both sums; lane group g keeps key 16*(g & 1) + c
-        sc[j] = (g & 1) ? part[1] : part[0];
-        if (prep.hist && (g >> 1) == (j & 1)) {  // groups 0, 1 count the even tiles, groups 2, 3 the odd ones
-            const int64_t key = tile_key0(j) + 16 * (g & 1) + c;
-            if (key < L && key <= p) atomicAdd(&hist_lds[score_key(sc[j]) >> 21], 1u);
-        }
+    for (int j = 0; j < kAhead8; ++j) {  // in tile order (see the bf16 scan)
+        load_tile(blk0, j, buf[j]);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    const __amdgpu_buffer_rsrc_t out = wt_rsrc(scores + (int64_t)row * L);
-    if (g < 2) {
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        float sc[kTilesPerWave];
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
-            const int64_t key = tile_key0(j) + 16 * g + c;
-            if (key < L) store_wt4(out, 4u * (uint32_t)key, key <= p ? sc[j] : -INFINITY);
+            if (j + kAhead8 < kTilesPerWave) load_tile(blk, j + kAhead8, buf[(j + kAhead8) % kBufs]);
+            else load_tile(blk + 1, j + kAhead8 - kTilesPerWave, buf[(j + kAhead8) % kBufs]);
+            uint8_t* slot = my_stage + (j & 1) * kTile8Bytes;
+#pragma unroll
+            for (int i = 0; i < kLoads8; ++i) {
+                const int k = 8 * i + (lane >> 3);
+                *reinterpret_cast<u32x4_t*>(slot + 16 * (8 * k + ((lane & 7) ^ ((k >> 1) & 7)))) = buf[j % kBufs][i];
+            }
+            float part[2];
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk) {
+                const int k = 16 * kbk + c;
+                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int s = 2 * kk + (g >> 1);
+                    const long kv =
+                        *reinterpret_cast<const long*>(slot + 16 * (8 * k + (s ^ ((k >> 1) & 7))) + 8 * (g & 1));
+                    a0 = mfma16x16x32_fp8(qa[0][kk], kv, a0);
+                    a1 = mfma16x16x32_fp8(qa[1][kk], kv, a1);
+                }
+                float v = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
+                    v = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                }
+                v += __shfl_xor(v, 16, kWave);
+                v += __shfl_xor(v, 32, kWave);
+                part[kbk] = v;
+            }
+            // every lane of column c now holds both sums; lane group g keeps key 16*(g & 1) + c
+            sc[j] = (g & 1) ? part[1] : part[0];
+            if (prep.hist && (g >> 1) == (j & 1)) {  // groups 0, 1 count the even tiles, groups 2, 3 the odd ones
+                const int64_t key = tile_key0(blk, j) + 16 * (g & 1) + c;
+                if (key < L && key <= p) atomicAdd(&hist_lds[score_key(sc[j]) >> 21], 1u);
+            }
+        }
+        if (g < 2) {  // lane groups 0 and 1 keep the tile's two 16-key halves
+#pragma unroll
+            for (int j = 0; j < kTilesPerWave; ++j) {
+                const int64_t key = tile_key0(blk, j) + 16 * g + c;
+                sst[(blk - blk0) * kKeysPerBlock + (kWaves * j + wave) * kTile8 + 16 * g + c] =
+                    key <= p ? sc[j] : -INFINITY;
+            }
         }
     }
+    __syncthreads();  // every wave's scores (and histogram counts) are in LDS
+    store_scores(scores + (int64_t)row * L, sst, (int64_t)blk0 * kKeysPerBlock,
+                 (int)min((int64_t)(blk1 - blk0) * kKeysPerBlock, (int64_t)L - (int64_t)blk0 * kKeysPerBlock), L,
+                 kWaves * kWave);
     if (prep.hist) prep_flush(prep, row, hist_lds, kWaves * kWave);
 }
 
@@ -554,27 +625,74 @@ int64_t indexer_grid_blocks(int B, int T, int L, bool fp8) {
     return (int64_t)B * T * ((L + keys_per_block - 1) / keys_per_block);
 }
 
-template <int W, int N>
-hipError_t launch_indexer_cfg(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
-                              const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                              TopkPrep prep) {
-    constexpr int keys_per_block = W * kTile * N;
+// Resident workgroups per CU of a kernel at this block size (looked up once per device and kernel).
+template <typename K>
+int resident_per_cu(K kernel, int threads, std::atomic<int>* cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Workgroups per row and blocks per workgroup: all of the rows' workgroups
+// resident at once when there are few rows (at most max_per blocks each), one
+// block each when there are many.
+struct DecodeGrid {
+    int wpr, per;
+};
+DecodeGrid decode_grid(int rows, int nblk, int64_t slots, int max_per) {
+    int wpr = nblk;
+    if (slots > 0 && 2 * (int64_t)rows <= slots) wpr = (int)std::min<int64_t>(nblk, slots / rows);
+    wpr = std::max(wpr, (nblk + max_per - 1) / max_per);
+    const int per = (nblk + wpr - 1) / wpr;
+    return DecodeGrid{(nblk + per - 1) / per, per};
+}
+
+hipError_t launch_indexer_decode(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
+                                 const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                                 TopkPrep prep) {
+    constexpr int W = kDecodeWaves;
+    constexpr int keys_per_block = W * kTile * kDecodeTiles;
+    static std::atomic<int> occ[64];
+    const auto kernel = indexer_decode_kernel<W, kAhead>;
+    const int rows = B * T;
     const int nblk = (L + keys_per_block - 1) / keys_per_block;
-    dim3 grid((unsigned)((int64_t)nblk * B * T));
-    hipLaunchKernelGGL((indexer_decode_kernel<W, N>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx, k_bstride,
-                       q_pos, T, L, nblk, scores, prep);
+    const int64_t slots = (int64_t)resident_per_cu(kernel, W * kWave, occ) * device_cu_count();
+    const DecodeGrid dg = decode_grid(rows, nblk, slots, kDecodeMaxPer);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)((int64_t)rows * dg.wpr)), dim3(W * kWave), 0, stream, q_idx, w, k_idx,
+                       k_bstride, q_pos, T, L, nblk, dg.wpr, dg.per, scores, prep);
     return hipGetLastError();
 }
 
-template <int W, int N, int A>
-hipError_t launch_indexer_fp8_cfg(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                                  const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
-                                  TopkPrep prep) {
-    constexpr int keys_per_block = W * kTile8 * N;
+hipError_t launch_indexer_decode_fp8(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                                     const int32_t* q_pos, int B, int T, int L, float* scores, hipStream_t stream,
+                                     TopkPrep prep) {
+    constexpr int W = kDecode8Waves;
+    constexpr int keys_per_block = W * kTile8 * kDecode8Tiles;
+    static std::atomic<int> occ[64];
+    const auto kernel = indexer_decode_fp8_kernel<W, kDecode8Ahead>;
+    const int rows = B * T;
     const int nblk = (L + keys_per_block - 1) / keys_per_block;
-    dim3 grid((unsigned)((int64_t)nblk * B * T));
-    hipLaunchKernelGGL((indexer_decode_fp8_kernel<W, N, A>), grid, dim3(W * kWave), 0, stream, q_idx, w, k_idx,
-                       k_bstride, q_pos, T, L, nblk, scores, prep);
+    const int64_t slots = (int64_t)resident_per_cu(kernel, W * kWave, occ) * device_cu_count();
+    const DecodeGrid dg = decode_grid(rows, nblk, slots, kDecode8MaxPer);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)((int64_t)rows * dg.wpr)), dim3(W * kWave), 0, stream, q_idx, w, k_idx,
+                       k_bstride, q_pos, T, L, nblk, dg.wpr, dg.per, scores, prep);
     return hipGetLastError();
 }
 
@@ -588,8 +706,7 @@ hipError_t launch_indexer_fp8(const uint8_t* q_idx, const float* w, const uint8_
                            q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, prep);
         return hipGetLastError();
     }
-    return launch_indexer_fp8_cfg<kDecode8Waves, kDecode8Tiles, kDecode8Ahead>(q_idx, w, k_idx, k_bstride, q_pos, B,
-                                                                               T, L, scores, stream, prep);
+    return launch_indexer_decode_fp8(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, stream, prep);
 }
 
 hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
@@ -602,8 +719,7 @@ hipError_t launch_indexer(const uint16_t* q_idx, const float* w, const uint16_t*
                            q_idx, w, k_idx, k_bstride, q_pos, T, L, nqg, nkb, scores, prep);
         return hipGetLastError();
     }
-    return launch_indexer_cfg<kDecodeWaves, kDecodeTiles>(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, stream,
-                                                          prep);
+    return launch_indexer_decode(q_idx, w, k_idx, k_bstride, q_pos, B, T, L, scores, stream, prep);
 }
 
 }  // namespace dsa
