@@ -565,9 +565,8 @@ __device__ __forceinline__ void wait_gathers(int tiles_left, int nload) {
 // dims per lane: lane s holds split s's log2-sum-exp, the maximum and the
 // denominator come from wave reductions, the weights reach the accumulation
 // through readlane, and the loads of all NB >= nsplit partials go out first
-// (NB = 8 when there are at most 8 splits, else 16).  The partials are read
-// with device-scope loads: in the merging launch other workgroups wrote them.
-constexpr int kMergeNB = 8;
+// (NB = 8 when there are at most 8 splits, else 16).
+constexpr int kCombineNB = 8;
 static_assert(kWave * 8 == kDv, "8 value dims per lane");
 
 template <int NB>
@@ -582,9 +581,12 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
         const int sp = min(u, nsplit - 1);  // past the end: a valid split, weight 0 below
-        v[u] = load_dev16(po, 2u * (uint32_t)(sp * kHq * kDv + 8 * lane));
+        v[u] = __builtin_bit_cast(u32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(po, (int)(2u * (uint32_t)(sp * kHq * kDv + 8 * lane)), 0, 0));
     }
-    const float ls = lane < nsplit ? load_dev4(pl, 4u * (uint32_t)(lane * kHq)) : -INFINITY;
+    const float ls =
+        lane < nsplit ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pl, (int)(4u * (uint32_t)(lane * kHq)), 0, 0))
+                      : -INFINITY;
     float M = ls;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
@@ -611,81 +613,6 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
     if (lse && lane == 0)
         store_wt4(wt_rsrc(lse + (int64_t)bt * kHq), 4u * head,
                   den > 0.0f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY);
-}
-
-// Merging inside the split launch.  Split s of a query merges head group s
-// (heads s*hpg .. s*hpg + hpg - 1, hpg = ceil(64 / nsplit), one wave per head)
-// once every split of the query has written its partial, so the separate
-// combine launch and its start-up go away.  Per query, three counters in the
-// workspace: arrivals, the head groups claimed, the workgroups finished.
-//   - Each workgroup writes its partial through to memory (device-scope
-//     stores), waits until they are acknowledged, then counts its arrival.
-//   - It waits (bounded) until all nsplit have arrived, claims its own head
-//     group and merges it.  The launch holds at most one workgroup per CU and
-//     the host only takes this path when rows * nsplit fits on the chip, so
-//     the wait ends within the spread of the splits' finishing times.
-//   - The last to arrive also claims and merges every head group still
-//     unclaimed (none, unless a wait ran out), so each group is merged exactly
-//     once whatever the residency.
-//   - The last to finish clears the three counters for the next launch; the
-//     selection that precedes a group's first attention launch clears them too.
-constexpr int kSyncWords = 32;         // per query, 128 bytes apart
-constexpr int kSpinLimit = 1 << 16;    // about 2 ms of polling before a wait gives up
-
-__device__ __forceinline__ void merge_group(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse,
-                                            int bt, int group, int nsplit, int wave, int lane) {
-    const int hpg = (kHq + nsplit - 1) / nsplit;
-    const int h_end = min(kHq, (group + 1) * hpg);
-    for (int h = group * hpg + wave; h < h_end; h += 2 * kWaves) {
-        if (nsplit <= kMergeNB) combine_head<kMergeNB>(part_o, part_lse, bt, h, nsplit, out, lse, lane);
-        else combine_head<kMaxQuerySplits>(part_o, part_lse, bt, h, nsplit, out, lse, lane);
-    }
-}
-
-__device__ __forceinline__ void merge_splits(const uint16_t* part_o, const float* part_lse, uint16_t* out, float* lse,
-                                          uint32_t* ctr, int bt, int split, int nsplit, int wave, int lane,
-                                          uint32_t* bcast) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's written-through stores are acknowledged
-    __syncthreads();
-    const uint32_t bit = 1u << split;
-    const uint32_t all = nsplit >= 32 ? 0xFFFFFFFFu : (1u << nsplit) - 1u;
-    if (threadIdx.x == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = before + 1 == (uint32_t)nsplit;
-        bool ready = last;
-        for (int it = 0; !ready && it < kSpinLimit; ++it) {
-            __builtin_amdgcn_s_sleep(1);
-            ready = __hip_atomic_load(&ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)nsplit;
-        }
-        uint32_t mine = 0;
-        if (ready) mine = (__hip_atomic_fetch_or(&ctr[1], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bit) ? 0u : 1u;
-        bcast[0] = mine;
-        bcast[1] = last ? 1u : 0u;
-    }
-    __syncthreads();
-    const bool mine = bcast[0] != 0, last = bcast[1] != 0;
-    if (mine) merge_group(part_o, part_lse, out, lse, bt, split, nsplit, wave, lane);
-    if (last) {
-        __syncthreads();  // every thread has read bcast
-        if (threadIdx.x == 0)
-            bcast[0] = ~__hip_atomic_fetch_or(&ctr[1], all, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & all;
-        __syncthreads();
-        uint32_t rest = bcast[0];
-        while (rest) {
-            const int gidx = __builtin_ctz(rest);
-            rest &= rest - 1u;
-            merge_group(part_o, part_lse, out, lse, bt, gidx, nsplit, wave, lane);
-        }
-    }
-    __syncthreads();  // this workgroup is done with the counters
-    if (threadIdx.x == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done + 1 == (uint32_t)nsplit) {
-            __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctr[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 // ------------------------------------------------------------------ the attention kernel: two roles per SIMD
@@ -716,8 +643,7 @@ template <bool DIRECT, bool FP8, int STAGES>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_any, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint32_t* __restrict__ sync) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int grp = blockIdx.x / (kXcds * nsplit);
     const int rem = blockIdx.x % (kXcds * nsplit);
     const int split = rem / kXcds;
@@ -932,16 +858,13 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         const int h = 8 * wave + i;
         store_wt16(dst, 2u * (h * kDv + 8 * lane), *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane));
     }
-    if constexpr (!DIRECT) {
-        // the statistics area is free: every wave passed the staging barrier after reading it
-        if (sync) merge_splits(part_o, part_lse, out, lse, sync + (int64_t)bt * kSyncWords, bt, split, nsplit, wave,
-                               lane, reinterpret_cast<uint32_t*>(sx));
-    }
 }
 
-// The split partials merged in a launch of their own (when the splits of every
-// query cannot all be resident at once): one wave per (query, head), blocks
-// numbered like the split kernel.
+// The split partials merged in a launch of their own: one wave per (query,
+// head), blocks numbered like the split kernel.  (Merging inside the split
+// launch instead, each split merging a group of heads once all splits of its
+// query had written their partials, measured 0.5 us per layer slower at
+// decode 128K x 32.)
 constexpr int kCombineThreads = kWave;
 
 template <int NB>
@@ -985,39 +908,10 @@ SplitPlan plan_splits(int rows, int k, int ns) {
 // The partials' layout: enough splits for about kTargetBlocks workgroups.
 SplitPlan plan(int rows, int k) { return plan_splits(rows, k, (kTargetBlocks + rows - 1) / rows); }
 
-// A plan whose splits merge inside the split launch: every split of every query
-// resident at once (one workgroup per CU), no more splits than the partials'
-// layout holds, and at most kMergeNB, so that each split's head group keeps
-// all eight waves busy (measured: at decode 128K, B = 32, 8 splits, a layer
-// takes 0.8 us less than with the combine launch; at 1M, B = 4, 16 splits of 4
-// heads each, 1.2 us more).  nsplit == 0 when there is none.
-SplitPlan plan_merged(int rows, int k, int cus) {
-    const SplitPlan p = plan(rows, k);
-    const int ns = min(p.nsplit, cus / rows);
-    if (p.nsplit < 2 || p.nsplit > kMergeNB || ns < 2) return SplitPlan{0, 0};
-    const SplitPlan m = plan_splits(rows, k, ns);
-    if (m.nsplit < 2 || m.nsplit > p.nsplit || (int64_t)rows * m.nsplit > cus) return SplitPlan{0, 0};
-    return m;
-}
-
-// Compute units of the current device (looked up once per device).
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
-// Workspace: [partials bf16][log2-sum-exps fp32][per-query merge counters], 256-byte aligned parts.
+// Workspace: [partials bf16][log2-sum-exps fp32], 256-byte aligned parts.
 struct AttnWs {
     uint16_t* part_o;
     float* part_lse;
-    uint32_t* sync;
 };
 
 size_t part_o_bytes(int rows, int k) {
@@ -1029,37 +923,31 @@ size_t part_lse_bytes(int rows, int k) {
 
 AttnWs attn_ws(void* ws, int rows, int k) {
     char* b = reinterpret_cast<char*>(ws);
-    return AttnWs{reinterpret_cast<uint16_t*>(b), reinterpret_cast<float*>(b + part_o_bytes(rows, k)),
-                  reinterpret_cast<uint32_t*>(b + part_o_bytes(rows, k) + part_lse_bytes(rows, k))};
+    return AttnWs{reinterpret_cast<uint16_t*>(b), reinterpret_cast<float*>(b + part_o_bytes(rows, k))};
 }
 
 template <bool FP8, typename KV>
 hipError_t launch_attn_impl(const uint16_t* q, const KV* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
-                            int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, bool merge,
-                            hipStream_t stream) {
+                            int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
     const int rows = B * T;
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     const SplitPlan p = plan(rows, k);
     if (p.nsplit == 1) {
         hipLaunchKernelGGL((sparse_mla_kernel<true, FP8, FP8 ? kStages8 : kDirectStages>), dim3(xcd_grid(rows, 1)),
                            dim3(2 * kThreads), 0, stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1,
-                           scale_log2, nullptr, nullptr, out, lse, nullptr);
+                           scale_log2, nullptr, nullptr, out, lse);
         return hipGetLastError();
     }
     const AttnWs w = attn_ws(ws, rows, k);
-    const SplitPlan m = merge ? plan_merged(rows, k, device_cus()) : SplitPlan{0, 0};
-    const SplitPlan& use = m.nsplit ? m : p;
     decltype(&sparse_mla_kernel<false, FP8, 3>) split_kernel;
     if constexpr (FP8) split_kernel = sparse_mla_kernel<false, true, kStages8>;
-    else split_kernel = use.rows_per_split <= kFewTiles * kRows ? sparse_mla_kernel<false, false, 3>
-                                                                : sparse_mla_kernel<false, false, 4>;
-    hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, use.nsplit)), dim3(2 * kThreads), 0, stream, q, kv,
-                       kv_bstride, idx, rows, T, L, k, use.rows_per_split, use.nsplit, scale_log2, w.part_o,
-                       w.part_lse, out, lse, m.nsplit ? w.sync : nullptr);
-    if (!m.nsplit)
-        hipLaunchKernelGGL(use.nsplit <= kMergeNB ? attn_combine_kernel<kMergeNB> : attn_combine_kernel<kMaxQuerySplits>,
-                           dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, w.part_o, w.part_lse, rows,
-                           use.nsplit, out, lse);
+    else split_kernel = p.rows_per_split <= kFewTiles * kRows ? sparse_mla_kernel<false, false, 3>
+                                                              : sparse_mla_kernel<false, false, 4>;
+    hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q, kv, kv_bstride,
+                       idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, w.part_o, w.part_lse, out, lse);
+    hipLaunchKernelGGL(p.nsplit <= kCombineNB ? attn_combine_kernel<kCombineNB> : attn_combine_kernel<kMaxQuerySplits>,
+                       dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, w.part_o, w.part_lse, rows,
+                       p.nsplit, out, lse);
     return hipGetLastError();
 }
 
@@ -1069,27 +957,18 @@ int attn_num_splits(int rows, int k) { return plan(rows, k).nsplit; }
 
 size_t attn_ws_bytes(int rows, int k) {
     if (plan(rows, k).nsplit == 1) return 0;
-    return part_o_bytes(rows, k) + part_lse_bytes(rows, k) + align_up((size_t)rows * kSyncWords * 4, 256);
-}
-
-AttnSync attn_sync(void* ws, int rows, int k) {
-    AttnSync z;
-    if (plan(rows, k).nsplit == 1) return z;
-    z.base = attn_ws(ws, rows, k).sync;
-    z.words = kSyncWords;
-    return z;
+    return part_o_bytes(rows, k) + part_lse_bytes(rows, k);
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
-                       int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream,
-                       bool merge) {
-    return launch_attn_impl<false>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, merge, stream);
+                       int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+    return launch_attn_impl<false>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, stream);
 }
 
 hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                            int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                           hipStream_t stream, bool merge) {
-    return launch_attn_impl<true>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, merge, stream);
+                           hipStream_t stream) {
+    return launch_attn_impl<true>(q, kv, kv_bstride, idx, B, T, L, k, sm_scale, out, lse, ws, stream);
 }
 
 }  // namespace dsa

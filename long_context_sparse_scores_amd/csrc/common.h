@@ -32,16 +32,10 @@ __device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off
     store_wt4(r, off, __float_as_uint(v));
 }
 
-// Device-scope loads (sc1): they miss in this XCD's L2, so they see what
+// Device-scope load (sc1): it misses in this XCD's L2, so it sees what
 // workgroups on other XCDs wrote through to memory during the same launch.
-__device__ __forceinline__ u32x4_t load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
-}
 __device__ __forceinline__ uint32_t load_dev4u(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 16);
-}
-__device__ __forceinline__ float load_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __uint_as_float(load_dev4u(r, off));
 }
 
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
@@ -129,36 +123,19 @@ enum class TopkState {
     kCleared,    // the histogram and counters are zero (TopkPrep without hist)
     kHistogram,  // counters zero and the histogram complete (TopkPrep with hist)
 };
-// clear_after: per-row words the selection clears after its work (the next
-// attention launch's merge counters), words per row at base + row * words.
-struct RowClear {
-    uint32_t* base = nullptr;
-    int words = 0;
-};
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, TopkState state = TopkState::kNone, RowClear clear_after = RowClear());
+                       hipStream_t stream, TopkState state = TopkState::kNone);
 
 int attn_num_splits(int rows, int k);
 size_t attn_ws_bytes(int rows, int k);
-// Per-query counters in an attention workspace that a launch with merge = true
-// needs zero when it starts (each such launch leaves them zero): `words` words
-// per query at base + row * words; base == nullptr when the shape has none.
-struct AttnSync {
-    uint32_t* base = nullptr;
-    int words = 0;
-};
-AttnSync attn_sync(void* ws, int rows, int k);
-// merge: merge the splits of a query inside the split launch when they can all
-// be resident at once (the workspace's counters must then be zero); otherwise,
-// and always with merge = false, a combine launch follows.
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                        int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                       hipStream_t stream, bool merge = false);
+                       hipStream_t stream);
 
 // The same attention over latent rows stored as E4M3 codes (kv_bstride in bytes).
 hipError_t launch_attn_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_bstride, const int32_t* idx, int B,
                            int T, int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                           hipStream_t stream, bool merge = false);
+                           hipStream_t stream);
 
 size_t verify_ws_bytes(int B, int S, int V);
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* draft_tokens, const float* u_acc,

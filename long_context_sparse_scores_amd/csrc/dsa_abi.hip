@@ -187,18 +187,14 @@ int launch_group(const dsa_group_args& a, void* ws, hipStream_t s) {
                                      : dsa::launch_indexer(in.q_idx, in.w, in.k_idx, a.k_bstride, a.q_pos, B, T, L,
                                                            scores, s, prep);
             if (e != hipSuccess) return hip_status(e, "dsa_layer_group/indexer");
-            // the selection also clears the counters with which the attention
-            // launches below merge their splits in-kernel
-            const dsa::AttnSync sync = dsa::attn_sync(attn_ws, rows, k);
             e = dsa::launch_topk(scores, a.q_pos, rows, L, k, in.idx_out, topk_ws, s,
-                                 hist ? dsa::TopkState::kHistogram : dsa::TopkState::kCleared,
-                                 dsa::RowClear{sync.base, sync.words});
+                                 hist ? dsa::TopkState::kHistogram : dsa::TopkState::kCleared);
             if (e != hipSuccess) return hip_status(e, "dsa_layer_group/topk");
         }
         const hipError_t e = a.kv_fp8[l] ? dsa::launch_attn_fp8(a.q[l], a.kv_fp8[l], a.kv_bstride[l], in.idx_out, B, T,
-                                                                L, k, a.sm_scale, a.out[l], a.lse[l], attn_ws, s, true)
+                                                                L, k, a.sm_scale, a.out[l], a.lse[l], attn_ws, s)
                                          : dsa::launch_attn(a.q[l], a.kv[l], a.kv_bstride[l], in.idx_out, B, T, L, k,
-                                                            a.sm_scale, a.out[l], a.lse[l], attn_ws, s, true);
+                                                            a.sm_scale, a.out[l], a.lse[l], attn_ws, s);
         if (e != hipSuccess) return hip_status(e, "dsa_layer_group/attention");
     }
     return ok();

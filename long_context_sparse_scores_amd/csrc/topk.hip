@@ -299,11 +299,9 @@ __device__ __forceinline__ BinPick row_threshold(const HistPart<NT>& hp, uint32_
 
 // The selection is done with the row's histogram (every reader has read it):
 // leave it zero for the next selection, whose indexer adds into it, and mark
-// it so; clear the words the caller asked to be cleared.
+// it so.
 template <int NT>
-__device__ __forceinline__ void finish_row(const RowWs& rw, const Layout& lo, int row, RowClear clear) {
-    if (clear.base)
-        for (int i = threadIdx.x; i < clear.words; i += NT) clear.base[(int64_t)row * clear.words + i] = 0u;
+__device__ __forceinline__ void finish_row(const RowWs& rw, const Layout& lo, int row) {
     for (int i = threadIdx.x; i < kBins; i += NT) rw.hist1[i] = 0u;
     if (threadIdx.x == 0) rw.ctr[kStamp] = histogram_stamp(lo, row);
 }
@@ -716,14 +714,12 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                      const int32_t* __restrict__ q_pos, int L,
                                                                      int k, Layout lo, void* ws,
-                                                                     int32_t* __restrict__ idx, RowClear clear) {
+                                                                     int32_t* __restrict__ idx) {
     const int row = blockIdx.x;
-    if (clear.base)
-        for (int i = threadIdx.x; i < clear.words; i += kSelectThreads) clear.base[(int64_t)row * clear.words + i] = 0u;
     const int64_t n = n_visible(q_pos, row, L);
     int32_t* out = idx + (int64_t)row * k;
     const RowWs rw = row_ws(ws, row, lo);
-    finish_row<kSelectThreads>(rw, lo, row, RowClear());  // the filter pass was the histogram's last reader
+    finish_row<kSelectThreads>(rw, lo, row);  // the filter pass was the histogram's last reader
     if (n <= k) {
         for (int j = threadIdx.x; j < k; j += kSelectThreads) out[j] = j < n ? j : -1;
         return;
@@ -751,7 +747,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float
 __global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float* __restrict__ scores,
                                                                     const int32_t* __restrict__ q_pos, int L, int k,
                                                                     Layout lo, void* ws, int hist_checked,
-                                                                    int32_t* __restrict__ idx, RowClear clear) {
+                                                                    int32_t* __restrict__ idx) {
     constexpr int NT = kSelectThreads;
     const int row = blockIdx.x / lo.fnslice;
     const int slice = blockIdx.x % lo.fnslice;
@@ -783,7 +779,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float*
     const uint32_t T = b0.bin;
     if (n <= k) {
         if (slice == 0) {
-            finish_row<NT>(rw, lo, row, clear);
+            finish_row<NT>(rw, lo, row);
             for (int j = threadIdx.x; j < k; j += NT) out[j] = j < n ? j : -1;
         }
         return;
@@ -829,7 +825,7 @@ __global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float*
     if (!sl.cut) return;
 
     // ---- the last slice workgroup of the row selects
-    finish_row<NT>(rw, lo, row, clear);  // every slice has read the histogram
+    finish_row<NT>(rw, lo, row);  // every slice has read the histogram
     const uint32_t need = (uint32_t)k - b0.above;
     // The counts and the first W entries of every region in one round trip
     // (W = kCandLds / nact: the regions' usual fill); entries of a region past
@@ -991,7 +987,7 @@ TopkPrep topk_prep(void* ws, int rows, int L, bool hist) {
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int L, int k, int32_t* idx, void* ws,
-                       hipStream_t stream, TopkState state, RowClear clear_after) {
+                       hipStream_t stream, TopkState state) {
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
     if (state == TopkState::kNone) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
@@ -1004,13 +1000,12 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
     // the rows with more of them resident per CU.
     if (state == TopkState::kHistogram || rows <= kFusedTarget) {
         hipLaunchKernelGGL(topk_fused_kernel, dim3((unsigned)((int64_t)rows * lo.fnslice)), dim3(kSelectThreads), 0,
-                           stream, scores, q_pos, L, k, lo, ws, state == TopkState::kHistogram ? 1 : 0, idx,
-                           clear_after);
+                           stream, scores, q_pos, L, k, lo, ws, state == TopkState::kHistogram ? 1 : 0, idx);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws, 0);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
-                       idx, clear_after);
+                       idx);
     return hipGetLastError();
 }
 
