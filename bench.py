@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--extra-cpu-seconds", type=float, default=4.0, help="oracle sample time per extra workload")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (reference for HBM byte counters)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="no GPU work: read rocprofv3 --pmc output folders DIR/fetch, DIR/write (FETCH_SIZE, "
+                         "WRITE_SIZE of an --indexer-only run of this workload), DIR/cfetch, DIR/cwrite (the same "
+                         "of --copy-calibrate) and, if present, DIR/gfetch, DIR/gwrite (a group run); write "
+                         "profiles/<indexer>_<workload>_traffic.json and print the per-kernel table")
     return ap.parse_args()
 
 
@@ -94,6 +99,10 @@ def main():
         print("bench.py: this build runs on one GPU only (requested --gpus %d); the multi-GPU "
               "context-parallel path is a design, not a measured configuration." % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.write_traffic:
+        write_traffic(args)
+        return
 
     import torch
 
@@ -378,6 +387,103 @@ def copy_calibrate(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     log("bench: 5 copies of %d bytes done" % n)
+
+
+def read_counter(folder, counter):
+    """Per-dispatch values of one rocprofv3 counter: {kernel name: [values in
+    dispatch order]}, summed over the rows of each dispatch."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (d, name) in sorted(per):
+        out.setdefault(name, []).append(per[(d, name)])
+    return out
+
+
+def short_kernel_name(name):
+    return name.replace("void ", "").replace("dsa::(anonymous namespace)::", "").split("(")[0].strip()
+
+
+def write_traffic(args):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by 1 GiB over its own reading for a 1 GiB device copy."""
+    import hashlib
+    import synth
+    d = args.write_traffic
+    gib = 1 << 30
+
+    def mean_after(vals, skip):
+        v = vals[skip:] if len(vals) > skip else vals
+        return sum(v) / len(v)
+
+    copy_name = lambda m: next(n for n in m if "copyBuffer" in n or "copy" in n.lower())
+    cf, cw = read_counter(os.path.join(d, "cfetch"), "FETCH_SIZE"), read_counter(os.path.join(d, "cwrite"), "WRITE_SIZE")
+    cf_kib, cw_kib = mean_after(cf[copy_name(cf)], 1), mean_after(cw[copy_name(cw)], 1)
+    ff, wf = gib / (cf_kib * 1024), gib / (cw_kib * 1024)  # true bytes per counted byte
+    kname = "indexer_decode_fp8_kernel" if args.index_fp8 else "indexer_decode_kernel"
+    fe, wr = read_counter(os.path.join(d, "fetch"), "FETCH_SIZE"), read_counter(os.path.join(d, "write"), "WRITE_SIZE")
+    kf = next(n for n in fe if kname in n)
+    kw = next(n for n in wr if kname in n)
+    f_kib, w_kib = mean_after(fe[kf], 2), mean_after(wr[kw], 2)
+    cfg = synth.CONFIGS[args.workload]
+    key_bytes = 128 if args.index_fp8 else 256
+    rows = cfg.B * cfg.T
+    alg = cfg.B * cfg.L * key_bytes + rows * 32 * (128 if args.index_fp8 else 256) + rows * 32 * 4
+    src = "indexer.hip"
+    fpre = " --index-fp8" if args.index_fp8 else ""
+    rec = {
+        "kernel": kname,
+        "workload": cfg.name,
+        "source": src,
+        "source_sha256": hashlib.sha256(open(os.path.join(ROOT, "long_context_sparse_scores_amd", "csrc", src),
+                                             "rb").read()).hexdigest(),
+        "dispatches_counted": [len(fe[kf]) - 2, len(wr[kw]) - 2],
+        "fetch_size_kib_per_launch_raw": round(f_kib, 2),
+        "write_size_kib_per_launch_raw": round(w_kib, 2),
+        "copy_calibration": {"bytes_copied": gib, "fetch_size_kib_raw": round(cf_kib, 2),
+                             "write_size_kib_raw": round(cw_kib, 2), "fetch_factor": round(ff, 5),
+                             "write_factor": round(wf, 5)},
+        "fetch_bytes_per_launch": int(f_kib * 1024 * ff),
+        "write_bytes_per_launch": int(w_kib * 1024 * wf),
+        "algorithmic_bytes_per_launch": alg,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d %s/fetch -o run --output-format csv -- python3 bench.py --workload %s%s "
+            "--no-cpu --indexer-only --steps 5 --warmup 1" % (d, cfg.name, fpre),
+            "rocprofv3 --pmc WRITE_SIZE -d %s/write -o run --output-format csv -- python3 bench.py --workload %s%s "
+            "--no-cpu --indexer-only --steps 5 --warmup 1" % (d, cfg.name, fpre),
+            "rocprofv3 --pmc FETCH_SIZE -d %s/cfetch -o run --output-format csv -- python3 bench.py --copy-calibrate" % d,
+            "rocprofv3 --pmc WRITE_SIZE -d %s/cwrite -o run --output-format csv -- python3 bench.py --copy-calibrate" % d,
+            "python3 bench.py --write-traffic %s --workload %s%s" % (d, cfg.name, fpre),
+        ],
+        "note": "per-launch averages over the indexer dispatches after the first two; the counters read KiB per "
+                "dispatch; each is scaled by 1 GiB / (its reading for a 1 GiB device copy). The written bytes are "
+                "the fp32 score rows (B*T*L*4).",
+    }
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    out = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % ("indexer_fp8" if args.index_fp8 else "indexer",
+                                                                 cfg.name))
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    log("bench: wrote %s" % out)
+    gf, gw = os.path.join(d, "gfetch"), os.path.join(d, "gwrite")
+    if os.path.isdir(gf) and os.path.isdir(gw):
+        fe, wr = read_counter(gf, "FETCH_SIZE"), read_counter(gw, "WRITE_SIZE")
+        print("| kernel | dispatches | fetched MB per launch | written MB per launch |")
+        print("|---|---|---|---|")
+        for n in sorted(fe, key=lambda n: -mean_after(fe[n], 2)):
+            if "copy" in n.lower() or "fill" in n.lower():
+                continue
+            w = wr.get(n, [0.0])
+            print("| %s | %d | %.1f | %.1f |" % (short_kernel_name(n), len(fe[n]), mean_after(fe[n], 2) * 1024 * ff / 1e6,
+                                              mean_after(w, 2) * 1024 * wf / 1e6))
 
 
 def cpu_model():

@@ -226,6 +226,7 @@ struct SelectLds {
     uint32_t sel[kSelMax];
     uint32_t scratch[NT / kWave];
     uint32_t sbase[kFusedMaxSlices], scnt[kFusedMaxSlices];  // fused pass: slice offsets and counts
+    uint32_t sextra[kFusedMaxSlices];                         // fused pass: offsets of entries past the first read
     uint32_t gkey[kWave];                                     // a small group's keys (positions in sel)
     BinPick pick;
     uint32_t nsel, cut, cut_key;
@@ -406,15 +407,35 @@ __device__ __forceinline__ Cut find_cut(SelectLds<NT>& s, uint32_t T, uint32_t n
     return Cut{kstar, pos_cut};
 }
 
+// The largest s < n with a[s] <= x, for a non-decreasing a with a[0] <= x and
+// n <= kFusedMaxSlices: with a the offsets of consecutive regions in their
+// concatenation, the region that holds entry x (the last of any empty ones).
+__device__ __forceinline__ int last_le(const uint32_t* a, int n, uint32_t x) {
+    int s = 0;
+#pragma unroll
+    for (int step = kFusedMaxSlices / 2; step > 0; step >>= 1)
+        if (s + step < n && a[s + step] <= x) s += step;
+    return s;
+}
+
+// Where the selection finds the row's candidates (the keys whose top digit is
+// T or above): the filter pass's list, the fused pass's per-slice regions (none
+// overflowed; s.sbase holds their offsets), or the row's scores.
+enum class CandSource { kList, kRegions, kScores };
+struct Regions {
+    int nact = 0;  // regions (active slices)
+    int pcap = 0;  // entries per region
+};
+
 // The k kept positions of one row with n > k visible keys, ascending, into
-// out[0, k): NT threads.  The candidates (the keys whose top digit is T or
-// above; need = k minus the count of keys above T's bin) come from the filter
-// pass's list of ncand entries when from_list, else from the row's scores
-// (the list overflowed).
+// out[0, k): NT threads.  The candidates number ncand; need = k minus the count
+// of keys above T's bin.  Regions are read with device-scope loads (other
+// workgroups of this launch wrote them).
 template <int NT>
 __device__ __forceinline__ void select_row(const float* __restrict__ row_scores, int64_t n, int k, const RowWs& rw,
-                                           bool from_list, uint32_t ncand, uint32_t T, uint32_t need,
+                                           CandSource src, Regions rg, uint32_t ncand, uint32_t T, uint32_t need,
                                            int32_t* __restrict__ out, SelectLds<NT>& s) {
+    const bool from_list = src == CandSource::kList;
     const bool in_lds = from_list && ncand <= (uint32_t)kCandLds;
     const int lane = lane_id();
     constexpr uint32_t kStep = kSelBatch * NT;
@@ -461,6 +482,20 @@ __device__ __forceinline__ void select_row(const float* __restrict__ row_scores,
                     ok[j] = i < ncand;
                     ck[j] = ok[j] ? rw.ckey[i] : 0u;
                     cp[j] = ok[j] ? rw.cpos[i] : 0u;
+                }
+                g(ck, cp, ok);
+            }
+        } else if (src == CandSource::kRegions) {
+            const __amdgpu_buffer_rsrc_t pos_r = wt_rsrc(rw.cpos), key_r = wt_rsrc(rw.ckey);
+            for (uint32_t i0 = 0; i0 < ncand; i0 += kStep) {
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j) {
+                    const uint32_t i = i0 + j * NT + threadIdx.x;
+                    ok[j] = i < ncand;
+                    const int r = last_le(s.sbase, rg.nact, ok[j] ? i : 0u);
+                    const uint32_t off = 4u * ((uint32_t)r * (uint32_t)rg.pcap + (i - s.sbase[r]));
+                    ck[j] = ok[j] ? load_dev4u(key_r, off) : 0u;
+                    cp[j] = ok[j] ? load_dev4u(pos_r, off) : 0u;
                 }
                 g(ck, cp, ok);
             }
@@ -726,8 +761,9 @@ __global__ __launch_bounds__(kSelectThreads) void topk_select_kernel(const float
     }
     __shared__ SelectLds<kSelectThreads> sl;
     const uint32_t ncand = rw.ctr[kCtrCand];
-    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, rw, ncand <= (uint32_t)lo.cap, ncand, rw.ctr[kStT],
-                               (uint32_t)k - rw.ctr[kStAbove], out, sl);
+    select_row<kSelectThreads>(scores + (int64_t)row * L, n, k, rw,
+                               ncand <= (uint32_t)lo.cap ? CandSource::kList : CandSource::kScores, Regions(), ncand,
+                               rw.ctr[kStT], (uint32_t)k - rw.ctr[kStAbove], out, sl);
 }
 
 // Filter and selection in one launch, for rows whose top-digit histogram the
@@ -855,68 +891,143 @@ __global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float*
     for (int i = threadIdx.x; i < kBins; i += NT) sl.h[i] = 0u;
     lds_sync();
     const uint32_t beyond = sl.nsel;
-    if (ncand > (uint32_t)kCandLds) {
-        select_row<NT>(row_scores, n, k, rw, false, ncand, T, need, out, sl);
+    if (ncand > (uint32_t)kCandLds && (beyond & 2u)) {  // too many to hold, and a region overflowed
+        select_row<NT>(row_scores, n, k, rw, CandSource::kScores, Regions(), ncand, T, need, out, sl);
         return;
     }
-    // Candidates to LDS in position order (entry o of slice s's region is
-    // candidate sbase[s] + o), counting the middle digit of those in T's bin.
-    auto place = [&](uint32_t c, uint32_t pos, uint32_t key) {
-        sl.cand.pos[c] = pos;
-        sl.cand.key[c] = key;
-        if ((key >> 21) == T) atomicAdd(&sl.h[(key >> 10) & 0x7FFu], 1u);
-    };
+    BinPick b1;        // the middle digit of K* among the keys in T's bin
+    uint32_t nlds;     // candidates in the LDS copy, in position order
+    if (ncand > (uint32_t)kCandLds) {
+        // More candidates than the LDS copy holds (long rows): one pass over
+        // the regions finds the middle digit, a second copies to LDS only the
+        // keys whose top 22 bits are K*'s or above, about k of them.
+        auto region_batch = [&](uint32_t i0, uint32_t (&ck)[kSelBatch], uint32_t (&cp)[kSelBatch],
+                                bool (&ok)[kSelBatch]) {
 #pragma unroll
-    for (int j = 0; j < kSelBatch; ++j) {
-        const uint32_t e = j * NT + threadIdx.x;
-        const uint32_t sidx = e / W, o = e - sidx * W;
-        if (sidx < (uint32_t)nact) {
-            const uint32_t cs = sl.scnt[sidx];
-            if (o < cs && cs <= (uint32_t)lo.pcap) place(sl.sbase[sidx] + o, cp[j], ck[j]);  // overflowed: below
-        }
-    }
-    for (int sidx = 0; (beyond & 1u) && sidx < nact; ++sidx) {
-        const uint32_t cs = sl.scnt[sidx];
-        if (cs <= W || cs > (uint32_t)lo.pcap) continue;
-        for (uint32_t o = W + threadIdx.x; o < cs; o += NT) {
-            const uint32_t off = 4u * ((uint32_t)sidx * (uint32_t)lo.pcap + o);
-            place(sl.sbase[sidx] + o, load_dev4u(pos_r, off), load_dev4u(key_r, off));
-        }
-    }
-    const bool overflowed = (beyond & 2u) != 0u;
-    for (int sidx = 0; overflowed && sidx < nact; ++sidx) {
-        if (sl.scnt[sidx] <= (uint32_t)lo.pcap) continue;
-        // this slice's region overflowed: its candidates again, from its scores
-        const int64_t s0 = (int64_t)sidx * lo.fslice, s1 = min(s0 + (int64_t)lo.fslice, n);
-        uint32_t run = sl.sbase[sidx];
-        for (int64_t i0 = s0; i0 < s1; i0 += (int64_t)kFPer * NT) {
-            load_batch(i0, s1);
-            bool f[kFPer];
-            uint32_t key[kFPer];
-#pragma unroll
-            for (int j = 0; j < kFPer; ++j) {
-                key[j] = score_key(v[j]);
-                f[j] = i0 + j * NT + (int)threadIdx.x < s1 && (key[j] >> 21) >= T;
+            for (int j = 0; j < kSelBatch; ++j) {
+                const uint32_t i = i0 + j * NT + threadIdx.x;
+                ok[j] = i < ncand;
+                const int r = last_le(sl.sbase, nact, ok[j] ? i : 0u);
+                const uint32_t off = 4u * ((uint32_t)r * (uint32_t)lo.pcap + (i - sl.sbase[r]));
+                ck[j] = ok[j] ? load_dev4u(key_r, off) : 0u;
+                cp[j] = ok[j] ? load_dev4u(pos_r, off) : 0u;
             }
-            const uint32_t c = ordered_slots<NT, kFPer>(f, sl.sel, sl.scratch, [&](uint32_t slot, int j) {
-                slot += run;  // below ncand: the same scores and T give the same count
+        };
+        for (uint32_t i0 = 0; i0 < ncand; i0 += kSelBatch * NT) {
+            uint32_t ck[kSelBatch], cq[kSelBatch];
+            bool ok[kSelBatch];
+            region_batch(i0, ck, cq, ok);
+#pragma unroll
+            for (int j = 0; j < kSelBatch; ++j)
+                if (ok[j] && (ck[j] >> 21) == T) atomicAdd(&sl.h[(ck[j] >> 10) & 0x7FFu], 1u);
+        }
+        lds_sync();
+        b1 = pick_bin<NT>(load_hist<NT>(sl.h, kBins), kBins, need, sl.scratch, &sl.pick);
+        const uint32_t prefix = (T << 11) | b1.bin;
+        const uint32_t nsel = ((uint32_t)k - need) + b1.above + b1.count;  // keys at K*'s top 22 bits or above
+        if (nsel > (uint32_t)kCandLds) {  // so many keys tied on K*'s top 22 bits: passes over the regions
+            Regions rg;
+            rg.nact = nact;
+            rg.pcap = lo.pcap;
+            select_row<NT>(row_scores, n, k, rw, CandSource::kRegions, rg, ncand, T, need, out, sl);
+            return;
+        }
+        uint32_t run = 0;
+        for (uint32_t i0 = 0; i0 < ncand; i0 += kSelBatch * NT) {
+            uint32_t ck[kSelBatch], cq[kSelBatch];
+            bool ok[kSelBatch], f[kSelBatch];
+            region_batch(i0, ck, cq, ok);
+#pragma unroll
+            for (int j = 0; j < kSelBatch; ++j) f[j] = ok[j] && (ck[j] >> 10) >= prefix;
+            const uint32_t c = ordered_slots<NT, kSelBatch>(f, sl.sel, sl.scratch, [&](uint32_t slot, int j) {
+                slot += run;
                 if (slot < (uint32_t)kCandLds) {
-                    sl.cand.pos[slot] = (uint32_t)(i0 + j * NT + threadIdx.x);
-                    sl.cand.key[slot] = key[j];
-                    if ((key[j] >> 21) == T) atomicAdd(&sl.h[(key[j] >> 10) & 0x7FFu], 1u);
+                    sl.cand.pos[slot] = cq[j];
+                    sl.cand.key[slot] = ck[j];
                 }
             });
             run += c;
         }
+        nlds = run;  // == nsel
+    } else {
+        // Candidates to LDS in position order (entry o of slice s's region is
+        // candidate sbase[s] + o), counting the middle digit of those in T's bin.
+        auto place = [&](uint32_t c, uint32_t pos, uint32_t key) {
+            sl.cand.pos[c] = pos;
+            sl.cand.key[c] = key;
+            if ((key >> 21) == T) atomicAdd(&sl.h[(key >> 10) & 0x7FFu], 1u);
+        };
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+            const uint32_t e = j * NT + threadIdx.x;
+            const uint32_t sidx = e / W, o = e - sidx * W;
+            if (sidx < (uint32_t)nact) {
+                const uint32_t cs = sl.scnt[sidx];
+                if (o < cs && cs <= (uint32_t)lo.pcap) place(sl.sbase[sidx] + o, cp[j], ck[j]);  // overflowed: below
+            }
+        }
+        if (beyond & 1u) {
+            // Entries W.. of the regions that hold more (and did not overflow), in
+            // one round: their extra counts, scanned, address them like the regions.
+            const uint32_t cs = (int)threadIdx.x < nact ? sl.scnt[threadIdx.x] : 0u;
+            uint32_t nextra;
+            const uint32_t ex = excl_scan<NT>(cs > W && cs <= (uint32_t)lo.pcap ? cs - W : 0u, sl.scratch, &nextra);
+            if ((int)threadIdx.x < nact) sl.sextra[threadIdx.x] = ex;
+            lds_sync();
+            for (uint32_t i0 = 0; i0 < nextra; i0 += kSelBatch * NT) {
+                uint32_t xp[kSelBatch], xk[kSelBatch], xc[kSelBatch];
+                bool xo[kSelBatch];
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j) {
+                    const uint32_t i = i0 + j * NT + threadIdx.x;
+                    xo[j] = i < nextra;
+                    const int r = last_le(sl.sextra, nact, xo[j] ? i : 0u);
+                    const uint32_t o = W + (i - sl.sextra[r]);
+                    const uint32_t off = 4u * ((uint32_t)r * (uint32_t)lo.pcap + o);
+                    xc[j] = sl.sbase[r] + o;
+                    xp[j] = xo[j] ? load_dev4u(pos_r, off) : 0u;
+                    xk[j] = xo[j] ? load_dev4u(key_r, off) : 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < kSelBatch; ++j)
+                    if (xo[j]) place(xc[j], xp[j], xk[j]);
+            }
+        }
+        const bool overflowed = (beyond & 2u) != 0u;
+        for (int sidx = 0; overflowed && sidx < nact; ++sidx) {
+            if (sl.scnt[sidx] <= (uint32_t)lo.pcap) continue;
+            // this slice's region overflowed: its candidates again, from its scores
+            const int64_t s0 = (int64_t)sidx * lo.fslice, s1 = min(s0 + (int64_t)lo.fslice, n);
+            uint32_t run = sl.sbase[sidx];
+            for (int64_t i0 = s0; i0 < s1; i0 += (int64_t)kFPer * NT) {
+                load_batch(i0, s1);
+                bool f[kFPer];
+                uint32_t key[kFPer];
+#pragma unroll
+                for (int j = 0; j < kFPer; ++j) {
+                    key[j] = score_key(v[j]);
+                    f[j] = i0 + j * NT + (int)threadIdx.x < s1 && (key[j] >> 21) >= T;
+                }
+                const uint32_t c = ordered_slots<NT, kFPer>(f, sl.sel, sl.scratch, [&](uint32_t slot, int j) {
+                    slot += run;  // below ncand: the same scores and T give the same count
+                    if (slot < (uint32_t)kCandLds) {
+                        sl.cand.pos[slot] = (uint32_t)(i0 + j * NT + threadIdx.x);
+                        sl.cand.key[slot] = key[j];
+                        if ((key[j] >> 21) == T) atomicAdd(&sl.h[(key[j] >> 10) & 0x7FFu], 1u);
+                    }
+                });
+                run += c;
+            }
+        }
+        lds_sync();
+        b1 = pick_bin<NT>(load_hist<NT>(sl.h, kBins), kBins, need, sl.scratch, &sl.pick);
+        nlds = ncand;
     }
-    lds_sync();
-    const HistPart<NT> hmid = load_hist<NT>(sl.h, kBins);
-    const BinPick b1 = pick_bin<NT>(hmid, kBins, need, sl.scratch, &sl.pick);
     auto for_candidates = [&](auto&& f) {
 #pragma unroll
         for (int j = 0; j < kSelBatch; ++j) {
             const uint32_t c = j * NT + threadIdx.x;
-            if (c < ncand) f(sl.cand.key[c], sl.cand.pos[c]);
+            if (c < nlds) f(sl.cand.key[c], sl.cand.pos[c]);
         }
     };
     const Cut cut = find_cut<NT>(sl, T, need, b1, for_candidates);
@@ -926,9 +1037,9 @@ __global__ __launch_bounds__(kSelectThreads) void topk_fused_kernel(const float*
 #pragma unroll
     for (int j = 0; j < kSelBatch; ++j) {
         const uint32_t c = j * NT + threadIdx.x;
-        const uint32_t key = c < ncand ? sl.cand.key[c] : 0u;
-        kp[j] = c < ncand ? sl.cand.pos[c] : 0u;
-        f[j] = c < ncand && (key > cut.kstar || (key == cut.kstar && kp[j] <= cut.pos_cut));
+        const uint32_t key = c < nlds ? sl.cand.key[c] : 0u;
+        kp[j] = c < nlds ? sl.cand.pos[c] : 0u;
+        f[j] = c < nlds && (key > cut.kstar || (key == cut.kstar && kp[j] <= cut.pos_cut));
     }
     const __amdgpu_buffer_rsrc_t out_wt = wt_rsrc(out);
     ordered_slots<NT, kSelBatch>(f, sl.sel, sl.scratch,
