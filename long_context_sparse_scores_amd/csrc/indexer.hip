@@ -372,6 +372,29 @@ constexpr int kPfTileBytes = kPfTileKeys * kD * 2;   // 16 KiB
 constexpr int kPfKeysPerBlock = 2048;          // keys per workgroup
 constexpr int kPrefillMinQueries = 8;          // chunks of at least this many queries per sequence
 
+// Causal skip for a multi-query workgroup: keys past the largest position of
+// its queries are visible to none of them, so whole tiles past it are neither
+// loaded nor computed; their scores are written as -inf (fill_masked).
+__device__ __forceinline__ int64_t group_max_pos(const int32_t* __restrict__ q_pos, int b, int T, int qg) {
+    int64_t m = -1;
+#pragma unroll
+    for (int i = 0; i < kPfQueries; ++i) {
+        const int t = min(qg * kPfQueries + i, T - 1);
+        m = max(m, (int64_t)q_pos[(int64_t)b * T + t]);
+    }
+    return m;
+}
+
+// -inf for keys [k0, k1) of the group's score rows (queries below T).
+__device__ __forceinline__ void fill_masked(__amdgpu_buffer_rsrc_t grp_out, int qg, int T, int L, int64_t k0,
+                                            int64_t k1) {
+    const int nk = (int)(k1 - k0);
+    if (nk <= 0) return;
+    const int nq = min(kPfQueries, T - qg * kPfQueries);
+    for (int i = threadIdx.x; i < nq * nk; i += 256)
+        store_wt4(grp_out, 4u * (uint32_t)((int64_t)(i / nk) * L + k0 + i % nk), -INFINITY);
+}
+
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb,
@@ -419,7 +442,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
 
     const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
-    const int ntiles = (int)((min((int64_t)L, key0 + kPfKeysPerBlock) - key0 + kPfTileKeys - 1) / kPfTileKeys);
+    const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
+    const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
+    const int ntiles = (int)((kvis_end - key0 + kPfTileKeys - 1) / kPfTileKeys);
+    fill_masked(grp_out, qg, T, L, key0 + (int64_t)ntiles * kPfTileKeys, kblk_end);
+    if (ntiles == 0) return;
     // tile loads: thread (wave st, lane) brings chunk lane%16 of keys 16*st + 4i + lane/16, i < 4
     u32x4_t ld[4];
     auto load_tile = [&](int j) {
@@ -549,7 +576,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
 
     const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
-    const int ntiles = (int)((min((int64_t)L, key0 + kPfKeysPerBlock) - key0 + kPf8TileKeys - 1) / kPf8TileKeys);
+    const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
+    const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
+    const int ntiles = (int)((kvis_end - key0 + kPf8TileKeys - 1) / kPf8TileKeys);
+    fill_masked(grp_out, qg, T, L, key0 + (int64_t)ntiles * kPf8TileKeys, kblk_end);
+    if (ntiles == 0) return;
     // tile loads: thread i brings 16-byte chunks i and i + 256 (key = chunk / 8, s = chunk % 8)
     u32x4_t ld[2];
     auto load_tile = [&](int j) {
