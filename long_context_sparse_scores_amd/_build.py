@@ -7,9 +7,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libdsa.so")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU forms are disabled for every HIP translation unit.
+# Packed-fp32 VALU forms are disabled for every HIP translation unit.  MFMA
+# results go to VGPRs rather than AGPRs (no v_accvgpr_read copies before the
+# indexers' epilogues; the other kernels compile the same either way).
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
+# Per-file additions.  indexer.hip: its ReLU (fmaxf) is one v_max_f32 only
+# when NaNs need not be quieted; the scores are defined for finite inputs.
+FILE_FLAGS = {"indexer.hip": ["-fno-honor-nans"]}
 
 
 def sources():
@@ -24,7 +32,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = ["hipcc"] + HIP_FLAGS + ["-c", src, "-o", obj]
+        cmd = ["hipcc"] + HIP_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -30,6 +30,11 @@
 namespace dsa {
 namespace {
 
+// ReLU as one v_max_f32: this file is compiled with -fno-honor-nans, so max(x, 0)
+// needs no extra instruction to quiet a signalling NaN first; scores of finite
+// inputs are unchanged.
+__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
+
 constexpr int kH = 32;
 constexpr int kD = 128;
 constexpr int kTile = 16;                      // keys per MFMA tile
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
             float part = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                part = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, part);
-                part = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, part);
+                part = fmaf(wv[0][r], relu(a0[r]), part);
+                part = fmaf(wv[1][r], relu(a1[r]), part);
             }
             part += __shfl_xor(part, 16, kWave);
             part += __shfl_xor(part, 32, kWave);
@@ -325,8 +330,8 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
                 float v = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v = fmaf(wv[0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
-                    v = fmaf(wv[1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                    v = fmaf(wv[0][r], relu(a0[r]), v);
+                    v = fmaf(wv[1][r], relu(a1[r]), v);
                 }
                 v += __shfl_xor(v, 16, kWave);
                 v += __shfl_xor(v, 32, kWave);
@@ -490,8 +495,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
                 float v = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v = fmaf(wv[i][0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
-                    v = fmaf(wv[i][1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                    v = fmaf(wv[i][0][r], relu(a0[r]), v);
+                    v = fmaf(wv[i][1][r], relu(a1[r]), v);
                 }
                 part[i] = v;
             }
@@ -623,8 +628,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
                 float v = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v = fmaf(wv[i][0][r], a0[r] > 0.0f ? a0[r] : 0.0f, v);
-                    v = fmaf(wv[i][1][r], a1[r] > 0.0f ? a1[r] : 0.0f, v);
+                    v = fmaf(wv[i][0][r], relu(a0[r]), v);
+                    v = fmaf(wv[i][1][r], relu(a1[r]), v);
                 }
                 part[i] = v;
             }
