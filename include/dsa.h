@@ -60,7 +60,7 @@ extern "C" {
 #define DSA_LATENT_DIM 576
 #define DSA_VALUE_DIM 512
 #define DSA_GROUP_LAYERS_MAX 8
-#define DSA_ATTN_CONTEXT_MAX 4194304 /* rows per sequence the attention kernels address (2^22) */
+#define DSA_ATTN_CONTEXT_MAX 4194304 /* keys per sequence the indexer and attention kernels address (2^22) */
 
 enum {
     DSA_OK = 0,
@@ -84,7 +84,7 @@ const char* dsa_last_error(void);
  *   q_idx   [B,T,H,D] bf16      w [B,T,H] fp32      q_pos [B,T] int32
  *   k_idx   row s of batch b at k_idx + b*k_bstride + s*D (bf16), s < L
  *   scores  [B,T,L] fp32 (output)
- * H must be 32 and D 128.  Needs no workspace. */
+ * H must be 32 and D 128; L <= DSA_ATTN_CONTEXT_MAX.  Needs no workspace. */
 int dsa_indexer_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t k_bstride,
                        const int32_t* q_pos, int B, int T, int L, int H, int D, float* scores, void* stream);
 

@@ -22,6 +22,13 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
+// A raw buffer of `bytes` bytes (at most 2^31 - 1): a lane whose offset plus
+// access size passes the end reads zeros and its store is dropped, so a
+// ragged edge needs no branch (kOutOfRange is past any such buffer).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ void store_wt16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
 }

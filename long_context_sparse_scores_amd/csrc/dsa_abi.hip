@@ -51,6 +51,7 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, int64_t 
                   int B, int T, int L, int H, int D, const float* scores, int elem_bytes = 2) {
     if (!q_idx || !w || !k_idx || !q_pos || !scores) return fail(DSA_ERR_NULL, "indexer: NULL pointer argument");
     if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "indexer: B=%d T=%d L=%d must be >= 1", B, T, L);
+    if (L > DSA_ATTN_CONTEXT_MAX) return fail(DSA_ERR_SHAPE, "indexer: L=%d above %d", L, DSA_ATTN_CONTEXT_MAX);
     if (H != DSA_INDEX_HEADS || D != DSA_INDEX_DIM)
         return fail(DSA_ERR_UNSUPPORTED, "indexer: H=%d D=%d, supported H=%d D=%d", H, D, DSA_INDEX_HEADS,
                     DSA_INDEX_DIM);

@@ -400,6 +400,51 @@ __device__ __forceinline__ void fill_masked(__amdgpu_buffer_rsrc_t grp_out, int 
         store_wt4(grp_out, 4u * (uint32_t)((int64_t)(i / nk) * L + k0 + i % nk), -INFINITY);
 }
 
+// The wave's 4 per-query partial scores summed over its 4 lane groups: lane
+// group g returns query g's total.  v_permlane32_swap trades the upper 32
+// lanes of its first operand for the lower 32 of its second, and
+// v_permlane16_swap the odd 16-lane rows of its first operand for the even
+// rows of its second; after each swap the two registers add up to one query's
+// sum over twice as many lane groups.  No LDS round trip, no lane selects.
+__device__ __forceinline__ float sum_lane_groups(const float (&part)[4]) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float x = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // lanes 0-31: query 0, 32-63: query 2
+    const float y = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // lanes 0-31: query 1, 32-63: query 3
+    const auto sxy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(sxy[0]) + __uint_as_float(sxy[1]);
+}
+
+// Per-lane constants of a multi-query workgroup's score stores: lane group g
+// writes row 4*wave + g of the group's score rows, key column c of each
+// 16-key sub-tile.  The row buffer ends after the group's last query below T,
+// so rows past it drop their stores; keys past L get an offset past the end.
+struct PfOut {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t off;  // bytes: (row * L + key0 + c) * 4
+    int nk;        // keys of the block below L, minus c
+    int vis;       // last key of the block this lane's query sees, minus c (may be < 0)
+};
+__device__ __forceinline__ PfOut pf_out(float* scores, const int32_t* __restrict__ q_pos, int b, int T, int L, int qg,
+                                        int wave, int g, int c, int64_t key0) {
+    PfOut o;
+    const int nq = min(kPfQueries, T - qg * kPfQueries);
+    o.rs = sized_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L, 4u * (uint32_t)nq * (uint32_t)L);
+    const int row = kPfQPerWave * wave + g;
+    o.off = 4u * ((uint32_t)row * (uint32_t)L + (uint32_t)key0 + (uint32_t)c);
+    o.nk = (int)min((int64_t)L - key0, (int64_t)kPfKeysPerBlock) - c;
+    const int64_t p = q_pos[(int64_t)b * T + min(qg * kPfQueries + row, T - 1)];
+    o.vis = (int)max(min(p - key0, (int64_t)kPfKeysPerBlock), (int64_t)-1) - c;
+    return o;
+}
+// Score of key key0 + kbase + c (kbase: the sub-tile's first key in the
+// block, wave-uniform): -inf past the query's position; dropped for keys past
+// L and rows past the last query.
+__device__ __forceinline__ void pf_store(const PfOut& o, int kbase, float score) {
+    const uint32_t off = kbase < o.nk ? o.off + 4u * (uint32_t)kbase : kOutOfRange;
+    store_wt4(o.rs, off, kbase <= o.vis ? score : -INFINITY);
+}
+
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     int64_t k_bstride, const int32_t* __restrict__ q_pos, int T, int L, int nqg, int nkb,
@@ -409,7 +454,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const int qg = (blockIdx.x / nkb) % nqg;     // query group within the sequence
     const int b = blockIdx.x / (nkb * nqg);
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane & 15;
     const int g = lane >> 4;
     const int t0 = qg * kPfQueries + kPfQPerWave * wave;  // this wave's first query
@@ -438,29 +483,25 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) wv[i][ht][r] = w[row * kH + 16 * ht + 4 * g + r];
     }
-    // this lane stores query 4w+g
-    const int my_t = t0 + g;
-    const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
-    const int64_t my_p = q_pos[my_row];
-    // this workgroup's 16 score rows (offsets below 16 * L * 4 bytes)
-    const __amdgpu_buffer_rsrc_t grp_out = wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L);
-
-    const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
+    const PfOut out = pf_out(scores, q_pos, b, T, L, qg, wave, g, c, key0);
+
     const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
     const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
     const int ntiles = (int)((kvis_end - key0 + kPfTileKeys - 1) / kPfTileKeys);
-    fill_masked(grp_out, qg, T, L, key0 + (int64_t)ntiles * kPfTileKeys, kblk_end);
+    fill_masked(wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L), qg, T, L,
+                key0 + (int64_t)ntiles * kPfTileKeys, kblk_end);
     if (ntiles == 0) return;
-    // tile loads: thread (wave st, lane) brings chunk lane%16 of keys 16*st + 4i + lane/16, i < 4
+    // tile loads: thread (wave st, lane) brings chunk lane%16 of keys 16*st + 4i + lane/16, i < 4;
+    // keys past L read zeros (their scores are never stored), so the tile after the last is safe
+    const __amdgpu_buffer_rsrc_t krs = sized_rsrc(k_idx + (int64_t)b * k_bstride, (uint32_t)L * (kD * 2));
+    const uint32_t ld_off = (uint32_t)key0 * (kD * 2) + (16 * wave + (lane >> 4)) * (kD * 2) + 16 * (lane & 15);
     u32x4_t ld[4];
     auto load_tile = [&](int j) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int64_t key = key0 + (int64_t)j * kPfTileKeys + 16 * wave + 4 * i + (lane >> 4);
-            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
-            ld[i] = *reinterpret_cast<const u32x4_t*>(kb + key * kD + 8 * (lane & 15));
-        }
+        for (int i = 0; i < 4; ++i)
+            ld[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    krs, (int)(ld_off + (uint32_t)j * kPfTileBytes + i * 4 * kD * 2), 0, 0));
     };
     auto store_tile = [&](int j) {  // chunk s of key k (within a 16-key sub-tile) at 16k + (s ^ k)
         uint16_t* sub = stage + (j & 1) * (kPfTileBytes / 2) + wave * (16 * kD);
@@ -474,7 +515,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     store_tile(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1);  // in flight while tile j is computed
+        load_tile(j + 1);  // in flight while tile j is computed
         const uint16_t* tile = stage + (j & 1) * (kPfTileBytes / 2);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -500,20 +541,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
                 }
                 part[i] = v;
             }
-            // transpose-reduce over the 4 lane groups: group g ends with query g's total
-            const bool hi = (g & 2) != 0, lo = (g & 1) != 0;
-            const float r0 = __shfl_xor(hi ? part[0] : part[2], 32, kWave);
-            const float r1 = __shfl_xor(hi ? part[1] : part[3], 32, kWave);
-            const float k0 = (hi ? part[2] : part[0]) + r0;
-            const float k1 = (hi ? part[3] : part[1]) + r1;
-            const float rr = __shfl_xor(lo ? k0 : k1, 16, kWave);
-            const float score = (lo ? k1 : k0) + rr;
-            const int64_t key = key0 + (int64_t)j * kPfTileKeys + 16 * st + c;
-            if (my_t < T && key < L)
-                store_wt4(grp_out, 4u * (uint32_t)((int64_t)(my_t - qg * kPfQueries) * L + key),
-                          key <= my_p ? score : -INFINITY);
+            pf_store(out, j * kPfTileKeys + 16 * st, sum_lane_groups(part));
         }
-        if (j + 1 < ntiles) store_tile(j + 1);
+        store_tile(j + 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 }
@@ -573,29 +603,25 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) wv[i][ht][r] = w[row * kH + 16 * ht + 4 * g + r];
     }
-    const int my_t = t0 + g;
-    const int64_t my_row = (int64_t)b * T + min(my_t, T - 1);
-    const int64_t my_p = q_pos[my_row];
-    // this workgroup's 16 score rows (offsets below 16 * L * 4 bytes)
-    const __amdgpu_buffer_rsrc_t grp_out = wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L);
-
-    const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
     const int64_t key0 = (int64_t)kb_i * kPfKeysPerBlock;
+    const PfOut out = pf_out(scores, q_pos, b, T, L, qg, wave, g, c, key0);
+
     const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
     const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
     const int ntiles = (int)((kvis_end - key0 + kPf8TileKeys - 1) / kPf8TileKeys);
-    fill_masked(grp_out, qg, T, L, key0 + (int64_t)ntiles * kPf8TileKeys, kblk_end);
+    fill_masked(wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L), qg, T, L,
+                key0 + (int64_t)ntiles * kPf8TileKeys, kblk_end);
     if (ntiles == 0) return;
-    // tile loads: thread i brings 16-byte chunks i and i + 256 (key = chunk / 8, s = chunk % 8)
+    // tile loads: thread i brings 16-byte chunks i and i + 256 (key = chunk / 8, s = chunk % 8);
+    // keys past L read zeros (their scores are never stored), so the tile after the last is safe
+    const __amdgpu_buffer_rsrc_t krs = sized_rsrc(k_idx + (int64_t)b * k_bstride, (uint32_t)L * kD8);
+    const uint32_t ld_off = (uint32_t)key0 * kD8 + 16u * threadIdx.x;
     u32x4_t ld[2];
     auto load_tile = [&](int j) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int chunk = (int)threadIdx.x + 256 * h;
-            int64_t key = key0 + (int64_t)j * kPf8TileKeys + (chunk >> 3);
-            key = key < L ? key : (int64_t)L - 1;  // ragged tail: a valid row, never stored
-            ld[h] = *reinterpret_cast<const u32x4_t*>(kb + key * kD8 + 16 * (chunk & 7));
-        }
+        for (int h = 0; h < 2; ++h)
+            ld[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    krs, (int)(ld_off + (uint32_t)j * kPf8TileBytes + h * 4096), 0, 0));
     };
     auto store_tile = [&](int j) {
         uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
@@ -610,7 +636,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     store_tile(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) load_tile(j + 1);  // in flight while tile j is computed
+        load_tile(j + 1);  // in flight while tile j is computed
         const uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
 #pragma unroll
         for (int st = 0; st < kPf8TileKeys / 16; ++st) {
@@ -633,20 +659,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
                 }
                 part[i] = v;
             }
-            // transpose-reduce over the 4 lane groups: group g ends with query g's total
-            const bool hi_g = (g & 2) != 0, lo_g = (g & 1) != 0;
-            const float r0 = __shfl_xor(hi_g ? part[0] : part[2], 32, kWave);
-            const float r1 = __shfl_xor(hi_g ? part[1] : part[3], 32, kWave);
-            const float k0 = (hi_g ? part[2] : part[0]) + r0;
-            const float k1 = (hi_g ? part[3] : part[1]) + r1;
-            const float rr = __shfl_xor(lo_g ? k0 : k1, 16, kWave);
-            const float score = (lo_g ? k1 : k0) + rr;
-            const int64_t key = key0 + (int64_t)j * kPf8TileKeys + 16 * st + c;
-            if (my_t < T && key < L)
-                store_wt4(grp_out, 4u * (uint32_t)((int64_t)(my_t - qg * kPfQueries) * L + key),
-                          key <= my_p ? score : -INFINITY);
+            pf_store(out, j * kPf8TileKeys + 16 * st, sum_lane_groups(part));
         }
-        if (j + 1 < ntiles) store_tile(j + 1);
+        store_tile(j + 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 }

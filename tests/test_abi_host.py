@@ -85,9 +85,12 @@ def test_validation_rejects_before_launch(dsa):
     assert lib.dsa_sparse_mla_attn(fake, fake, big_l * 576, fake, 1, 1, big_l, 64, 576, 512, 16, 0.1, fake, None,
                                    None, 0, None) == -2
     assert "above" in dsa.last_error()
+    # the indexer's score offsets are 32-bit: the same context limit
+    assert lib.dsa_indexer_scores(fake, fake, fake, 1 << 34, fake, 1, 1, big_l, 32, 128, fake, None) == -2
+    assert "above" in dsa.last_error()
     # a decode grid (1024 keys per workgroup) past 2^31 workgroups, rejected before launch
-    big_b = 1 << 14
-    assert lib.dsa_indexer_scores(fake, fake, fake, 1 << 34, fake, big_b, 1, 1 << 27, 32, 128, fake, None) == -2
+    big_b = 1 << 20
+    assert lib.dsa_indexer_scores(fake, fake, fake, 1 << 34, fake, big_b, 1, 1 << 22, 32, 128, fake, None) == -2
     assert "grid" in dsa.last_error()
     # misalignment
     assert lib.dsa_indexer_scores(fake + 2, fake, fake, 16 * 128, fake, 1, 1, 16, 32, 128, fake, None) == -4
