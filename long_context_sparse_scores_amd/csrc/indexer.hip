@@ -517,21 +517,26 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     for (int j = 0; j < ntiles; ++j) {
         load_tile(j + 1);  // in flight while tile j is computed
         const uint16_t* tile = stage + (j & 1) * (kPfTileBytes / 2);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint16_t* sub = tile + st * (16 * kD);
-            bf16x8_t kv[4];
+        // B operands of sub-tile st + 1 are read while sub-tile st is computed
+        bf16x8_t kv[2][4];
+        auto read_sub = [&](int st) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kv[kk] = *reinterpret_cast<const bf16x8_t*>(sub + 8 * (16 * c + ((4 * kk + g) ^ c)));
+                kv[st & 1][kk] =
+                    *reinterpret_cast<const bf16x8_t*>(tile + st * (16 * kD) + 8 * (16 * c + ((4 * kk + g) ^ c)));
+        };
+        read_sub(0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st + 1 < 4) read_sub(st + 1);
             float part[kPfQPerWave];
 #pragma unroll
             for (int i = 0; i < kPfQPerWave; ++i) {
                 f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    a0 = mfma16x16x32(qa[i][0][kk], kv[kk], a0);
-                    a1 = mfma16x16x32(qa[i][1][kk], kv[kk], a1);
+                    a0 = mfma16x16x32(qa[i][0][kk], kv[st & 1][kk], a0);
+                    a1 = mfma16x16x32(qa[i][1][kk], kv[st & 1][kk], a1);
                 }
                 float v = 0.0f;
 #pragma unroll
