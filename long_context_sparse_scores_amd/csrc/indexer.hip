@@ -368,8 +368,9 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
 // Key tiles of 64 keys go through a double-buffered, swizzled LDS stage and
 // every B operand read from it feeds 8 MFMAs (4 queries x 2 head blocks).  The
 // ReLU, the head weights and the sum over heads are folded into the epilogue;
-// a 3-shuffle transpose-reduce leaves query 4w+g's score in lane group g, so
-// one store covers a 16-key sub-tile for the wave's 4 queries.
+// a sum over the four lane groups by permlane swaps leaves query 4w+g's score
+// in lane group g, so one store covers a 16-key sub-tile for the wave's 4
+// queries.
 constexpr int kPfQueries = 16;                 // queries per workgroup
 constexpr int kPfQPerWave = 4;
 constexpr int kPfTileKeys = 64;                // keys per LDS tile
