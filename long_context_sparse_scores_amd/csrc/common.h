@@ -29,6 +29,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sized_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// 16-byte streaming load (nt: the line is not kept for reuse).
+__device__ __forceinline__ u32x4_t load_nt16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 __device__ __forceinline__ void store_wt16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
 }

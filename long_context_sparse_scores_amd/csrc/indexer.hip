@@ -60,6 +60,23 @@ __device__ __forceinline__ void prep_start(const TopkPrep& prep, int row, int bl
     }
 }
 
+// Sum over the four 16-lane groups of a wave, every lane ending with the total
+// (the MFMA C layout spreads a key's 32 heads over the groups).
+// v_permlane16_swap(x, x) pairs each row with its neighbour, v_permlane32_swap
+// each half with the other; the two swapped copies add up to the pair's sum.
+__device__ __forceinline__ float sum_all_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
+// Histogram bin of a score, or the spare bin kTopBins (never flushed) for a
+// key the selection does not see: one LDS add with no branch.
+__device__ __forceinline__ int hist_bin(float score, bool counted) {
+    return counted ? (int)(score_key(score) >> 21) : kTopBins;
+}
+
 __device__ __forceinline__ void prep_flush(const TopkPrep& prep, int row, const uint32_t* hist_lds, int nthreads) {
     __syncthreads();  // every wave's counts are in
     uint32_t* gh = prep.base + row * prep.stride;
@@ -104,7 +121,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     static_assert(kTilesPerWave % 4 == 0, "the four lane groups take whole tiles each");
     static_assert(kTilesPerWave % kBufs == 0, "tile j of every block sits in buffer j % kBufs");
     __shared__ __attribute__((aligned(16))) uint16_t stage[kWaves * 2 * kTileBytes / 2];
-    __shared__ uint32_t hist_lds[kTopBins];
+    __shared__ uint32_t hist_lds[kTopBins + 1];  // + the spare bin of keys not counted
     __shared__ __attribute__((aligned(16))) float sst[kDecodeMaxPer * kKeysPerBlock];  // scores of the range
     const int row = blockIdx.x / wpr;  // b*T + t
     const int blk0 = (blockIdx.x % wpr) * per;
@@ -112,10 +129,11 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
     if (blk0 >= blk1) return;
     const int b = row / T;
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane & 15;  // key within tile (B/C column)
     const int g = lane >> 4;  // lane group: 8-dim slice of each 32-dim step; head row block in C
     const int64_t p = q_pos[row];
+    const int last_seen = (int)min(p, (int64_t)L - 1);  // keys the selection counts: 0 .. last_seen
     prep_start(prep, row, blk0, hist_lds, kWaves * kWave);
 
     // A operands: q rows (heads) 16*ht + c, dims 32*kk + 8*g .. +7.
@@ -133,22 +151,20 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[ht][r] = w[(int64_t)row * kH + 16 * ht + 4 * g + r];
 
-    const uint16_t* kb = k_idx + (int64_t)b * k_bstride;
+    // The sequence's keys as a buffer of L rows: rows past L (the ragged tail,
+    // the last block's look-ahead) read as zeros and their scores are never used.
+    const __amdgpu_buffer_rsrc_t krs = sized_rsrc(k_idx + (int64_t)b * k_bstride, (uint32_t)L * (kD * 2));
     // Tile j of block blk for this wave covers keys blk*kKeysPerBlock + (kWaves*j + wave)*16 .. +15;
     // at each step the block's waves read kWaves*16 consecutive keys.
-    auto tile_key0 = [&](int blk, int j) {
-        return (int64_t)blk * kKeysPerBlock + (int64_t)(kWaves * j + wave) * kTile;
-    };
+    auto tile_key0 = [&](int blk, int j) { return blk * kKeysPerBlock + (kWaves * j + wave) * kTile; };
     uint16_t* my_stage = stage + wave * kTileBytes;  // two 4 KiB slots per wave
+    const uint32_t ld_lane = (uint32_t)(lane >> 4) * (kD * 2) + 16u * (lane & 15);
 
     u32x4_t buf[kBufs][kLoads];
     auto load_tile = [&](int blk, int j, u32x4_t (&dst)[kLoads]) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            int64_t key = tile_key0(blk, j) + 4 * i + (lane >> 4);
-            key = key < L ? key : (int64_t)L - 1;  // past the row (or the last block's look-ahead): a valid row, never used
-            dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + key * kD + 8 * (lane & 15)));
-        }
+        for (int i = 0; i < kLoads; ++i)  // keys tile_key0 + 4i + lane/16, 16-byte chunk lane%16
+            dst[i] = load_nt16(krs, (uint32_t)tile_key0(blk, j) * (kD * 2) + ld_lane + i * (4 * kD * 2));
     };
     // In tile order (no reordering by the scheduler): the loop's first wait,
     // for tile 0, then counts only the loads issued after it, on entry as on
@@ -186,13 +202,10 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_kernel(
                 part = fmaf(wv[0][r], relu(a0[r]), part);
                 part = fmaf(wv[1][r], relu(a1[r]), part);
             }
-            part += __shfl_xor(part, 16, kWave);
-            part += __shfl_xor(part, 32, kWave);
+            part = sum_all_groups(part);
             sc[j] = part;
-            if (prep.hist && g == (j & 3)) {  // lane group g counts the tiles j = g (mod 4)
-                const int64_t key = tile_key0(blk, j) + c;
-                if (key < L && key <= p) atomicAdd(&hist_lds[score_key(part) >> 21], 1u);
-            }
+            if (prep.hist && g == (j & 3))  // lane group g counts the tiles j = g (mod 4)
+                atomicAdd(&hist_lds[hist_bin(part, tile_key0(blk, j) + c <= last_seen)], 1u);
         }
         if (g == 0) {  // lane group 0 keeps the scores (the others hold the same sums)
 #pragma unroll
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
     static_assert(kTilesPerWave % 2 == 0, "lane groups 2, 3 take the odd tiles");
     static_assert(kTilesPerWave % kBufs == 0, "tile j of every block sits in buffer j % kBufs");
     __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * 2 * kTile8Bytes];
-    __shared__ uint32_t hist_lds[kTopBins];
+    __shared__ uint32_t hist_lds[kTopBins + 1];  // + the spare bin of keys not counted
     __shared__ __attribute__((aligned(16))) float sst[kDecode8MaxPer * kKeysPerBlock];  // scores of the range
     const int row = blockIdx.x / wpr;  // b*T + t
     const int blk0 = (blockIdx.x % wpr) * per;
@@ -265,6 +278,7 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
     const int c = lane & 15;
     const int g = lane >> 4;
     const int64_t p = q_pos[row];
+    const int last_seen = (int)min(p, (int64_t)L - 1);  // keys the selection counts: 0 .. last_seen
     prep_start(prep, row, blk0, hist_lds, kWaves * kWave);
 
     // A operands: head 16*ht + c, dims 32*kk + 8*g .. +7 (8 codes).
@@ -281,20 +295,16 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[ht][r] = w[(int64_t)row * kH + 16 * ht + 4 * g + r];
 
-    const uint8_t* kb = k_idx + (int64_t)b * k_bstride;
-    auto tile_key0 = [&](int blk, int j) {
-        return (int64_t)blk * kKeysPerBlock + (int64_t)(kWaves * j + wave) * kTile8;
-    };
+    // keys past L (the ragged tail, the last block's look-ahead) read as zeros, their scores never used
+    const __amdgpu_buffer_rsrc_t krs = sized_rsrc(k_idx + (int64_t)b * k_bstride, (uint32_t)L * kD8);
+    auto tile_key0 = [&](int blk, int j) { return blk * kKeysPerBlock + (kWaves * j + wave) * kTile8; };
     uint8_t* my_stage = stage + wave * 2 * kTile8Bytes;
 
     u32x4_t buf[kBufs][kLoads8];
     auto load_tile = [&](int blk, int j, u32x4_t (&dst)[kLoads8]) {
 #pragma unroll
-        for (int i = 0; i < kLoads8; ++i) {
-            int64_t key = tile_key0(blk, j) + 8 * i + (lane >> 3);
-            key = key < L ? key : (int64_t)L - 1;  // past the row (or the last block's look-ahead): a valid row, never used
-            dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + key * kD8 + 16 * (lane & 7)));
-        }
+        for (int i = 0; i < kLoads8; ++i)  // keys tile_key0 + 8i + lane/8, 16-byte chunk lane%8: 1 KiB contiguous
+            dst[i] = load_nt16(krs, (uint32_t)tile_key0(blk, j) * kD8 + 16u * lane + i * 1024);
     };
 #pragma unroll
     for (int j = 0; j < kAhead8; ++j) {  // in tile order (see the bf16 scan)
@@ -333,16 +343,12 @@ __global__ __launch_bounds__(kWaves * kWave) void indexer_decode_fp8_kernel(
                     v = fmaf(wv[0][r], relu(a0[r]), v);
                     v = fmaf(wv[1][r], relu(a1[r]), v);
                 }
-                v += __shfl_xor(v, 16, kWave);
-                v += __shfl_xor(v, 32, kWave);
-                part[kbk] = v;
+                part[kbk] = sum_all_groups(v);
             }
             // every lane of column c now holds both sums; lane group g keeps key 16*(g & 1) + c
             sc[j] = (g & 1) ? part[1] : part[0];
-            if (prep.hist && (g >> 1) == (j & 1)) {  // groups 0, 1 count the even tiles, groups 2, 3 the odd ones
-                const int64_t key = tile_key0(blk, j) + 16 * (g & 1) + c;
-                if (key < L && key <= p) atomicAdd(&hist_lds[score_key(sc[j]) >> 21], 1u);
-            }
+            if (prep.hist && (g >> 1) == (j & 1))  // groups 0, 1 count the even tiles, groups 2, 3 the odd ones
+                atomicAdd(&hist_lds[hist_bin(sc[j], tile_key0(blk, j) + 16 * (g & 1) + c <= last_seen)], 1u);
         }
         if (g < 2) {  // lane groups 0 and 1 keep the tile's two 16-key halves
 #pragma unroll
