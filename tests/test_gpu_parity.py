@@ -85,6 +85,32 @@ def test_indexer_multi_query_edges_guarded(dsa, fp8):
     assert torch.isnan(guard[B * T * L:]).all().item()
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_indexer_decode_edges_guarded(dsa, fp8):
+    # per-query path (T < 8) at its edges: a key cache of exactly L rows whose
+    # last block reads past it, a length that is no multiple of the 1024-key
+    # blocks or the 16-key tiles, positions 0, in the middle and at the last
+    # key; the scores sit in a larger buffer whose tail must stay untouched
+    B, T, L = 3, 2, 3 * 1024 + 517
+    say("indexer decode edges fp8=%s B=%d T=%d L=%d" % (fp8, B, T, L))
+    qi = synth.int_bf16(35, 1, (B, T, 32, 128))
+    w = synth.pow2_f32(35, 2, (B, T, 32))
+    ki = synth.int_bf16(35, 3, (B, L, 128))
+    pos = np.array([[0, L - 1], [1500, 2047], [L - 1, L - 2]], np.int32)
+    guard = torch.full((B * T * L + 4096,), float("nan"), dtype=torch.float32, device=DEV)
+    scores = guard[:B * T * L].view(B, T, L)
+    if fp8:
+        qi, ki = (synth.to_e4m3(synth.bf16_to_f32(a)) for a in (qi, ki))
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEV)
+        dsa.indexer_scores_fp8(dev(qi), f32_dev(w), dev(ki), i32_dev(pos), scores=scores)
+    else:
+        dsa.indexer_scores(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), scores=scores)
+    got = host(scores)
+    ref = oracle.indexer_scores(qi, w, ki, pos, fp8=fp8)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert torch.isnan(guard[B * T * L:]).all().item()
+
+
 def test_indexer_negative_weights(dsa):
     # general weights (not the test distribution): still exact for integer inputs
     B, T, L = 1, 2, 777
