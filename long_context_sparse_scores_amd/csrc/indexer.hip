@@ -24,6 +24,7 @@
 // in LDS and are stored after the stream, so the loop contains only loads.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -397,6 +398,40 @@ __device__ __forceinline__ int64_t group_max_pos(const int32_t* __restrict__ q_p
     return m;
 }
 
+// Smallest position among a multi-query workgroup's queries: key tiles below
+// it are visible to every query of the group.
+__device__ __forceinline__ int64_t group_min_pos(const int32_t* __restrict__ q_pos, int b, int T, int qg) {
+    int64_t m = INT64_MAX;
+#pragma unroll
+    for (int i = 0; i < kPfQueries; ++i) {
+        const int t = min(qg * kPfQueries + i, T - 1);
+        m = min(m, (int64_t)q_pos[(int64_t)b * T + t]);
+    }
+    return m;
+}
+
+// Tile loop of a multi-query workgroup: tile(j, masked, parity) for j < ntiles,
+// the first nfull tiles (every key below L and visible to every query) without
+// masking, in pairs so that each tile's LDS buffer (j & 1) is a compile-time
+// constant; a tile past nfull may still be fully visible, and masking it
+// changes nothing.
+template <typename Tile>
+__device__ __forceinline__ void pf_tile_runs(int ntiles, int nfull, Tile&& tile) {
+    using F = std::false_type;
+    using M = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int j = 0;
+    for (; j + 2 <= nfull; j += 2) {
+        tile(j, F(), P0());
+        tile(j + 1, F(), P1());
+    }
+    for (; j < ntiles; j += 2) {
+        tile(j, M(), P0());
+        if (j + 1 < ntiles) tile(j + 1, M(), P1());
+    }
+}
+
 // -inf for keys [k0, k1) of the group's score rows (queries below T).
 __device__ __forceinline__ void fill_masked(__amdgpu_buffer_rsrc_t grp_out, int qg, int T, int L, int64_t k0,
                                             int64_t k1) {
@@ -446,10 +481,17 @@ __device__ __forceinline__ PfOut pf_out(float* scores, const int32_t* __restrict
 }
 // Score of key key0 + kbase + c (kbase: the sub-tile's first key in the
 // block, wave-uniform): -inf past the query's position; dropped for keys past
-// L and rows past the last query.
+// L and rows past the last query.  Unmasked (a tile below L that every query
+// sees): the wave-uniform key offset goes in the scalar offset; rows past the
+// last query still fall outside the buffer by their own offset.
+template <bool kMasked>
 __device__ __forceinline__ void pf_store(const PfOut& o, int kbase, float score) {
-    const uint32_t off = kbase < o.nk ? o.off + 4u * (uint32_t)kbase : kOutOfRange;
-    store_wt4(o.rs, off, kbase <= o.vis ? score : -INFINITY);
+    if constexpr (kMasked) {
+        const uint32_t off = kbase < o.nk ? o.off + 4u * (uint32_t)kbase : kOutOfRange;
+        store_wt4(o.rs, off, kbase <= o.vis ? score : -INFINITY);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), o.rs, (int)o.off, (int)(4u * (uint32_t)kbase), 16);
+    }
 }
 
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
@@ -496,6 +538,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
     const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
     const int ntiles = (int)((kvis_end - key0 + kPfTileKeys - 1) / kPfTileKeys);
+    const int64_t kall_end = min(kblk_end, max(key0, group_min_pos(q_pos, b, T, qg) + 1));  // seen by all
+    const int nfull = (int)((kall_end - key0) / kPfTileKeys);
     fill_masked(wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L), qg, T, L,
                 key0 + (int64_t)ntiles * kPfTileKeys, kblk_end);
     if (ntiles == 0) return;
@@ -510,8 +554,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
             ld[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                     krs, (int)(ld_off + (uint32_t)j * kPfTileBytes + i * 4 * kD * 2), 0, 0));
     };
-    auto store_tile = [&](int j) {  // chunk s of key k (within a 16-key sub-tile) at 16k + (s ^ k)
-        uint16_t* sub = stage + (j & 1) * (kPfTileBytes / 2) + wave * (16 * kD);
+    auto store_tile = [&](int parity) {  // chunk s of key k (within a 16-key sub-tile) at 16k + (s ^ k)
+        uint16_t* sub = stage + parity * (kPfTileBytes / 2) + wave * (16 * kD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int k = 4 * i + (lane >> 4);
@@ -521,9 +565,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     load_tile(0);
     store_tile(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int j = 0; j < ntiles; ++j) {
+    pf_tile_runs(ntiles, nfull, [&](int j, auto masked, auto parity) {
+        constexpr int kP = decltype(parity)::value;
         load_tile(j + 1);  // in flight while tile j is computed
-        const uint16_t* tile = stage + (j & 1) * (kPfTileBytes / 2);
+        const uint16_t* tile = stage + kP * (kPfTileBytes / 2);
         // B operands of sub-tile st + 1 are read while sub-tile st is computed
         bf16x8_t kv[2][4];
         auto read_sub = [&](int st) {
@@ -553,11 +598,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
                 }
                 part[i] = v;
             }
-            pf_store(out, j * kPfTileKeys + 16 * st, sum_lane_groups(part));
+            pf_store<decltype(masked)::value>(out, j * kPfTileKeys + 16 * st, sum_lane_groups(part));
         }
-        store_tile(j + 1);
+        store_tile(kP ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+    });
 }
 
 
@@ -621,6 +666,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     const int64_t kblk_end = min((int64_t)L, key0 + kPfKeysPerBlock);
     const int64_t kvis_end = min(kblk_end, max(key0, group_max_pos(q_pos, b, T, qg) + 1));
     const int ntiles = (int)((kvis_end - key0 + kPf8TileKeys - 1) / kPf8TileKeys);
+    const int64_t kall_end = min(kblk_end, max(key0, group_min_pos(q_pos, b, T, qg) + 1));  // seen by all
+    const int nfull = (int)((kall_end - key0) / kPf8TileKeys);
     fill_masked(wt_rsrc(scores + ((int64_t)b * T + qg * kPfQueries) * L), qg, T, L,
                 key0 + (int64_t)ntiles * kPf8TileKeys, kblk_end);
     if (ntiles == 0) return;
@@ -635,8 +682,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
             ld[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                     krs, (int)(ld_off + (uint32_t)j * kPf8TileBytes + h * 4096), 0, 0));
     };
-    auto store_tile = [&](int j) {
-        uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
+    auto store_tile = [&](int parity) {
+        uint8_t* tile = stage + parity * kPf8TileBytes;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int chunk = (int)threadIdx.x + 256 * h;
@@ -647,9 +694,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
     load_tile(0);
     store_tile(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int j = 0; j < ntiles; ++j) {
+    pf_tile_runs(ntiles, nfull, [&](int j, auto masked, auto parity) {
+        constexpr int kP = decltype(parity)::value;
         load_tile(j + 1);  // in flight while tile j is computed
-        const uint8_t* tile = stage + (j & 1) * kPf8TileBytes;
+        const uint8_t* tile = stage + kP * kPf8TileBytes;
 #pragma unroll
         for (int st = 0; st < kPf8TileKeys / 16; ++st) {
             const int k = 16 * st + c;  // key of this lane's B column
@@ -671,11 +719,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
                 }
                 part[i] = v;
             }
-            pf_store(out, j * kPf8TileKeys + 16 * st, sum_lane_groups(part));
+            pf_store<decltype(masked)::value>(out, j * kPf8TileKeys + 16 * st, sum_lane_groups(part));
         }
-        store_tile(j + 1);
+        store_tile(kP ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+    });
 }
 }  // namespace
 
