@@ -577,28 +577,34 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
                 kv[st & 1][kk] =
                     *reinterpret_cast<const bf16x8_t*>(tile + st * (16 * kD) + 8 * (16 * c + ((4 * kk + g) ^ c)));
         };
+        // The tile's (sub-tile, query) pairs p = 4 st + i as a pipeline: each
+        // of pair p's 8 MFMAs issues beside one ReLU and weighted add of pair
+        // p - 1, in the plain sum's order (head row r, then head block), so two
+        // VALU instructions sit behind every MFMA instead of a VALU-only
+        // epilogue after each query; sched_barrier keeps that order.
+        const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc[2][2];  // [pair parity][head block]
+        float part[kPfQPerWave];
+        float v = 0.0f;
         read_sub(0);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            if (st + 1 < 4) read_sub(st + 1);
-            float part[kPfQPerWave];
+        for (int pp = 0; pp <= 4 * kPfQPerWave; ++pp) {
+            const int st = pp / kPfQPerWave, i = pp % kPfQPerWave;                 // pair pp (pp < 16)
+            const int pst = (pp - 1) / kPfQPerWave, pi = (pp - 1) % kPfQPerWave;   // pair pp - 1 (pp > 0)
+            if (pp < 4 * kPfQPerWave && i == 0 && st + 1 < 4) read_sub(st + 1);
 #pragma unroll
-            for (int i = 0; i < kPfQPerWave; ++i) {
-                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    a0 = mfma16x16x32(qa[i][0][kk], kv[st & 1][kk], a0);
-                    a1 = mfma16x16x32(qa[i][1][kk], kv[st & 1][kk], a1);
-                }
-                float v = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v = fmaf(wv[i][0][r], relu(a0[r]), v);
-                    v = fmaf(wv[i][1][r], relu(a1[r]), v);
-                }
-                part[i] = v;
+            for (int s = 0; s < 8; ++s) {
+                const int ht = s & 1, r = s >> 1;  // MFMA k-step r of head block ht; epilogue head row r
+                if (pp < 4 * kPfQPerWave)
+                    acc[pp & 1][ht] = mfma16x16x32(qa[i][ht][r], kv[st & 1][r], r == 0 ? zero4 : acc[pp & 1][ht]);
+                if (pp > 0) v = fmaf(wv[pi][ht][r], relu(acc[(pp - 1) & 1][ht][r]), s == 0 ? 0.0f : v);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            pf_store<decltype(masked)::value>(out, j * kPfTileKeys + 16 * st, sum_lane_groups(part));
+            if (pp > 0) {
+                part[pi] = v;
+                if (pi == kPfQPerWave - 1)
+                    pf_store<decltype(masked)::value>(out, j * kPfTileKeys + 16 * pst, sum_lane_groups(part));
+            }
         }
         store_tile(kP ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
