@@ -704,28 +704,39 @@ __global__ __launch_bounds__(256) void indexer_prefill_fp8_kernel(
         constexpr int kP = decltype(parity)::value;
         load_tile(j + 1);  // in flight while tile j is computed
         const uint8_t* tile = stage + kP * kPf8TileBytes;
-#pragma unroll
-        for (int st = 0; st < kPf8TileKeys / 16; ++st) {
+        i32x8_t kv[2];  // B operands of sub-tile st + 1 are read while sub-tile st is computed
+        auto read_sub = [&](int st) {
             const int k = 16 * st + c;  // key of this lane's B column
             const int f = (k >> 1) & 7;
             const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(tile + 16 * (8 * k + ((2 * g) ^ f)));
             const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(tile + 16 * (8 * k + ((2 * g + 1) ^ f)));
-            const i32x8_t kv = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            float part[kPfQPerWave];
+            kv[st & 1] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // (sub-tile, query) pairs as a pipeline, as in the bf16 kernel: pair
+        // p's two MFMAs issue among the 16 epilogue instructions of pair p - 1.
+        const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc[2][2];  // [pair parity][head block]
+        float part[kPfQPerWave];
+        float v = 0.0f;
+        read_sub(0);
 #pragma unroll
-            for (int i = 0; i < kPfQPerWave; ++i) {
-                const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-                const f32x4_t a0 = mfma16x16x128_fp8(qa[i][0], kv, zero4);
-                const f32x4_t a1 = mfma16x16x128_fp8(qa[i][1], kv, zero4);
-                float v = 0.0f;
+        for (int pp = 0; pp <= 4 * kPfQPerWave; ++pp) {
+            const int st = pp / kPfQPerWave, i = pp % kPfQPerWave;                 // pair pp (pp < 16)
+            const int pst = (pp - 1) / kPfQPerWave, pi = (pp - 1) % kPfQPerWave;   // pair pp - 1 (pp > 0)
+            if (pp < 4 * kPfQPerWave && i == 0 && st + 1 < 4) read_sub(st + 1);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v = fmaf(wv[i][0][r], relu(a0[r]), v);
-                    v = fmaf(wv[i][1][r], relu(a1[r]), v);
-                }
-                part[i] = v;
+            for (int s = 0; s < 8; ++s) {
+                const int ht = s & 1, r = s >> 1;  // epilogue head row r of head block ht
+                if (pp < 4 * kPfQPerWave && (s & 3) == 0)
+                    acc[pp & 1][s >> 2] = mfma16x16x128_fp8(qa[i][s >> 2], kv[st & 1], zero4);
+                if (pp > 0) v = fmaf(wv[pi][ht][r], relu(acc[(pp - 1) & 1][ht][r]), s == 0 ? 0.0f : v);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            pf_store<decltype(masked)::value>(out, j * kPf8TileKeys + 16 * st, sum_lane_groups(part));
+            if (pp > 0) {
+                part[pi] = v;
+                if (pi == kPfQPerWave - 1)
+                    pf_store<decltype(masked)::value>(out, j * kPf8TileKeys + 16 * pst, sum_lane_groups(part));
+            }
         }
         store_tile(kP ^ 1);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
