@@ -247,10 +247,15 @@ def bench_group(cfg, args):
     # ---------------- per-phase breakdown (same kernels, called one entry point at a time)
     topk_ws = torch.empty(dsa.topk_workspace_size(B, T, L, k), dtype=torch.uint8, device=dev)
     attn_ws = torch.empty(max(256, dsa.attn_workspace_size(B, T, k)), dtype=torch.uint8, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 + nl)]
     phase = np.zeros(2 + nl)
     reps = max(5, args.steps // 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 + nl)] for _ in range(reps + 2)]
+    # Group steps queued first keep the GPU busy while the host queues the
+    # phases, so no event sees the GPU idle waiting for the next launch.
+    for _ in range(20):
+        group_step()
     for r in range(reps + 2):
+        ev = evs[r]
         ev[0].record()
         indexer_step()
         ev[1].record()
@@ -259,9 +264,9 @@ def bench_group(cfg, args):
         for l in range(nl):
             dsa.sparse_mla_attn(qs[l], kvs[l], idx, cfg.sm_scale, out=outs[l], ws=attn_ws)
             ev[3 + l].record()
-        torch.cuda.synchronize()
-        if r >= 2:
-            phase += [ev[i].elapsed_time(ev[i + 1]) for i in range(2 + nl)]
+    torch.cuda.synchronize()
+    for ev in evs[2:]:
+        phase += [ev[i].elapsed_time(ev[i + 1]) for i in range(2 + nl)]
     phase /= reps
     breakdown = {"indexer_ms": round(phase[0], 4), "topk_ms": round(phase[1], 4),
                  "attn_ms_per_layer": [round(x, 4) for x in phase[2:]]}
