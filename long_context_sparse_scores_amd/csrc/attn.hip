@@ -238,12 +238,11 @@ constexpr int kFlagOffset = kMainBytes + 4 * 16 * 4;
 __device__ __forceinline__ bf16x8_t softmax_tile(const f32x4_t (&s)[2], uint32_t valid, bool full, float scale_log2,
                                                  SoftmaxState& st, float& factor, bool& moved) {
     float x[8];
-    if (full) {  // wave-uniform: every row of the tile is visible
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = s[e >> 2][e & 3] * scale_log2;
-    } else {
+    for (int e = 0; e < 8; ++e) x[e] = s[e >> 2][e & 3] * scale_log2;
+    if (!full) {  // wave-uniform: some row of the tile is masked (in place, so the paths share registers)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ((valid >> e) & 1u) ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        for (int e = 0; e < 8; ++e) x[e] = ((valid >> e) & 1u) ? x[e] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     factor = 1.0f;
