@@ -12,11 +12,14 @@
 // of a dense 32x128 by 128xN contraction on the matrix cores:
 // v_mfma_f32_16x16x32_bf16, two 16-head blocks sharing each 16-key B operand.
 //
-// Keys are read with plain 16-byte loads in which every instruction covers
-// four whole keys (1 KiB contiguous), one 16-key tile per wave at a time: with
-// two workgroups of four waves per CU that is about 8 MiB in flight over the
-// chip, which streams at the chip's measured read rate (7.0 TB/s at 128K x 32;
-// one or three tiles ahead per wave measured 2% and 7% slower).  Each tile is
+// Keys are read with 16-byte loads through a raw buffer of the sequence's L
+// rows (rows past L read as zeros, so the ragged end needs no clamp), every
+// instruction covering four whole keys (1 KiB contiguous), and the sum over
+// the MFMA lane groups uses permlane swaps.  One 16-key tile per wave is in
+// flight at a time: with two workgroups of four waves per CU that is about
+// 8 MiB in flight over the chip, which streams at the chip's measured read
+// rate (7.0 TB/s at 128K x 32; one or three tiles ahead per wave measured 2%
+// and 7% slower).  Each tile is
 // then turned into the MFMA operand layout through a small wave-private LDS
 // slot: lane l writes chunk l%16 of key 4i + l/16, and reads back chunk
 // 4kk + l/16 of key l%16.  Chunk s of key k is stored at position 16k + (s ^ k),
