@@ -246,11 +246,12 @@ constexpr int kD8 = 128;                        // bytes per key
 constexpr int kTile8Bytes = kTile8 * kD8;       // 4 KiB
 constexpr int kLoads8 = kTile8Bytes / (kWave * 16);  // 4 loads of 1 KiB per tile
 
-// 4 waves x 16 tiles of 32 keys per block (2048 keys), one tile loaded ahead
-// (measured at 128K x 32 and 1M x 4: 81.7 us against 82.9 with none, 86.8 with three).
+// 4 waves x 16 tiles of 32 keys per block (2048 keys), no tile loaded ahead
+// (with the buffer loads, measured at 128K x 32: 79.5 us against 80.8 with one
+// and 84.5 with three; at 1M x 4: 79.4 against 81.4 with one).
 constexpr int kDecode8Waves = 4;
 constexpr int kDecode8Tiles = 16;
-constexpr int kDecode8Ahead = 1;
+constexpr int kDecode8Ahead = 0;
 constexpr int kDecode8MaxPer = 4;  // blocks per workgroup (their scores wait in LDS)
 
 __device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, f32x4_t c) {
