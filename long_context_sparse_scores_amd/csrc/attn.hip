@@ -70,6 +70,12 @@ constexpr int kTargetBlocks = 256;                // one resident block per CU
 // rounds than they save (measured at 1M, B = 4: 64 splits of one tile 29 us per
 // layer, 32 splits 19.8, 16 splits 18.4, 8 splits 20.6).
 constexpr int kMaxQuerySplits = 16;
+// A split launch whose bf16 row gathers come to at least this many bytes
+// streams them past the caches (nontemporal loads).  Measured with four
+// layers back to back: B = 32 at 128K (72 MiB of rows per launch), 27.9 ->
+// 25.5 us per layer in the group step; B = 16 (36 MiB), 18.9 -> 20.5 us
+// streamed, so smaller launches keep plain loads.
+constexpr int64_t kStreamGatherBytes = 64ll << 20;
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs, block ids dealt round-robin
 constexpr float kRescaleSlack = 32.0f;            // log2 units: P < 2^32, |O| < 2^46 in fp32
 
@@ -91,14 +97,29 @@ constexpr int kMainBytes = kRows * 1024;
 // The compiler warns that it may not preserve a reserved register across asm;
 // that is harmless here, because nothing else in these kernels keeps a value
 // in m0: in their assembly every write of m0 is one of these statements.
+// STREAM adds the nontemporal hint: the rows are read once, and they do not
+// displace from the caches what the following kernels read back (the split
+// partials, the next layer's inputs).
+template <bool STREAM>
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte_addr) : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_byte_addr)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_byte_addr)
+                     : "memory", "m0");
 }
 
 // Same, with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.
+template <bool STREAM>
 __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_byte_addr)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
+                     "s"(lds_byte_addr)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_byte_addr)
+                     : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
@@ -150,9 +171,10 @@ __device__ __forceinline__ GatherPlan plan_gather(const uint16_t* __restrict__ k
 }
 
 // Load i of the plan: i < 8 the main part of row 8w+i, i == 8 the tails.
+template <bool STREAM>
 __device__ __forceinline__ void issue_gather(const GatherPlan& gp, int i) {
     if (!gp.active) return;
-    lds_dma16(i < 8 ? gp.src[i] : gp.tail, i < 8 ? gp.lds[i] : gp.lds_tail);
+    lds_dma16<STREAM>(i < 8 ? gp.src[i] : gp.tail, i < 8 ? gp.lds[i] : gp.lds_tail);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -410,9 +432,10 @@ __device__ __forceinline__ GatherPlan8 plan_gather8(const uint8_t* __restrict__ 
     return gp;
 }
 
+template <bool STREAM>
 __device__ __forceinline__ void issue_gather(const GatherPlan8& gp, int i) {
     if (!gp.active || i >= gp.nload) return;
-    lds_dma16_sbase(gp.base, gp.off[i], gp.lds[i]);
+    lds_dma16_sbase<STREAM>(gp.base, gp.off[i], gp.lds[i]);
 }
 
 // Wait until at most `tiles` (0..5) E4M3 tile gathers of this wave, of nload
@@ -638,7 +661,7 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
 // FP8: the latent rows are E4M3 codes in a ring of seven 18 KiB tiles with the
 // rescale records beside it; otherwise bf16 tiles with the records in the
 // freed K-tail of each tile (the bf16 decode configuration uses all 160 KiB).
-template <bool DIRECT, bool FP8, int STAGES>
+template <bool DIRECT, bool FP8, int STAGES, bool STREAM = false>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_any, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
@@ -788,7 +811,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         for (int t = 0; t < kStages - 1 && t < ntiles; ++t) {
             const auto gp = plan_tile<FP8>(kvb, rows_lds, t, buf(t), vw, lane);
 #pragma unroll
-            for (int i = 0; i < kMaxLoads; ++i) issue_gather(gp, i);
+            for (int i = 0; i < kMaxLoads; ++i) issue_gather<STREAM>(gp, i);
         }
         PvAcc acc;
 #pragma unroll
@@ -809,7 +832,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
             wait_gathers<FP8>(min(ntiles - 1, t + kStages - 2) - (t + 1), nload);
             lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
 #pragma unroll
-            for (int i = 0; i < kMaxLoads; ++i) issue_gather(next, i);  // tile t + kStages - 1
+            for (int i = 0; i < kMaxLoads; ++i) issue_gather<STREAM>(next, i);  // tile t + kStages - 1
             if constexpr (FP8) apply_rescale8(records[t % kStages], c, acc);
             else apply_rescale(buf16(t), c, acc);
             load_p(pl, lane, pbv);
@@ -940,8 +963,9 @@ hipError_t launch_attn_impl(const uint16_t* q, const KV* kv, int64_t kv_bstride,
     const AttnWs w = attn_ws(ws, rows, k);
     decltype(&sparse_mla_kernel<false, FP8, 3>) split_kernel;
     if constexpr (FP8) split_kernel = sparse_mla_kernel<false, true, kStages8>;
-    else split_kernel = p.rows_per_split <= kFewTiles * kRows ? sparse_mla_kernel<false, false, 3>
-                                                              : sparse_mla_kernel<false, false, 4>;
+    else if (p.rows_per_split <= kFewTiles * kRows) split_kernel = sparse_mla_kernel<false, false, 3>;
+    else if ((int64_t)rows * k * kDqk * 2 >= kStreamGatherBytes) split_kernel = sparse_mla_kernel<false, false, 4, true>;
+    else split_kernel = sparse_mla_kernel<false, false, 4>;
     hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q, kv, kv_bstride,
                        idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, w.part_o, w.part_lse, out, lse);
     hipLaunchKernelGGL(p.nsplit <= kCombineNB ? attn_combine_kernel<kCombineNB> : attn_combine_kernel<kMaxQuerySplits>,
