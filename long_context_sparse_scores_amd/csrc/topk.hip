@@ -618,7 +618,10 @@ __global__ __launch_bounds__(kThreads) void topk_init_kernel(void* ws, Layout lo
 // in few top-digit bins, so the LDS atomics of one instruction collide, and
 // finer bins spread them; that pays on long slices (one per row at prefill),
 // where the atomics bound the pass.
-template <int FINE>
+// VEC (rows of a multiple of 4 keys, so every slice starts 16-byte aligned):
+// 16-byte nontemporal loads, 4 keys per lane and load; the quad holding the
+// end of the visible keys is read whole (it lies inside the row) and masked.
+template <int FINE, bool VEC>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ q_pos, int L, int k,
                                                              Layout lo, void* ws) {
@@ -635,16 +638,34 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
     const float* src = scores + (int64_t)row * L + start;
     const int m = (int)((n - start) < lo.slice ? (n - start) : lo.slice);
     lds_sync();
-    for (int i0 = 0; i0 < m; i0 += kBatch * kThreads) {
-        float v[kBatch];
+    if constexpr (VEC) {
+        for (int i0 = 0; i0 < m; i0 += kBatch * kThreads) {
+            f32x4_t v[kBatch / 4];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int i = i0 + j * kThreads + threadIdx.x;
-            v[j] = i < m ? src[i] : 0.0f;
+            for (int j = 0; j < kBatch / 4; ++j) {
+                const int i = i0 + 4 * (j * kThreads + (int)threadIdx.x);
+                v[j] = i < m ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + i))
+                             : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch / 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (i0 + 4 * (j * kThreads + (int)threadIdx.x) + e < m)
+                        atomicAdd(&h[score_key(v[j][e]) >> (32 - FINE)], 1u);
         }
+    } else {
+        for (int i0 = 0; i0 < m; i0 += kBatch * kThreads) {
+            float v[kBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (i0 + j * kThreads + (int)threadIdx.x < m) atomicAdd(&h[score_key(v[j]) >> (32 - FINE)], 1u);
+            for (int j = 0; j < kBatch; ++j) {
+                const int i = i0 + j * kThreads + threadIdx.x;
+                v[j] = i < m ? src[i] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (i0 + j * kThreads + (int)threadIdx.x < m) atomicAdd(&h[score_key(v[j]) >> (32 - FINE)], 1u);
+        }
     }
     lds_sync();
     uint32_t* g = row_ws(ws, row, lo).hist1;
@@ -659,7 +680,10 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
 // hist_checked: the histogram was added by the indexer onto what the last
 // selection left, so it is used only when that selection's stamp is there and
 // it counts the row's visible keys exactly; otherwise it was built from zero
-// in this call.
+// in this call.  VEC: 16-byte nontemporal loads as in topk_hist_kernel (each
+// wave's range starts at a multiple of 64 keys); the candidates reach the
+// row's list in another order, which the selection does not depend on.
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ q_pos, int L, int k,
                                                                Layout lo, void* ws, int hist_checked) {
@@ -684,11 +708,27 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     const int64_t w1 = min(w0 + lo.slice / kWaves, n);
     const float* row_scores = scores + (int64_t)row * L;
     float v[kBatch];
+    // value j of this lane: key i0 + j * 64 + lane, or (VEC) i0 + 4 * ((j / 4) * 64 + lane) + j % 4
+    auto key_at = [&](int64_t i0, int j) -> int64_t {
+        return VEC ? i0 + 4 * ((j / 4) * kWave + lane) + (j % 4) : i0 + j * kWave + lane;
+    };
     auto load_batch = [&](int64_t i0) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int64_t i = i0 + j * kWave + lane;
-            v[j] = row_scores[i < w1 ? i : w1 - 1];  // w1 >= 1; past w1 never used
+            for (int j = 0; j < kBatch / 4; ++j) {
+                const int64_t i = i0 + 4 * (j * kWave + lane);
+                // a quad starting before w1 lies inside the row (L is a multiple of 4); past w1 never used
+                const f32x4_t x = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4_t*>(row_scores + (i < w1 ? i : (w1 - 1) / 4 * 4)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int64_t i = i0 + j * kWave + lane;
+                v[j] = row_scores[i < w1 ? i : w1 - 1];  // w1 >= 1; past w1 never used
+            }
         }
     };
     load_batch(w0);
@@ -725,7 +765,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         if (i0 != w0) load_batch(i0);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int64_t i = i0 + j * kWave + lane;
+            const int64_t i = key_at(i0, j);
             const uint32_t key = score_key(v[j]);
             const bool cand = i < w1 && (key >> 21) >= T;
             const uint64_t m = __ballot(cand);
@@ -1101,11 +1141,14 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
                        hipStream_t stream, TopkState state) {
     const Layout lo = make_layout(rows, L);
     const unsigned grid = (unsigned)((int64_t)rows * lo.nslice);
+    // 16-byte loads in the streaming passes when every row starts 16-byte aligned
+    const bool vec = L % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
     if (state == TopkState::kNone) hipLaunchKernelGGL(topk_init_kernel, dim3(rows), dim3(kThreads), 0, stream, ws, lo);
     // finer LDS bins for long slices (measured: prefill 4096 x 128K rows, one slice per row)
     if (state != TopkState::kHistogram)
-        hipLaunchKernelGGL(lo.slice >= kFineSlice ? topk_hist_kernel<13> : topk_hist_kernel<11>, dim3(grid),
-                           dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
+        hipLaunchKernelGGL(lo.slice >= kFineSlice ? (vec ? topk_hist_kernel<13, true> : topk_hist_kernel<13, false>)
+                                                  : (vec ? topk_hist_kernel<11, true> : topk_hist_kernel<11, false>),
+                           dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws);
     // The fused pass unless there are many rows (prefill) and no histogram
     // from the indexer: there the separate filter's small workgroups stream
     // the rows with more of them resident per CU.
@@ -1114,7 +1157,8 @@ hipError_t launch_topk(const float* scores, const int32_t* q_pos, int rows, int 
                            stream, scores, q_pos, L, k, lo, ws, state == TopkState::kHistogram ? 1 : 0, idx);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(grid), dim3(kThreads), 0, stream, scores, q_pos, L, k, lo, ws, 0);
+    hipLaunchKernelGGL(vec ? topk_filter_kernel<true> : topk_filter_kernel<false>, dim3(grid), dim3(kThreads), 0,
+                       stream, scores, q_pos, L, k, lo, ws, 0);
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelectThreads), 0, stream, scores, q_pos, L, k, lo, ws,
                        idx);
     return hipGetLastError();

@@ -274,6 +274,21 @@ def test_topk_many_rows(dsa):
     _topk_case(dsa, s, pos, 1000)
 
 
+@pytest.mark.parametrize("L", [4098, 4099])
+def test_topk_many_rows_key_loads(dsa, L):
+    # 300 ragged rows on the many-row path with a length that is not a
+    # multiple of 4: rows then do not all start 16-byte aligned, and the
+    # streaming passes load one key per lane instead of four
+    rng = np.random.default_rng(L)
+    B, T = 1, 300
+    say("topk %d rows of %d keys" % (T, L))
+    s = (rng.integers(0, 64, size=(B, T, L)) / 8).astype(np.float32)
+    s[0, ::11] = 5.0
+    pos = ((np.arange(T, dtype=np.int32) * 53 + 2100) % L)[None]
+    pos[0, :3] = L - 1
+    _topk_case(dsa, s, pos, 2048)
+
+
 # ------------------------------------------------------------------ attention
 def test_attn_tiny_layers(dsa):
     cfg = synth.TINY
