@@ -324,6 +324,26 @@ def test_attn_masked_ragged(dsa):
     np.testing.assert_allclose(host(lse)[fin], ref_lse[fin], atol=LSE_TOL, rtol=0)
 
 
+@pytest.mark.parametrize("B", [28, 32])
+def test_attn_split_launch_either_side_of_streaming(dsa, B):
+    # 28 x 2048 rows (63 MiB) keep plain gathers, 32 x 2048 (72 MiB) stream
+    # them past the caches: the same kernel with another load hint, checked
+    # here with masked, out-of-range and duplicated entries
+    rng = np.random.default_rng(60 + B)
+    T, L, k = 1, 3000, 2048
+    say("attn split launch B=%d" % B)
+    q = synth.normal_bf16(43, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(43, 2, (B, L, 576))
+    idx = np.stack([np.sort(rng.choice(L, size=(T, k), replace=False), axis=1) for _ in range(B)]).astype(np.int32)
+    idx[0, 0, 1500:] = -1
+    idx[1, 0, 7] = L + 11         # out of range: masked
+    idx[2, 0, 100:200] = idx[2, 0, 99]  # a repeated row counts once per occurrence
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16)
+    assert_attn_close(host(out), ref)
+    np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
 def test_attn_dense_case(dsa):
     # k >= p+1: every visible row selected, sparse attention == dense causal attention
     B, T, L, k = 1, 3, 500, 512
