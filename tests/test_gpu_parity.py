@@ -730,6 +730,43 @@ def test_group_without_indexshare(dsa):
         assert not np.array_equal(got_idx[l], got_idx[0]), "layer %d selected the same rows as layer 0" % l
 
 
+def _sweep_shape(seed):
+    # a seeded shape: batch, queries per sequence, keys, k and ragged positions
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 5))
+    T = int(rng.choice([1, 1, 2, 5, 9]))
+    L = int(rng.choice([17, 300, 1023, 2049, 4100, 6001]))
+    k = int(rng.choice([1, 5, 33, 100, 256, 700, 2048]))
+    pos = rng.integers(0, L, size=(B, T)).astype(np.int32)
+    pos[0, -1] = L - 1
+    return B, T, L, k, pos
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_group_shape_sweep(dsa, seed):
+    # Seeded shapes across the launch configurations (split or whole lists,
+    # one to sixteen splits, k below or above the visible keys, ragged
+    # positions, lengths that are not multiples of a tile): the shared list
+    # bit-exact against the oracle, every query's output of two layers within
+    # tolerance.
+    B, T, L, k, pos = _sweep_shape(seed)
+    say("group sweep seed=%d B=%d T=%d L=%d k=%d" % (seed, B, T, L, k))
+    qi = synth.int_bf16(200 + seed, 1, (B, T, 32, 128))
+    w = synth.pow2_f32(200 + seed, 2, (B, T, 32))
+    ki = synth.int_bf16(200 + seed, 3, (B, L, 128))
+    qs = [synth.normal_bf16(200 + seed, 4 + l, (B, T, 64, 576)) for l in range(2)]
+    kvs = [synth.normal_bf16(200 + seed, 6 + l, (B, L, 576)) for l in range(2)]
+    idx, outs, lses = dsa.layer_group(bf16_dev(qi), f32_dev(w), bf16_dev(ki), i32_dev(pos), k,
+                                      [bf16_dev(q) for q in qs], [bf16_dev(kv) for kv in kvs], 1 / 16,
+                                      want_lse=True)
+    _, ref_idx, ref_outs, ref_lses = oracle.layer_group(qi, w, ki, pos, k, qs, kvs, 1 / 16)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    for l in range(2):
+        assert_attn_close(host(outs[l]), ref_outs[l], "layer %d" % l)
+        fin = np.isfinite(ref_lses[l])
+        np.testing.assert_allclose(host(lses[l])[fin], ref_lses[l][fin], atol=LSE_TOL, rtol=0)
+
+
 @pytest.mark.parametrize("B", [32, 40, 64, 100])
 def test_group_batch_sizes(dsa, B):
     # Batches of 32+ one-token queries: each list is split in 8 (B = 32),
