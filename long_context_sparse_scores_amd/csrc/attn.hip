@@ -198,25 +198,22 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Work split over four waves w = 2*hh + kk (in the bf16 kernel the score
-// waves take the first two jobs and the value waves the third; in the E4M3
-// kernel each wave does all three):
-//   Q.K^T  wave w computes partial S^T for the 32 heads of head blocks 2hh and
-//          2hh+1 over k-steps 9kk .. 9kk+8 (latent dims 288kk .. +287), q in
-//          registers; partner waves w and w^1 swap the halves of the block the
-//          other one owns through LDS, so wave w ends with S^T of head block w.
-//   softmax  wave w, head block w (heads 16w .. 16w+15), into P^T (bf16) in LDS.
-//   P.V    wave w, value dims 128w .. 128w+127 of all 64 heads, with the four
-//          P^T blocks read from LDS.
-// Every tile is then read from LDS about 1.5 times per workgroup (Q.K^T
-// twice over half the dims, P.V once) instead of 4 times per phase.
+// Work split over the waves of a workgroup that takes HB head blocks (the
+// score waves take the first two jobs, the value waves the third):
+//   Q.K^T  score wave w < HB computes S^T for head block w (16 heads) over the
+//          whole 576-dim contraction, the block's q in registers;
+//   softmax  the same wave, into P^T (bf16) in LDS;
+//   P.V    value wave w, value dims 128w .. 128w+127 of the HB head blocks,
+//          with the P^T blocks read from LDS.
+// Each active score wave reads the whole tile, so Q.K^T reads a tile from LDS
+// HB times per workgroup and P.V once; in exchange no partial sums cross waves.
 struct SoftmaxState {
     float m_ref;  // reference maximum (log2 units) of head 16w + c
     float lsum;   // this lane's share of the softmax denominator of head 16w + c
 };
 
-struct PvAcc {
-    f32x4_t o[8][4];  // O^T: value dims 128w + 16d + 4g + r of head 16hb + c
+template <int HB> struct PvAcc {
+    f32x4_t o[8][HB];  // O^T: value dims 128w + 16d + 4g + r of head 16hb + c of the workgroup's heads
 };
 
 // Per-lane LDS read addresses of one tile (bytes, relative to the tile), split
@@ -245,12 +242,6 @@ __device__ __forceinline__ TileAddr tile_addr(int lane) {
     for (int d = 0; d < 8; ++d) a.tr[d] = tr_row * 1024 + 16 * ((2 * d + (q >> 1)) ^ (tr_row & 15)) + 8 * (q & 1);
     return a;
 }
-
-// Rescale factors of a tile's softmax live in that tile's K-tail region once
-// Q.K^T has read it: float fac[4][16] (per head block, per head), then uint32
-// flag[4] (block hb moved its reference).  P.V of the same tile reads them.
-constexpr int kFacOffset = kMainBytes;
-constexpr int kFlagOffset = kMainBytes + 4 * 16 * 4;
 
 // Online softmax of the S^T block of head block w for one tile (bit e of
 // `valid`: value e of this lane is a visible row).  Updates the reference
@@ -306,51 +297,29 @@ __device__ __forceinline__ int list_entry(const int32_t* sel, int j, int nrows, 
     return (r >= 0 && r < L) ? r : -1;
 }
 
-// Apply the rescale factors recorded with tile tv's softmax to the accumulators.
-__device__ __forceinline__ void apply_rescale(const uint16_t* tv, int c, PvAcc& acc) {
-    const char* base = reinterpret_cast<const char*>(tv);
-    const u32x4_t fl = *reinterpret_cast<const u32x4_t*>(base + kFlagOffset);
-    const uint32_t any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
-    if (any) {
-        const float* fac = reinterpret_cast<const float*>(base + kFacOffset);
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-            if (__builtin_amdgcn_readfirstlane(fl[hb])) {
-                const float f = fac[16 * hb + c];
-#pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    acc.o[d][hb] *= f;
-                    __builtin_amdgcn_sched_barrier(0);  // one 4-register block at a time
-                }
-            }
-        }
-    }
-}
-
-// Q.K^T partial of tile `tq`: this wave's half of the dims, both head blocks of
-// its pair, accumulated into sp[row block][head block of the pair].
-__device__ __forceinline__ void qk_partial(const uint16_t* tq, const TileAddr& ad, const bf16x8_t (&qb)[2][9], int kk,
-                                           f32x4_t (&sp)[2][2]) {
+// S^T of tile `tq` for one head block over the whole 576-dim contraction.
+// qf[ks] holds the block's q for k-step ks; even and odd k-steps accumulate
+// apart so that no MFMA waits on the one just issued, and the two halves are
+// summed at the end.
+__device__ __forceinline__ void qk_full(const uint16_t* tq, const TileAddr& ad, const bf16x8_t (&qf)[kDqk / 32],
+                                        f32x4_t (&s)[2]) {
+    f32x4_t acc[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) acc[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kl = 0; kl < 9; ++kl) {
-        // k-step 9kk + kl: both candidates index the offset table at compile time
-        const int off_lo = ad.qk[kl & 3] + 256 * (kl >> 2);  // kk = 0: always in the main part
-        const int off_hi = kl < 7 ? ad.qk[(kl + 1) & 3] + 256 * ((9 + kl) >> 2) : ad.qt[kl - 7];
-        const int off = kk ? off_hi : off_lo;
-        const int rb1 = (kk && kl >= 7) ? 16 * 128 : 16 * 1024;  // next row block: tail rows are 128 B
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+        const int off = ks < 16 ? ad.qk[ks & 3] + 256 * (ks >> 2) : ad.qt[ks - 16];
+        const int rb1 = ks < 16 ? 16 * 1024 : 16 * 128;  // next row block: tail rows are 128 B
         const char* p = reinterpret_cast<const char*>(tq) + off;
         const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(p);
         const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(p + rb1);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
-            sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
-        }
+        acc[0][ks & 1] = mfma16x16x32(a0, qf[ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16x16x32(a1, qf[ks], acc[1][ks & 1]);
     }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) s[rb] = acc[rb][0] + acc[rb][1];
 }
 
 // Output rows staged in LDS by the epilogue: 64 rows of 512 bf16, padded to
@@ -358,14 +327,16 @@ __device__ __forceinline__ void qk_partial(const uint16_t* tq, const TileAddr& a
 constexpr int kStageRow = 2 * kDv + 16;
 
 // ------------------------------------------------------------------ P.V helpers of the bf16 tiles
-__device__ __forceinline__ void load_p(const bf16x8_t* __restrict__ pl, int lane, bf16x8_t (&pbv)[4]) {
+template <int HB>
+__device__ __forceinline__ void load_p(const bf16x8_t* __restrict__ pl, int lane, bf16x8_t (&pbv)[HB]) {
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pbv[hb] = pl[hb * kWave + lane];
+    for (int hb = 0; hb < HB; ++hb) pbv[hb] = pl[hb * kWave + lane];
 }
 
-// P.V of tile tv for value dims 128 vw .. +127 of all four head blocks.
-__device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, const bf16x8_t (&pbv)[4], int vw,
-                                        PvAcc& acc) {
+// P.V of tile tv for value dims 128 vw .. +127 of the workgroup's HB head blocks.
+template <int HB>
+__device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, const bf16x8_t (&pbv)[HB], int vw,
+                                        PvAcc<HB>& acc) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
         const char* p = reinterpret_cast<const char*>(tv) + ad.tr[d] + 256 * vw;
@@ -373,7 +344,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, 
         const bf16x4_t hi = lds_read_tr16(p + 16 * 1024);
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+        for (int hb = 0; hb < HB; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
     }
 }
 
@@ -499,17 +470,18 @@ __device__ __forceinline__ TileAddr8 tile_addr8(int lane) {
     return a;
 }
 
-struct Rescale8 {
+struct RescaleRecord {
     float fac[4 * 16];  // per head block, per head
     uint32_t flag[4];   // block hb moved its reference
 };
 
-__device__ __forceinline__ void apply_rescale8(const Rescale8& rs, int c, PvAcc& acc) {
+template <int HB>
+__device__ __forceinline__ void apply_rescale(const RescaleRecord& rs, int c, PvAcc<HB>& acc) {
     const u32x4_t fl = *reinterpret_cast<const u32x4_t*>(rs.flag);
-    const uint32_t any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+    const uint32_t any = __builtin_amdgcn_readfirstlane(fl[0] | (HB > 1 ? fl[1] : 0u) | (HB > 2 ? fl[2] | fl[3] : 0u));
     if (any) {
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
             if (__builtin_amdgcn_readfirstlane(fl[hb])) {
                 const float f = rs.fac[16 * hb + c];
 #pragma unroll
@@ -522,39 +494,40 @@ __device__ __forceinline__ void apply_rescale8(const Rescale8& rs, int c, PvAcc&
     }
 }
 
-// Q.K^T partial of E4M3 tile `tq`: this wave's half of the dims, both head
-// blocks of its pair (the rows widened exactly to bf16 as they are read).
-__device__ __forceinline__ void qk_partial8(const uint8_t* tq, const TileAddr8& ad, const bf16x8_t (&qb)[2][9],
-                                            int kk, int g, f32x4_t (&sp)[2][2]) {
+// S^T of E4M3 tile `tq` for one head block over the whole contraction (the
+// rows widened exactly to bf16 as they are read), in the same order of MFMAs
+// and sums as qk_full, so both caches give bit-identical scores for the same
+// values.
+__device__ __forceinline__ void qk_full8(const uint8_t* tq, const TileAddr8& ad, const bf16x8_t (&qf)[kDqk / 32], int g,
+                                         f32x4_t (&s)[2]) {
+    f32x4_t acc[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sp[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) acc[rb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kl = 0; kl < 9; ++kl) {
-        const int s = 18 * kk + 2 * kl + (g >> 1);  // chunk of dims 32(9kk + kl) + 8g .. +7
-        const uint2 r0 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * (s ^ ad.fq0));
-        const uint2 r1 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * kRow8 + 16 * (s ^ ad.fq1));
-        const bf16x8_t a0 = e4m3x8_to_bf16x8(r0.x, r0.y);
-        const bf16x8_t a1 = e4m3x8_to_bf16x8(r1.x, r1.y);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            sp[0][h] = mfma16x16x32(a0, qb[h][kl], sp[0][h]);
-            sp[1][h] = mfma16x16x32(a1, qb[h][kl], sp[1][h]);
-        }
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+        const int ch = 2 * ks + (g >> 1);  // chunk of dims 32ks + 8g .. +7
+        const uint2 r0 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * (ch ^ ad.fq0));
+        const uint2 r1 = *reinterpret_cast<const uint2*>(tq + ad.qk + 16 * kRow8 + 16 * (ch ^ ad.fq1));
+        acc[0][ks & 1] = mfma16x16x32(e4m3x8_to_bf16x8(r0.x, r0.y), qf[ks], acc[0][ks & 1]);
+        acc[1][ks & 1] = mfma16x16x32(e4m3x8_to_bf16x8(r1.x, r1.y), qf[ks], acc[1][ks & 1]);
     }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) s[rb] = acc[rb][0] + acc[rb][1];
 }
 
-// P.V of E4M3 tile tv for value dims 128 vw .. +127 of all four head blocks.
-__device__ __forceinline__ void pv_tile8(const uint8_t* tv, const TileAddr8& ad, const bf16x8_t (&pbv)[4], int vw,
-                                         PvAcc& acc) {
+// P.V of E4M3 tile tv for value dims 128 vw .. +127 of the workgroup's HB head blocks.
+template <int HB>
+__device__ __forceinline__ void pv_tile8(const uint8_t* tv, const TileAddr8& ad, const bf16x8_t (&pbv)[HB], int vw,
+                                         PvAcc<HB>& acc) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {  // value dims 128 vw + 16 d .. +15: chunk 8 vw + d
         const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2_t*)(tv + ad.pv + 16 * ((8 * vw + d) ^ ad.fpv)));
         const bf16x8_t a = e4m3x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
+        for (int hb = 0; hb < HB; ++hb) acc.o[d][hb] = mfma16x16x32(a, pbv[hb], acc.o[d][hb]);
     }
 }
 
@@ -638,37 +611,42 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
 }
 
 // ------------------------------------------------------------------ the attention kernel: two roles per SIMD
-// Eight waves, two per SIMD.  Waves 0-3 ("score waves", w = 2hh + kk) do
-// Q.K^T, the partner exchange and the softmax of the work split described
-// above; waves 4-7 ("value waves") issue the gathers and do P.V for value
-// dims 128(w-4) .. +127 of all 64 heads.  Each tile step has two phases
-// between workgroup barriers:
-//   phase 1  score waves: Q.K^T of tile t+1, partials sent to the partner;
-//            value waves: the gathers of tile t+kStages-1 (planned one
-//            iteration earlier), tile t's rescale record applied, its four
-//            P^T blocks loaded into registers;
-//   phase 2  score waves: scores and softmax of tile t+1 (P^T and rescale
-//            record to LDS); value waves: the next gather plan beside P.V of
-//            tile t, then the wait for their loads of tile t+1.
-// So every SIMD runs one wave's softmax (VALU) beside the other's P.V (matrix
-// cores) instead of one after the other (with one wave per SIMD doing all
-// four jobs in turn, the matrix cores sat idle through every softmax; this
-// measured 1.56x faster per bf16 prefill layer).  The two roles run separate
-// loops with the same sequence of barriers, so the registers of one (q for the
-// score waves, the accumulators for the value waves) are not held by the
-// other.  P^T needs one buffer: the value waves read it before the phase
-// barrier that precedes its next write.
-// FP8: the latent rows are E4M3 codes in a ring of seven 18 KiB tiles with the
-// rescale records beside it; otherwise bf16 tiles with the records in the
-// freed K-tail of each tile (the bf16 decode configuration uses all 160 KiB).
-template <bool DIRECT, bool FP8, int STAGES, bool STREAM = false>
+// Eight waves, two per SIMD.  A workgroup takes one query, a split of its
+// index list and HB of its four 16-head blocks (heads 16 HB hg .. +16 HB - 1 for
+// head group hg).  Waves 0-3 ("score waves"): wave w < HB computes S^T of head
+// block w over the whole 576-dim contraction, q in registers, and runs its
+// softmax; waves 4-7 ("value waves") issue the gathers and do P.V for value
+// dims 128(w-4) .. +127 of the HB head blocks.  One workgroup barrier per tile
+// step; between two of them
+//   score waves: Q.K^T and softmax of tile t+1 (P^T and rescale record to LDS
+//                at parity (t+1) & 1);
+//   value waves: the gathers of tile t+kStages-1 (planned one iteration
+//                earlier), tile t's rescale record applied and its P^T blocks
+//                loaded, the next gather plan beside P.V of tile t, then the
+//                wait for their loads of tile t+1.
+// So on every SIMD one wave's Q.K^T and softmax run beside the other's P.V.
+// Each score wave reads the whole tile from LDS; no partial sums cross waves.
+// Head groups (HB < 4) let small batches spread a query over more
+// workgroups without more split partials: the groups of a query gather the
+// same rows, on one XCD, so all but the first read of a row come from its L2.
+// The two roles run separate loops with the same sequence of barriers, so the
+// registers of one (q for the score waves, the accumulators for the value
+// waves) are not held by the other.
+// FP8: the latent rows are E4M3 codes in a ring of seven 18 KiB tiles;
+// otherwise bf16 tiles (the bf16 decode configuration uses 157 of 160 KiB).
+template <bool DIRECT, bool FP8, int STAGES, bool STREAM = false, int HB = 4>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv_any, int64_t kv_bstride,
     const int32_t* __restrict__ idx, int rows, int T, int L, int k, int rows_per_split, int nsplit, float scale_log2,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
-    const int grp = blockIdx.x / (kXcds * nsplit);
-    const int rem = blockIdx.x % (kXcds * nsplit);
-    const int split = rem / kXcds;
+    static_assert(HB == 1 || HB == 2 || HB == 4, "head blocks per workgroup");
+    constexpr int kGroups = 4 / HB;  // head groups per query
+    const int nparts = nsplit * kGroups;
+    const int grp = blockIdx.x / (kXcds * nparts);
+    const int rem = blockIdx.x % (kXcds * nparts);
+    const int part = rem / kXcds;
+    const int split = part / kGroups;
+    const int h0 = 16 * HB * (part % kGroups);  // first head of this workgroup
     const int bt = grp * kXcds + rem % kXcds;
     if (bt >= rows) return;
     const int b = bt / T;
@@ -686,14 +664,12 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     using TileT = typename std::conditional<FP8, uint8_t, uint16_t>::type;
     __shared__ __attribute__((aligned(16))) TileT tiles[kStages * kTileBytes / sizeof(TileT)];
     static_assert(kHq * kStageRow <= (int)sizeof(tiles), "the output staging fits in the tile buffers");
-    __shared__ __attribute__((aligned(16))) f32x4_t sx[kWaves * 2 * kWave];   // Q.K^T partials in transit
-    __shared__ __attribute__((aligned(16))) bf16x8_t pl[kWaves * kWave];      // P^T of the four head blocks
+    // P^T and the rescale record of tile t at parity t & 1: the score waves
+    // write tile t+1's while the value waves read tile t's.
+    __shared__ __attribute__((aligned(16))) bf16x8_t pl[2 * HB * kWave];  // P^T of the HB head blocks
     __shared__ __attribute__((aligned(16))) int rows_lds[Cfg<DIRECT>::kMaxRows];
-    Rescale8* records = nullptr;  // FP8: rescale record of tile t at records[t % kStages]
-    if constexpr (FP8) {
-        __shared__ __attribute__((aligned(16))) Rescale8 rescale8[kStages8];
-        records = rescale8;
-    }
+    __shared__ __attribute__((aligned(16))) RescaleRecord records[2];
+    __shared__ __attribute__((aligned(16))) float stats[2 * kHq];  // epilogue: [0, 64) sums, [64, 128) maxima
     auto buf = [&](int t) __attribute__((always_inline)) {
         return reinterpret_cast<uint8_t*>(tiles) + (t % kStages) * kTileBytes;
     };
@@ -702,62 +678,45 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
     };
     const TileAddr ad = tile_addr(lane);     // bf16 operand addresses
     const TileAddr8 ad8 = tile_addr8(lane);  // E4M3 operand addresses
-    float* stats = reinterpret_cast<float*>(sx);  // epilogue: [0, 64) sums, [64, 128) maxima
-    char* st8 = reinterpret_cast<char*>(tiles);   // epilogue: output rows staged, kStageRow bytes apart
+    char* st8 = reinterpret_cast<char*>(tiles);  // epilogue: output rows staged, kStageRow bytes apart
 
     const int32_t* sel = idx + (int64_t)bt * k + j0;
     if (score) {
-        // ---------------- score waves, w = 2hh + kk.  qb[0] holds the wave's own
-        // head block w, qb[1] the partner's block w ^ 1, so the partial to keep
-        // and the partial to send need no selects.
-        const int sw = wave, kk = sw & 1;
-        bf16x8_t qb[2][9];
+        // ---------------- score waves: wave sw < HB, head block sw of the group
+        const int sw = wave;
+        const bool active = sw < HB;  // wave-uniform
+        bf16x8_t qf[kDqk / 32];
+        if (active) {
+            const uint16_t* qh = q + ((int64_t)bt * kHq + h0 + 16 * sw + c) * kDqk + 8 * g;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint16_t* qh = q + ((int64_t)bt * kHq + 16 * (sw ^ h) + c) * kDqk + 8 * g + 32 * 9 * kk;
-#pragma unroll
-            for (int kl = 0; kl < 9; ++kl) qb[h][kl] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * kl);
+            for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
         }
         for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
         __syncthreads();  // rows_lds ready
         SoftmaxState st;
         st.m_ref = -INFINITY;
         st.lsum = 0.0f;
-        // Q.K^T of tile t, the exchange and the softmax; P^T and the rescale record to LDS
+        // Q.K^T of tile t and the softmax; P^T and the rescale record to LDS
         auto scores_of = [&](int t) __attribute__((always_inline)) {
-            f32x4_t sp[2][2];
-            if constexpr (FP8) qk_partial8(buf(t), ad8, qb, kk, g, sp);
-            else qk_partial(buf16(t), ad, qb, kk, sp);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sx[((sw ^ 1) * 2 + rb) * kWave + lane] = sp[rb][1];
+            if (!active) return;
             // the tile's visible rows: one LDS read and a ballot give a wave-uniform mask
             const uint32_t tmask = (uint32_t)__ballot(rows_lds[t * kRows + (lane & 31)] >= 0);
-            lds_barrier();  // partials exchanged (phase 1 -> 2)
             f32x4_t s[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) s[rb] = sp[rb][0] + sx[(sw * 2 + rb) * kWave + lane];
+            if constexpr (FP8) qk_full8(buf(t), ad8, qf, g, s);
+            else qk_full(buf16(t), ad, qf, s);
             // value e of this lane is row e < 4 ? 4g + e : 16 + 4g + e - 4
             const uint32_t valid = ((tmask >> (4 * g)) & 0xFu) | (((tmask >> (16 + 4 * g)) & 0xFu) << 4);
             float factor;
             bool moved;
             const bf16x8_t pb = softmax_tile(s, valid, tmask == 0xFFFFFFFFu, scale_log2, st, factor, moved);
-            pl[sw * kWave + lane] = pb;
-            float* fac;
-            uint32_t* flag;
-            if constexpr (FP8) {
-                fac = records[t % kStages].fac;
-                flag = records[t % kStages].flag;
-            } else {
-                fac = reinterpret_cast<float*>(buf(t) + kFacOffset);
-                flag = reinterpret_cast<uint32_t*>(buf(t) + kFlagOffset);
-            }
-            if (g == 0) fac[16 * sw + c] = factor;
-            if (lane == 0) flag[sw] = moved ? 1u : 0u;
+            pl[((t & 1) * HB + sw) * kWave + lane] = pb;
+            if (g == 0) records[t & 1].fac[16 * sw + c] = factor;
+            if (lane == 0) records[t & 1].flag[sw] = moved ? 1u : 0u;
         };
         lds_barrier();  // tile 0 in LDS
         scores_of(0);
         for (int t = 0; t + 1 < ntiles; ++t) {
-            lds_barrier();  // tile t+1 in LDS; the value waves hold P^T of tile t
+            lds_barrier();  // tile t+1 in LDS; P^T of tile t-1 read by the value waves
             scores_of(t + 1);
         }
         lds_barrier();  // P^T and rescale record of the last tile visible
@@ -765,14 +724,14 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         float lsum = st.lsum;
         lsum += __shfl_xor(lsum, 16, kWave);
         lsum += __shfl_xor(lsum, 32, kWave);
-        if (g == 0) {
+        if (active && g == 0) {
             stats[16 * sw + c] = lsum;
             stats[64 + 16 * sw + c] = st.m_ref;
         }
         lds_barrier();  // stats visible
         lds_barrier();  // output rows staged
-        const int head = 16 * sw + c;
-        if (g == 0) {
+        const int head = h0 + 16 * sw + c;
+        if (active && g == 0) {
             if (DIRECT) {
                 if (lse)
                     store_wt4(wt_rsrc(lse + (int64_t)bt * kHq), 4u * head,
@@ -813,57 +772,51 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int i = 0; i < kMaxLoads; ++i) issue_gather<STREAM>(gp, i);
         }
-        PvAcc acc;
+        PvAcc<HB> acc;
 #pragma unroll
         for (int d = 0; d < 8; ++d)
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int hb = 0; hb < HB; ++hb) acc.o[d][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         wait_gathers<FP8>(min(ntiles - 1, kStages - 2), nload);  // tile 0 landed
         // The plan of each in-loop gather (addresses from rows_lds) is made one
-        // iteration ahead, beside the P.V work, so phase 1 only issues the loads.
+        // iteration ahead, beside the P.V work, so the loop head only issues the loads.
         auto next = plan_tile<FP8>(kvb, rows_lds, min(kStages - 1, ntiles - 1), buf(kStages - 1), vw, lane);
         next.active = kStages - 1 < ntiles;
         lds_barrier();  // tile 0 in LDS
         clear_masked(0);  // beside the score waves' Q.K^T, whose masked scores are discarded
-        lds_barrier();  // (score waves: partials of tile 0 exchanged)
-        bf16x8_t pbv[4];
+        bf16x8_t pbv[HB];
         for (int t = 0; t + 1 < ntiles; ++t) {
             // this thread's loads of tile t+1 are done once only those of later tiles are outstanding
             wait_gathers<FP8>(min(ntiles - 1, t + kStages - 2) - (t + 1), nload);
             lds_barrier();  // tile t+1 in LDS; P^T and rescale record of tile t visible; buffer t-1 free
 #pragma unroll
             for (int i = 0; i < kMaxLoads; ++i) issue_gather<STREAM>(next, i);  // tile t + kStages - 1
-            if constexpr (FP8) apply_rescale8(records[t % kStages], c, acc);
-            else apply_rescale(buf16(t), c, acc);
-            load_p(pl, lane, pbv);
-            lds_barrier();  // (phase 1 -> 2) P^T of tile t is in registers; the score waves may overwrite it
+            apply_rescale<HB>(records[t & 1], c, acc);
+            load_p<HB>(pl + (t & 1) * HB * kWave, lane, pbv);
             // tile t + kStages goes to this tile's buffer, next iteration, after this P.V and a barrier
             auto nx = plan_tile<FP8>(kvb, rows_lds, min(t + kStages, ntiles - 1), buf(t), vw, lane);
             nx.active = t + kStages < ntiles;
-            if constexpr (FP8) pv_tile8(buf(t), ad8, pbv, vw, acc);
-            else pv_tile(buf16(t), ad, pbv, vw, acc);
-            clear_masked(t + 1);  // its Q.K^T is done; its P.V comes after the next barriers
+            if constexpr (FP8) pv_tile8<HB>(buf(t), ad8, pbv, vw, acc);
+            else pv_tile<HB>(buf16(t), ad, pbv, vw, acc);
+            // before tile t+1's P.V, after the next barrier; beside its Q.K^T, whose
+            // masked scores are discarded
+            clear_masked(t + 1);
             next = nx;
         }
         lds_barrier();  // P^T and rescale record of the last tile visible
-        if constexpr (FP8) {
-            apply_rescale8(records[(ntiles - 1) % kStages], c, acc);
-            load_p(pl, lane, pbv);
-            pv_tile8(buf(ntiles - 1), ad8, pbv, vw, acc);
-        } else {
-            apply_rescale(buf16(ntiles - 1), c, acc);
-            load_p(pl, lane, pbv);
-            pv_tile(buf16(ntiles - 1), ad, pbv, vw, acc);
-        }
+        apply_rescale<HB>(records[(ntiles - 1) & 1], c, acc);
+        load_p<HB>(pl + ((ntiles - 1) & 1) * HB * kWave, lane, pbv);
+        if constexpr (FP8) pv_tile8<HB>(buf(ntiles - 1), ad8, pbv, vw, acc);
+        else pv_tile<HB>(buf16(ntiles - 1), ad, pbv, vw, acc);
         lds_barrier();  // stats visible; every value wave is done reading the tiles
-        float inv[4];
+        float inv[HB];
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
             const float ls = stats[16 * hb + c];
             inv[hb] = ls > 0.0f ? 1.0f / ls : 0.0f;
         }
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
+        for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 const f32x4_t& o = acc.o[d][hb];
@@ -872,12 +825,12 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         lds_barrier();  // output rows staged
     }
-    // every wave stores 8 of the 64 head rows, one 16-byte store per lane per row
-    const __amdgpu_buffer_rsrc_t dst = wt_rsrc(DIRECT ? out + (int64_t)bt * kHq * kDv
-                                                      : part_o + ((int64_t)bt * nsplit + split) * kHq * kDv);
+    // every wave stores 2 HB of the 16 HB head rows, one 16-byte store per lane per row
+    const __amdgpu_buffer_rsrc_t dst = wt_rsrc(DIRECT ? out + ((int64_t)bt * kHq + h0) * kDv
+                                                      : part_o + (((int64_t)bt * nsplit + split) * kHq + h0) * kDv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int h = 8 * wave + i;
+    for (int i = 0; i < 2 * HB; ++i) {
+        const int h = 2 * HB * wave + i;
         store_wt16(dst, 2u * (h * kDv + 8 * lane), *reinterpret_cast<const u32x4_t*>(st8 + h * kStageRow + 16 * lane));
     }
 }
@@ -908,6 +861,7 @@ unsigned xcd_grid(int rows, int per_row) {
 
 struct SplitPlan {
     int nsplit, rows_per_split;
+    int hgroups;  // head groups per query: 1, 2 or 4 workgroups share a split's rows
 };
 
 // Splits of about `ns` per query (clamped so that every split's row list fits
@@ -924,11 +878,28 @@ SplitPlan plan_splits(int rows, int k, int ns) {
     if (ns < 1) ns = 1;
     const int tiles_per = (tiles + ns - 1) / ns;
     const int rps = tiles_per * kRows;
-    return SplitPlan{(k + rps - 1) / rps, rps};
+    return SplitPlan{(k + rps - 1) / rps, rps, 1};
 }
 
-// The partials' layout: enough splits for about kTargetBlocks workgroups.
-SplitPlan plan(int rows, int k) { return plan_splits(rows, k, (kTargetBlocks + rows - 1) / rows); }
+// Batches of fewer than kGroupRows queries split each query's heads over two
+// workgroups (head groups), and take splits for about kTargetBlocks
+// workgroups in all.  Measured against whole-query workgroups (attention
+// launch pair per layer or draft step):
+//   B = 16, 128K: 8 splits x 2 groups against 16 splits, 19.4 -> 17.8 us;
+//   B = 4, 1M: 16 splits x 2 groups against 16 splits, 17.9 -> 16.3 us; with
+//   4 groups (256 workgroups) 20.7 us, with 8 splits x 2 groups 18.1 us.
+// At B = 32 (8 splits) 4 splits x 2 groups measured the same as 8 splits, so
+// full batches keep whole-query workgroups.
+constexpr int kGroupRows = 32;
+
+// The partials' layout: splits (and head groups) for about kTargetBlocks
+// workgroups.
+SplitPlan plan(int rows, int k) {
+    const int hg = rows < kGroupRows ? 2 : 1;
+    SplitPlan p = plan_splits(rows, k, (kTargetBlocks + rows * hg - 1) / (rows * hg));
+    p.hgroups = hg;
+    return p;
+}
 
 // Workspace: [partials bf16][log2-sum-exps fp32], 256-byte aligned parts.
 struct AttnWs {
@@ -948,6 +919,16 @@ AttnWs attn_ws(void* ws, int rows, int k) {
     return AttnWs{reinterpret_cast<uint16_t*>(b), reinterpret_cast<float*>(b + part_o_bytes(rows, k))};
 }
 
+template <bool DIRECT, bool FP8, int STAGES, bool STREAM>
+using AttnKernel = decltype(&sparse_mla_kernel<DIRECT, FP8, STAGES, STREAM, 4>);
+
+// The kernel instance for `hgroups` (1 or 2) head groups of 4 / hgroups head blocks.
+template <bool DIRECT, bool FP8, int STAGES, bool STREAM = false>
+AttnKernel<DIRECT, FP8, STAGES, STREAM> attn_kernel(int hgroups) {
+    return hgroups == 2 ? sparse_mla_kernel<DIRECT, FP8, STAGES, STREAM, 2>
+                        : sparse_mla_kernel<DIRECT, FP8, STAGES, STREAM, 4>;
+}
+
 template <bool FP8, typename KV>
 hipError_t launch_attn_impl(const uint16_t* q, const KV* kv, int64_t kv_bstride, const int32_t* idx, int B, int T,
                             int L, int k, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
@@ -955,19 +936,20 @@ hipError_t launch_attn_impl(const uint16_t* q, const KV* kv, int64_t kv_bstride,
     const float scale_log2 = sm_scale * 1.4426950408889634f;
     const SplitPlan p = plan(rows, k);
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL((sparse_mla_kernel<true, FP8, FP8 ? kStages8 : kDirectStages>), dim3(xcd_grid(rows, 1)),
-                           dim3(2 * kThreads), 0, stream, q, kv, kv_bstride, idx, rows, T, L, k, p.rows_per_split, 1,
-                           scale_log2, nullptr, nullptr, out, lse);
+        const auto direct_kernel = attn_kernel<true, FP8, FP8 ? kStages8 : kDirectStages>(p.hgroups);
+        hipLaunchKernelGGL(direct_kernel, dim3(xcd_grid(rows, p.hgroups)), dim3(2 * kThreads), 0, stream, q, kv, kv_bstride, idx, rows,
+                           T, L, k, p.rows_per_split, 1, scale_log2, nullptr, nullptr, out, lse);
         return hipGetLastError();
     }
     const AttnWs w = attn_ws(ws, rows, k);
-    decltype(&sparse_mla_kernel<false, FP8, 3>) split_kernel;
-    if constexpr (FP8) split_kernel = sparse_mla_kernel<false, true, kStages8>;
-    else if (p.rows_per_split <= kFewTiles * kRows) split_kernel = sparse_mla_kernel<false, false, 3>;
-    else if ((int64_t)rows * k * kDqk * 2 >= kStreamGatherBytes) split_kernel = sparse_mla_kernel<false, false, 4, true>;
-    else split_kernel = sparse_mla_kernel<false, false, 4>;
-    hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, p.nsplit)), dim3(2 * kThreads), 0, stream, q, kv, kv_bstride,
-                       idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, w.part_o, w.part_lse, out, lse);
+    AttnKernel<false, FP8, 3, false> split_kernel;
+    if constexpr (FP8) split_kernel = attn_kernel<false, true, kStages8>(p.hgroups);
+    else if (p.rows_per_split <= kFewTiles * kRows) split_kernel = attn_kernel<false, false, 3>(p.hgroups);
+    else if ((int64_t)rows * k * kDqk * 2 >= kStreamGatherBytes) split_kernel = attn_kernel<false, false, 4, true>(p.hgroups);
+    else split_kernel = attn_kernel<false, false, 4>(p.hgroups);
+    hipLaunchKernelGGL(split_kernel, dim3(xcd_grid(rows, p.nsplit * p.hgroups)), dim3(2 * kThreads), 0, stream, q, kv,
+                       kv_bstride, idx, rows, T, L, k, p.rows_per_split, p.nsplit, scale_log2, w.part_o, w.part_lse,
+                       out, lse);
     hipLaunchKernelGGL(p.nsplit <= kCombineNB ? attn_combine_kernel<kCombineNB> : attn_combine_kernel<kMaxQuerySplits>,
                        dim3(xcd_grid(rows, kHq)), dim3(kCombineThreads), 0, stream, w.part_o, w.part_lse, rows,
                        p.nsplit, out, lse);

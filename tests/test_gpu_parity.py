@@ -324,6 +324,25 @@ def test_attn_masked_ragged(dsa):
     np.testing.assert_allclose(host(lse)[fin], ref_lse[fin], atol=LSE_TOL, rtol=0)
 
 
+@pytest.mark.parametrize("B,T,k", [(3, 1, 20), (5, 1, 700), (4, 5, 2048), (33, 1, 600)])
+def test_attn_head_groups(dsa, B, T, k):
+    # Batches under 32 queries split each query's heads over two workgroups:
+    # one tile (a single split per query), short and long splits; 33 queries
+    # keep whole-query workgroups.  Masked and missing entries in every list.
+    rng = np.random.default_rng(60 + B)
+    L = 4000
+    say("attn head groups B=%d T=%d k=%d" % (B, T, k))
+    q = synth.normal_bf16(60, 1, (B, T, 64, 576))
+    kv = synth.normal_bf16(60, 2, (B, L, 576))
+    idx = np.sort(rng.choice(L, size=(B, T, k)), axis=2).astype(np.int32)
+    idx[..., 1] = -1
+    idx[0, 0, k // 2:] = L + 5
+    out, lse = dsa.sparse_mla_attn(bf16_dev(q), bf16_dev(kv), i32_dev(idx), 1 / 16, want_lse=True)
+    ref, ref_lse = oracle.sparse_mla_attn(q, kv, idx, 1 / 16)
+    assert_attn_close(host(out), ref)
+    np.testing.assert_allclose(host(lse), ref_lse, atol=LSE_TOL, rtol=0)
+
+
 @pytest.mark.parametrize("B", [28, 32])
 def test_attn_split_launch_either_side_of_streaming(dsa, B):
     # 28 x 2048 rows (63 MiB) keep plain gathers, 32 x 2048 (72 MiB) stream
