@@ -16,8 +16,10 @@
 //   S^T (32 rows x 64 heads) = K_rows . Q^T   q in registers
 //   O^T (512 dims x 64 heads) += V^T . P^T    V^T read with ds_read_b64_tr_b16,
 //                                             P^T (bf16) through LDS
-// The bf16 kernel splits this over eight waves in two roles, two waves per
-// SIMD, so that one wave's softmax runs beside another's P.V (see below).
+// The kernel splits this over eight waves in two roles, two waves per SIMD,
+// so that one wave's Q.K^T and softmax run beside another's P.V (see below).
+// Batches of fewer than 32 queries also split each query's 64 heads over two
+// workgroups (head groups).
 // Softmax is online in base 2 with a lazily moved reference maximum: the
 // accumulators are rescaled only when a tile's maximum exceeds the reference
 // by more than 32 (so P < 2^32 and the fp32 sums stay far from overflow);
@@ -206,7 +208,7 @@ __device__ __forceinline__ void lds_barrier() {
 //   P.V    value wave w, value dims 128w .. 128w+127 of the HB head blocks,
 //          with the P^T blocks read from LDS.
 // Each active score wave reads the whole tile, so Q.K^T reads a tile from LDS
-// HB times per workgroup and P.V once; in exchange no partial sums cross waves.
+// HB times per workgroup and P.V once; in return no partial sums cross waves.
 struct SoftmaxState {
     float m_ref;  // reference maximum (log2 units) of head 16w + c
     float lsum;   // this lane's share of the softmax denominator of head 16w + c
