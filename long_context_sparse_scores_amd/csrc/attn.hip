@@ -431,21 +431,18 @@ __device__ __forceinline__ void wait_tiles8(int tiles, int nload) {
     }
 }
 
-typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
-// 8 E4M3 codes (low byte first) -> 8 bf16, exactly.
+// 8 E4M3 codes (low byte first) -> 8 bf16, exactly: one v_cvt_scalef32_pk_bf16_fp8
+// per pair with a scale of 1 (every E4M3 value, subnormals included, is a
+// bf16 value), the lower code into the lower half.
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    const f32x2v_t a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-    const f32x2v_t b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-    const f32x2v_t c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-    const f32x2v_t d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-    u32x4_t r;
-    r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-    r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-    r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-    r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
-    return __builtin_bit_cast(bf16x8_t, r);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(c, d, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Per-lane parts of the operand addresses (bytes within a tile).
