@@ -355,8 +355,8 @@ __device__ __forceinline__ void pv_tile(const uint16_t* tv, const TileAddr& ad, 
 // seven: six tiles in flight while one is read, twice the rows in flight of
 // the bf16 tiles.  The work split, softmax and combine are the same; only the
 // gathers and the operand reads differ, each operand widened exactly to bf16
-// in registers (v_cvt_pk_f32_fp8; the upper halves of the fp32 results are the
-// bf16 values):
+// in registers (v_cvt_scalef32_pk_bf16_fp8 with a scale of 1, two codes per
+// instruction):
 //   Q.K^T  A operand, 8 dims of a row: one ds_read_b64;
 //   P.V    A operand, 8 rows of one dim: one ds_read_b64_tr_b8 (in each
 //          16-lane group, lane 8q + r receives byte r of the 8-byte chunks
