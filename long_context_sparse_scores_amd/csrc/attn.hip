@@ -684,13 +684,26 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         // ---------------- score waves: wave sw < HB, head block sw of the group
         const int sw = wave;
         const bool active = sw < HB;  // wave-uniform
+        // The row list is read before q: loads return in order, and the list
+        // is what the gathers wait for, while q is first needed by tile 0's Q.K^T.
+        constexpr int kListPer = Cfg<DIRECT>::kMaxRows / (2 * kThreads);
+        int le[kListPer];
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) {
+            const int j = threadIdx.x + 2 * kThreads * u;
+            le[u] = j < ntiles * kRows ? list_entry(sel, j, nrows, L) : -1;
+        }
         bf16x8_t qf[kDqk / 32];
         if (active) {
             const uint16_t* qh = q + ((int64_t)bt * kHq + h0 + 16 * sw + c) * kDqk + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks);
         }
-        for (int j = threadIdx.x; j < ntiles * kRows; j += 2 * kThreads) rows_lds[j] = list_entry(sel, j, nrows, L);
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u) {
+            const int j = threadIdx.x + 2 * kThreads * u;
+            if (j < ntiles * kRows) rows_lds[j] = le[u];
+        }
         __syncthreads();  // rows_lds ready
         SoftmaxState st;
         st.m_ref = -INFINITY;
