@@ -571,6 +571,10 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
     // split s of this (query, head): partial at po + s * kHq * kDv bf16, log2-sum-exp at pl + s * kHq
     const __amdgpu_buffer_rsrc_t po = wt_rsrc(part_o + ((int64_t)bt * nsplit * kHq + head) * kDv);
     const __amdgpu_buffer_rsrc_t pl = wt_rsrc(part_lse + (int64_t)bt * nsplit * kHq + head);
+    // the split weights first: their reductions run while the partials are in flight
+    const float ls =
+        lane < nsplit ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pl, (int)(4u * (uint32_t)(lane * kHq)), 0, 0))
+                      : -INFINITY;
     u32x4_t v[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
@@ -578,9 +582,6 @@ __device__ __forceinline__ void combine_head(const uint16_t* __restrict__ part_o
         v[u] = __builtin_bit_cast(u32x4_t,
                                   __builtin_amdgcn_raw_buffer_load_b128(po, (int)(2u * (uint32_t)(sp * kHq * kDv + 8 * lane)), 0, 0));
     }
-    const float ls =
-        lane < nsplit ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pl, (int)(4u * (uint32_t)(lane * kHq)), 0, 0))
-                      : -INFINITY;
     float M = ls;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
@@ -736,14 +737,11 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
         float lsum = st.lsum;
         lsum += __shfl_xor(lsum, 16, kWave);
         lsum += __shfl_xor(lsum, 32, kWave);
+        const int head = h0 + 16 * sw + c;
         if (active && g == 0) {
             stats[16 * sw + c] = lsum;
             stats[64 + 16 * sw + c] = st.m_ref;
-        }
-        lds_barrier();  // stats visible
-        lds_barrier();  // output rows staged
-        const int head = h0 + 16 * sw + c;
-        if (active && g == 0) {
+            // the log-sum-exp goes out now, beside the value waves' staging
             if (DIRECT) {
                 if (lse)
                     store_wt4(wt_rsrc(lse + (int64_t)bt * kHq), 4u * head,
@@ -753,6 +751,8 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2,
                           lsum > 0.0f ? st.m_ref + log2f(lsum) : -INFINITY);
             }
         }
+        lds_barrier();  // stats visible
+        lds_barrier();  // output rows staged
     } else {
         // ---------------- value waves
         const int vw = wave - kWaves;
